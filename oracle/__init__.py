@@ -1,0 +1,17 @@
+"""Float64 CPU oracle for the In-Place TTT fast-weight prefill (test infrastructure only).
+
+Only the test suite, the package smoke check and the benchmark's CPU-baseline leg
+may import this package; the HIP library and its binding never do.
+"""
+from .ipttt_oracle import (  # noqa: F401
+    chunk_ranges,
+    conv_chunk,
+    decode_steps,
+    final_weight_entries,
+    gate_up,
+    prefill,
+    prefill_prefix_form,
+    prefill_with_resets,
+    silu,
+    target_chunk,
+)
