@@ -1,0 +1,198 @@
+"""Benchmark of the fast-weight prefill on one MI355X.
+
+One step = reset of the fast weight to W_0 (a new sequence) + one
+ipttt_prefill_layer call over the whole sequence: gate/up, conv, projection,
+update scan and apply for every chunk. Inputs are seeded synthetic tensors of
+the workload's shape, resident in HBM before the timed region. Prints one JSON
+line. Per-kernel durations come from HIP events that the library records on
+the launch stream during the timed steps.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import torch  # noqa: E402
+
+import workloads as wl  # noqa: E402
+
+METRIC = "fast-weight prefill tokens/s per MLP layer at L=128k,B=1024; % MFMA/HBM roofline"
+PEAK = {"bf16": 2500.0, "f32": 157.3}  # dense TFLOP/s (MFMA bf16, fp32)
+HBM_PEAK = 8000.0                       # GB/s
+
+
+def kernel_work(w: wl.Workload, tokens: int):
+    """Algorithmic FLOPs and HBM bytes of one launch of each kernel over `tokens`
+    tokens (all sequences of one pass). Bytes count each operand once."""
+    d, F, Kc = w.d, w.d_ff, w.conv_k
+    el = 2 if w.dtype == "bf16" else 4
+    chunks = -(-tokens // w.chunk)
+    return {
+        "gateup": (4 * d * F * tokens, el * (tokens * d + 2 * F * d + 2 * tokens * F)),
+        "conv": (2 * Kc * d * tokens, el * (2 * tokens * d + Kc * d)),
+        "proj": (2 * d * d * tokens, el * (2 * tokens * d + d * d)),
+        # linear scan: Z^T and V read once, W read and written once, a bf16 copy of W per chunk
+        "update": (2 * d * F * tokens, el * tokens * (F + d) + 8 * F * d + el * chunks * F * d),
+        "apply": (2 * d * F * tokens, el * tokens * F + el * chunks * F * d + 4 * tokens * d),
+    }
+
+
+def cpu_baseline(w: wl.Workload, x, e, weights, n_chunks: int):
+    import numpy as np  # noqa: F401
+    from threadpoolctl import threadpool_info
+
+    import oracle
+
+    tokens = min(w.seq_len, n_chunks * w.chunk)
+    ow = wl.to_oracle(weights)
+    X = x[:1, :tokens].double().numpy()
+    E = e[:1, :tokens].double().numpy()
+    t0 = time.perf_counter()
+    oracle.prefill(X, E, ow["W_g"], ow["W_u"], ow["conv_w"], ow["Proj"], ow["W_0"], w.eta, w.chunk,
+                   update=w.update)
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {
+        "value": tokens / dt,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"first {tokens} tokens ({tokens // w.chunk} chunks) of sequence 0, float64 numpy, "
+                  f"{dt:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default=wl.HEADLINE, choices=sorted(wl.WORKLOADS))
+    ap.add_argument("--slab-chunks", type=int, default=0, help="chunks per pass (0 = all)")
+    ap.add_argument("--cpu-chunks", type=int, default=8, help="chunks in the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--generic", action="store_true", help="generic FMA kernels instead of MFMA")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    from chunked_weight_mlp_amd import ipttt
+
+    ipttt.load()
+    w = wl.WORKLOADS[args.workload]
+    dev = "cuda:0"
+    t0 = time.perf_counter()
+    weights = wl.make_weights(w)
+    x, e = wl.make_inputs(w)
+    print(f"[bench] inputs {w.name} generated in {time.perf_counter() - t0:.1f} s", file=sys.stderr,
+          flush=True)
+    wdev = {k: v.to(dev) for k, v in weights.items()}
+    xd, ed = x.to(dev), e.to(dev)
+    slab = args.slab_chunks or w.n_chunks
+    layer = ipttt.Layer(**wdev, chunk=w.chunk, eta=w.eta, update=w.update, max_batch=w.n_seq,
+                        slab_chunks=slab,
+                        flags=ipttt.IPTTT_FLAG_GENERIC_KERNELS if args.generic else 0)
+    o = torch.empty(xd.shape, dtype=torch.float32, device=dev)
+
+    def step():
+        layer.reset()
+        layer.prefill(xd, ed, o)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        print(f"[bench] warmup {i + 1}/{args.warmup} done", file=sys.stderr, flush=True)
+
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ipttt.ipttt_profile_begin(layer.handle)
+    wall0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    prof = ipttt.ipttt_profile_end(layer.handle)
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / args.steps
+    tokens = w.n_seq * w.seq_len
+    value = tokens / (ms_step / 1e3)
+    print(f"[bench] {args.steps} steps in {ms_total:.1f} ms (wall {wall * 1e3:.1f} ms)", file=sys.stderr,
+          flush=True)
+
+    # per-kernel live durations and the dominant kernel's roofline
+    passes = -(-w.n_chunks // slab)
+    tok_per_pass = w.n_seq * min(w.seq_len, slab * w.chunk)
+    work = kernel_work(w, tok_per_pass)
+    kernels = {}
+    for k, (n, ms) in prof.items():
+        if n == 0:
+            continue
+        avg = ms / n
+        entry = {"launches_per_step": n / args.steps, "avg_ms": round(avg, 4),
+                 "share": round(ms / max(ms_total, 1e-9), 4)}
+        if k in work:
+            per_pass = n / args.steps / passes          # launches of this kernel per pass
+            fl, by = (v / per_pass for v in work[k])
+            entry["tflops"] = round(fl / (avg * 1e-3) / 1e12, 2)
+            entry["gbps"] = round(by / (avg * 1e-3) / 1e9, 1)
+        kernels[k] = entry
+    dom = max((k for k in kernels if k in work), key=lambda k: prof[k][1])
+    per_pass = prof[dom][0] / args.steps / passes
+    dom_fl, dom_by = (v / per_pass for v in work[dom])
+    dom_avg_s = prof[dom][1] / prof[dom][0] * 1e-3
+    intensity = dom_fl / max(dom_by, 1)
+    ridge = PEAK[w.dtype] * 1e12 / (HBM_PEAK * 1e9)
+    if intensity >= ridge:
+        ach = dom_fl / dom_avg_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK[w.dtype], "unit": "TFLOP/s",
+                "frac": round(ach / PEAK[w.dtype], 4), "traffic": None, "kernel": dom}
+    else:
+        ach = dom_by / dom_avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK, 4), "traffic": None, "kernel": dom}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded Gaussian inputs and weights of the workload's shape)",
+        "config": {"workload": w.name, "d": w.d, "d_ff": w.d_ff, "seq_len": w.seq_len,
+                   "chunk": w.chunk, "batch": w.n_seq, "update": w.update, "eta": w.eta,
+                   "chunks_per_pass": slab, "kernels": "generic" if args.generic else "mfma"},
+        "tflops": round(w.flops_per_token() * tokens / (ms_step * 1e-3) / 1e12, 2),
+        "roofline": roof,
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, x, e, weights, args.cpu_chunks)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,92 @@
+// Internal declarations shared by the host library (ipttt.cpp) and the kernel
+// translation units. Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/ipttt.h"
+
+namespace ipttt {
+
+// Rows of a slab are chunk-padded: chunk j of the slab occupies rows
+// [j*Bp, j*Bp + B) and rows [j*Bp + B, (j+1)*Bp) are zero padding, so every
+// chunk starts on a 32-row boundary (one MFMA K-step of the update).
+constexpr int kChunkAlign = 32;
+
+inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+
+// Geometry of one slab of a prefill call.
+struct Slab {
+  int n_seq;        // sequences in the call
+  int d, F, Kc;     // widths, conv taps
+  int B, Bp;        // chunk, padded chunk pitch
+  int nc;           // chunks in this slab
+  int nc_cap;       // chunks the workspace is laid out for (row pitch = nc_cap*Bp)
+  int64_t Lp;       // padded rows per sequence in the workspace = nc_cap * Bp
+  int64_t tok0;     // first token of the slab within each sequence
+  int64_t L;        // tokens per sequence in the call
+  int64_t x_seq_stride;  // elements between sequences in x / e / o (= L_total * d)
+  float eta;
+  int mse;
+};
+
+// Byte offsets of the workspace buffers (all 256-byte aligned).
+struct WsLayout {
+  size_t z, zt, c, vt, s, rt, total;
+};
+
+WsLayout ws_layout(int elem, int n_seq, int d, int F, int Bp, int nc_cap, int mse);
+
+// Pointers into the workspace for one call.
+struct WsPtrs {
+  void *z;   // [n][Lp][F]      Z, token-major
+  void *zt;  // [n][F][Lp]      Z transposed (token-contiguous)
+  void *c;   // [n][Lp][d]      conv output
+  void *vt;  // [n][d][Lp]      target V transposed; eta*V for the linear rule
+  void *s;   // linear: [n][nc_cap][d][F] W snapshot per chunk; mse: [n][d][F]
+  void *rt;  // mse: [n][d][Bp] eta*(V - O) of the current chunk, transposed
+};
+
+struct Weights {
+  const void *w_gate, *w_up, *proj, *conv_w;
+};
+
+// ---- generic kernels (fp32 and bf16 storage, fp32 FMA) --------------------
+template <typename T>
+hipError_t gen_gateup(const Slab &s, const T *x, const Weights &w, const WsPtrs &ws,
+                      hipStream_t st);
+template <typename T>
+hipError_t gen_conv(const Slab &s, const T *e, const Weights &w, const WsPtrs &ws,
+                    hipStream_t st);
+template <typename T>
+hipError_t gen_proj(const Slab &s, const Weights &w, const WsPtrs &ws, hipStream_t st);
+template <typename T>
+hipError_t gen_snapshot(const Slab &s, const float *w_state, T *snap, int64_t snap_seq_stride,
+                        hipStream_t st);
+// W[c][f] += sum_t A[c][t] Zt[f][t] over one chunk j; optional snapshot of the new W.
+template <typename T>
+hipError_t gen_update(const Slab &s, int j, const T *a, int64_t a_ld, int64_t a_seq_stride,
+                      const WsPtrs &ws, float *w_state, T *snap_out, int64_t snap_seq_stride,
+                      hipStream_t st);
+// O rows of chunks [j0, j0+nj) from snapshots; mse also writes rt (nj must be 1).
+template <typename T>
+hipError_t gen_apply(const Slab &s, int j0, int nj, const T *snap, int64_t snap_seq_stride,
+                     int64_t snap_chunk_stride, const WsPtrs &ws, float *o, hipStream_t st);
+
+// ---- MFMA kernels (bf16 storage, gfx950) ----------------------------------
+bool mfma_supported(int d, int F);
+hipError_t mf_gateup(const Slab &s, const __bf16 *x, const Weights &w, const WsPtrs &ws,
+                     hipStream_t st);
+hipError_t mf_proj(const Slab &s, const Weights &w, const WsPtrs &ws, hipStream_t st);
+// Linear rule: for each chunk j of the slab, write snapshot S[j] = bf16(W) then
+// W += Zt_j^T-contract Vt_j; W stays in registers across the slab's chunks.
+hipError_t mf_update_scan(const Slab &s, const WsPtrs &ws, float *w_state, hipStream_t st);
+// MSE rule, one chunk j: W += Rt Zt_j^T-contract, snapshot S = bf16(new W).
+hipError_t mf_update_one(const Slab &s, int j, const WsPtrs &ws, float *w_state,
+                         hipStream_t st);
+hipError_t mf_apply(const Slab &s, int j0, int nj, const WsPtrs &ws, float *o,
+                    hipStream_t st);
+
+}  // namespace ipttt

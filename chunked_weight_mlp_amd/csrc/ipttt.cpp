@@ -1,0 +1,435 @@
+// Host side of libipttt: argument validation, workspace planning and the
+// chunk-scan launch sequence. Kernels live in kernels_*.hip.
+//
+// Linear rule, per slab of chunks (all sequences of the call at once):
+//   gate/up -> Z, Zt;  conv -> C;  proj -> Vt = eta * V
+//   update scan: snapshot S_j = W before chunk j, then W += eta Z_j^T V_j
+//   apply (batched over chunks): O_j = Z_j S_j
+// The update of one W tile never needs another tile, and the apply of chunk j
+// needs only the snapshot S_j, so applying every chunk after the scan is the
+// same computation as applying each chunk before its update.
+// MSE rule, per chunk: apply with S = W (current) -> O_j and Rt = eta (V - O_j);
+// update W += Z_j^T Rt and refresh S.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+
+struct ipttt_layer {
+  ipttt_layer_desc desc;
+  std::vector<uint8_t> was_reset;
+  bool mfma;
+  // per-kernel timing (ipttt_profile_begin / _end)
+  bool prof = false;
+  struct Rec {
+    int kind;
+    hipEvent_t a, b;
+  };
+  std::vector<Rec> recs;
+  std::vector<hipEvent_t> spare;
+  std::vector<hipEvent_t> all_events;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ipttt_status fail(ipttt_status s, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = std::string(ipttt_status_str(s)) + ": " + buf;
+  return s;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int elem_size(ipttt_dtype t) { return t == IPTTT_BF16 ? 2 : 4; }
+
+ipttt_status check_sizes(const ipttt_layer_desc *d) {
+  if (!d) return fail(IPTTT_E_INVALID, "descriptor is NULL");
+  if (d->d <= 0 || d->d_ff <= 0) return fail(IPTTT_E_INVALID, "d=%d d_ff=%d must be > 0", d->d, d->d_ff);
+  if (d->d > (1 << 16) || d->d_ff > (1 << 18))
+    return fail(IPTTT_E_UNSUPPORTED, "d=%d d_ff=%d exceed 65536 / 262144", d->d, d->d_ff);
+  if (d->chunk <= 0) return fail(IPTTT_E_INVALID, "chunk=%d must be > 0", d->chunk);
+  if (d->chunk > (1 << 16)) return fail(IPTTT_E_UNSUPPORTED, "chunk=%d exceeds 65536", d->chunk);
+  if (d->conv_k <= 0) return fail(IPTTT_E_INVALID, "conv_k=%d must be > 0", d->conv_k);
+  if (d->conv_k > 8) return fail(IPTTT_E_UNSUPPORTED, "conv_k=%d exceeds 8", d->conv_k);
+  if (d->max_batch <= 0) return fail(IPTTT_E_INVALID, "max_batch=%d must be > 0", d->max_batch);
+  if (d->in_dtype != IPTTT_F32 && d->in_dtype != IPTTT_BF16)
+    return fail(IPTTT_E_UNSUPPORTED, "in_dtype=%d", (int)d->in_dtype);
+  if (d->update != IPTTT_UPDATE_LINEAR && d->update != IPTTT_UPDATE_MSE)
+    return fail(IPTTT_E_UNSUPPORTED, "update=%d", (int)d->update);
+  if (!(d->eta == d->eta) || d->eta > 3.0e38f || d->eta < -3.0e38f)
+    return fail(IPTTT_E_INVALID, "eta is not finite");
+  if (d->flags & ~IPTTT_FLAG_GENERIC_KERNELS) return fail(IPTTT_E_INVALID, "unknown flags 0x%x", d->flags);
+  return IPTTT_OK;
+}
+
+int chunk_pitch(int B) { return (int)ipttt::round_up(B, ipttt::kChunkAlign); }
+
+bool use_mfma(const ipttt_layer_desc *d) {
+  return d->in_dtype == IPTTT_BF16 && !(d->flags & IPTTT_FLAG_GENERIC_KERNELS) &&
+         ipttt::mfma_supported(d->d, d->d_ff);
+}
+
+ipttt_status hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return IPTTT_OK;
+  return fail(IPTTT_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define TRY_HIP(expr, what)                                    \
+  do {                                                         \
+    ipttt_status _s = hip_status((expr), (what));              \
+    if (_s != IPTTT_OK) return _s;                             \
+  } while (0)
+
+// Records an event pair around one launch when the handle is profiling.
+struct ProfScope {
+  ipttt_layer *h;
+  int kind;
+  hipStream_t st;
+  hipEvent_t a = nullptr, b = nullptr;
+  static hipEvent_t take(ipttt_layer *h) {
+    if (!h->spare.empty()) {
+      hipEvent_t e = h->spare.back();
+      h->spare.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    h->all_events.push_back(e);
+    return e;
+  }
+  ProfScope(ipttt_layer *h_, int kind_, hipStream_t st_) : h(h_), kind(kind_), st(st_) {
+    if (!h->prof) return;
+    a = take(h);
+    b = take(h);
+    if (a && b) hipEventRecord(a, st);
+  }
+  ~ProfScope() {
+    if (!h->prof || !a || !b) return;
+    hipEventRecord(b, st);
+    h->recs.push_back({kind, a, b});
+  }
+};
+
+#define LAUNCH(kind, expr, what)                                   \
+  do {                                                             \
+    ProfScope _ps(h, (kind), st);                                  \
+    TRY_HIP((expr), (what));                                       \
+  } while (0)
+
+}  // namespace
+
+namespace ipttt {
+
+WsLayout ws_layout(int elem, int n_seq, int d, int F, int Bp, int nc_cap, int mse) {
+  WsLayout w{};
+  const size_t Lp = (size_t)nc_cap * Bp;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += (size_t)round_up((int64_t)bytes, 256);
+    return o;
+  };
+  w.z = take((size_t)n_seq * Lp * F * elem);
+  w.zt = take((size_t)n_seq * F * Lp * elem);
+  w.c = take((size_t)n_seq * Lp * d * elem);
+  w.vt = take((size_t)n_seq * d * Lp * elem);
+  w.s = take((size_t)n_seq * (mse ? 1 : nc_cap) * d * F * elem);
+  w.rt = mse ? take((size_t)n_seq * d * Bp * elem) : off;
+  w.total = off;
+  return w;
+}
+
+}  // namespace ipttt
+
+extern "C" {
+
+const char *ipttt_status_str(ipttt_status s) {
+  switch (s) {
+    case IPTTT_OK: return "IPTTT_OK";
+    case IPTTT_E_INVALID: return "IPTTT_E_INVALID";
+    case IPTTT_E_UNSUPPORTED: return "IPTTT_E_UNSUPPORTED";
+    case IPTTT_E_HIP: return "IPTTT_E_HIP";
+    case IPTTT_E_STATE: return "IPTTT_E_STATE";
+    case IPTTT_E_WORKSPACE: return "IPTTT_E_WORKSPACE";
+  }
+  return "IPTTT_E_UNKNOWN";
+}
+
+const char *ipttt_last_error(void) { return g_last_error.c_str(); }
+
+size_t ipttt_workspace_bytes(const ipttt_layer_desc *desc, int32_t batch, int32_t slab_chunks) {
+  std::string saved = g_last_error;
+  ipttt_status s = check_sizes(desc);
+  g_last_error = saved;
+  if (s != IPTTT_OK || batch < 1 || slab_chunks < 1) return 0;
+  return ipttt::ws_layout(elem_size(desc->in_dtype), batch, desc->d, desc->d_ff,
+                          chunk_pitch(desc->chunk), slab_chunks, desc->update == IPTTT_UPDATE_MSE)
+      .total;
+}
+
+ipttt_status ipttt_init(const ipttt_layer_desc *desc, ipttt_layer **out) {
+  if (!out) return fail(IPTTT_E_INVALID, "out is NULL");
+  *out = nullptr;
+  ipttt_status s = check_sizes(desc);
+  if (s != IPTTT_OK) return s;
+  const void *ptrs[] = {desc->w_gate, desc->w_up, desc->proj, desc->conv_w, desc->w0,
+                        desc->w_state, desc->workspace};
+  const char *names[] = {"w_gate", "w_up", "proj", "conv_w", "w0", "w_state", "workspace"};
+  for (int i = 0; i < 7; ++i) {
+    if (!ptrs[i]) return fail(IPTTT_E_INVALID, "%s is NULL", names[i]);
+    if (!aligned16(ptrs[i])) return fail(IPTTT_E_INVALID, "%s is not 16-byte aligned", names[i]);
+  }
+  if (((uintptr_t)desc->workspace & 255u) != 0)
+    return fail(IPTTT_E_INVALID, "workspace is not 256-byte aligned");
+  if (desc->workspace_bytes < ipttt_workspace_bytes(desc, 1, 1))
+    return fail(IPTTT_E_WORKSPACE, "workspace_bytes=%zu below the %zu bytes of one chunk of one sequence",
+                desc->workspace_bytes, ipttt_workspace_bytes(desc, 1, 1));
+  ipttt_layer *h = new (std::nothrow) ipttt_layer;
+  if (!h) return fail(IPTTT_E_INVALID, "out of host memory");
+  h->desc = *desc;
+  h->was_reset.assign((size_t)desc->max_batch, 0);
+  h->mfma = use_mfma(desc);
+  *out = h;
+  return IPTTT_OK;
+}
+
+void ipttt_destroy(ipttt_layer *h) {
+  if (!h) return;
+  for (hipEvent_t e : h->all_events) hipEventDestroy(e);
+  delete h;
+}
+
+ipttt_status ipttt_profile_begin(ipttt_layer *h) {
+  if (!h) return fail(IPTTT_E_INVALID, "handle is NULL");
+  for (auto &r : h->recs) {
+    h->spare.push_back(r.a);
+    h->spare.push_back(r.b);
+  }
+  h->recs.clear();
+  h->prof = true;
+  return IPTTT_OK;
+}
+
+ipttt_status ipttt_profile_end(ipttt_layer *h, int32_t *launches, double *ms) {
+  if (!h) return fail(IPTTT_E_INVALID, "handle is NULL");
+  if (!launches || !ms) return fail(IPTTT_E_INVALID, "launches and ms must be non-NULL");
+  for (int k = 0; k < IPTTT_K_COUNT; ++k) {
+    launches[k] = 0;
+    ms[k] = 0.0;
+  }
+  h->prof = false;
+  ipttt_status st = IPTTT_OK;
+  for (auto &r : h->recs) {
+    float t = 0.f;
+    if (st == IPTTT_OK) {
+      st = hip_status(hipEventSynchronize(r.b), "event synchronize");
+      if (st == IPTTT_OK) st = hip_status(hipEventElapsedTime(&t, r.a, r.b), "event elapsed time");
+    }
+    launches[r.kind] += 1;
+    ms[r.kind] += t;
+    h->spare.push_back(r.a);
+    h->spare.push_back(r.b);
+  }
+  h->recs.clear();
+  return st;
+}
+
+ipttt_status ipttt_reset_fast_weights(ipttt_layer *h, int32_t first_seq, int32_t n_seq,
+                                      void *hip_stream) {
+  if (!h) return fail(IPTTT_E_INVALID, "handle is NULL");
+  const ipttt_layer_desc &d = h->desc;
+  if (first_seq < 0 || n_seq < 0 || (int64_t)first_seq + n_seq > d.max_batch)
+    return fail(IPTTT_E_INVALID, "sequences [%d, %d) outside [0, %d)", first_seq, first_seq + n_seq,
+                d.max_batch);
+  const size_t bytes = (size_t)d.d * d.d_ff * sizeof(float);
+  hipStream_t st = (hipStream_t)hip_stream;
+  for (int32_t i = 0; i < n_seq; ++i)
+    TRY_HIP(hipMemcpyAsync(d.w_state + (size_t)(first_seq + i) * d.d * d.d_ff, d.w0, bytes,
+                           hipMemcpyDeviceToDevice, st),
+            "reset copy");
+  for (int32_t i = 0; i < n_seq; ++i) h->was_reset[(size_t)(first_seq + i)] = 1;
+  return IPTTT_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Runs the scan over `L` tokens of `n_seq` sequences whose state slots start
+// at `slot0`. x / e / o point at token 0 of the first sequence; sequences are
+// `seq_stride` elements apart.
+template <typename T>
+ipttt_status run_scan(ipttt_layer *h, const T *x, const T *e, float *o, int slot0, int n_seq,
+                      int64_t L, int64_t seq_stride, hipStream_t st) {
+  using namespace ipttt;
+  const ipttt_layer_desc &d = h->desc;
+  const int elem = (int)sizeof(T);
+  const int mse = d.update == IPTTT_UPDATE_MSE;
+  const int B = d.chunk, Bp = chunk_pitch(B);
+  const int64_t K = (L + B - 1) / B;
+  // largest slab that fits the workspace
+  int64_t lo = 1, hi = K;
+  if (ws_layout(elem, n_seq, d.d, d.d_ff, Bp, 1, mse).total > d.workspace_bytes)
+    return fail(IPTTT_E_WORKSPACE, "workspace_bytes=%zu cannot hold one chunk of %d sequences (%zu)",
+                d.workspace_bytes, n_seq, ws_layout(elem, n_seq, d.d, d.d_ff, Bp, 1, mse).total);
+  while (lo < hi) {
+    const int64_t mid = (lo + hi + 1) / 2;
+    if (ws_layout(elem, n_seq, d.d, d.d_ff, Bp, (int)mid, mse).total <= d.workspace_bytes)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  const int nc_cap = (int)lo;
+  const WsLayout lay = ws_layout(elem, n_seq, d.d, d.d_ff, Bp, nc_cap, mse);
+  char *base = (char *)d.workspace;
+  WsPtrs ws{base + lay.z, base + lay.zt, base + lay.c, base + lay.vt, base + lay.s, base + lay.rt};
+  Weights w{d.w_gate, d.w_up, d.proj, d.conv_w};
+  float *wst = d.w_state + (size_t)slot0 * d.d * d.d_ff;
+  const int64_t dF = (int64_t)d.d * d.d_ff;
+  const int64_t snap_seq_stride = mse ? dF : (int64_t)nc_cap * dF;
+
+  for (int64_t k0 = 0; k0 < K; k0 += nc_cap) {
+    Slab s{};
+    s.n_seq = n_seq;
+    s.d = d.d;
+    s.F = d.d_ff;
+    s.Kc = d.conv_k;
+    s.B = B;
+    s.Bp = Bp;
+    s.nc = (int)std::min<int64_t>(nc_cap, K - k0);
+    s.nc_cap = nc_cap;
+    s.Lp = (int64_t)nc_cap * Bp;
+    s.tok0 = k0 * B;
+    s.L = L;
+    s.x_seq_stride = seq_stride;
+    s.eta = d.eta;
+    s.mse = mse;
+    if (h->mfma) {
+      LAUNCH(IPTTT_K_GATEUP, mf_gateup(s, (const __bf16 *)x, w, ws, st), "gate/up launch");
+      LAUNCH(IPTTT_K_CONV, gen_conv<T>(s, e, w, ws, st), "conv launch");
+      LAUNCH(IPTTT_K_PROJ, mf_proj(s, w, ws, st), "proj launch");
+      if (!mse) {
+        LAUNCH(IPTTT_K_UPDATE, mf_update_scan(s, ws, wst, st), "update scan launch");
+        LAUNCH(IPTTT_K_APPLY, mf_apply(s, 0, s.nc, ws, o, st), "apply launch");
+      } else {
+        if (k0 == 0) LAUNCH(IPTTT_K_SNAPSHOT, gen_snapshot<T>(s, wst, (T *)ws.s, snap_seq_stride, st), "snapshot launch");
+        for (int j = 0; j < s.nc; ++j) {
+          LAUNCH(IPTTT_K_APPLY, mf_apply(s, j, 1, ws, o, st), "apply launch");
+          LAUNCH(IPTTT_K_UPDATE, mf_update_one(s, j, ws, wst, st), "update launch");
+        }
+      }
+    } else {
+      LAUNCH(IPTTT_K_GATEUP, gen_gateup<T>(s, x, w, ws, st), "gate/up launch");
+      LAUNCH(IPTTT_K_CONV, gen_conv<T>(s, e, w, ws, st), "conv launch");
+      LAUNCH(IPTTT_K_PROJ, gen_proj<T>(s, w, ws, st), "proj launch");
+      T *S = (T *)ws.s;
+      if (!mse) {
+        LAUNCH(IPTTT_K_SNAPSHOT, gen_snapshot<T>(s, wst, S, snap_seq_stride, st), "snapshot launch");
+        for (int j = 0; j < s.nc; ++j) {
+          T *next = (j + 1 < s.nc) ? S + (int64_t)(j + 1) * dF : nullptr;
+          LAUNCH(IPTTT_K_UPDATE,
+                 gen_update<T>(s, j, (const T *)ws.vt + (int64_t)j * Bp, s.Lp,
+                               (int64_t)d.d * s.Lp, ws, wst, next, snap_seq_stride, st),
+                 "update launch");
+        }
+        LAUNCH(IPTTT_K_APPLY, gen_apply<T>(s, 0, s.nc, S, snap_seq_stride, dF, ws, o, st), "apply launch");
+      } else {
+        if (k0 == 0) LAUNCH(IPTTT_K_SNAPSHOT, gen_snapshot<T>(s, wst, S, snap_seq_stride, st), "snapshot launch");
+        for (int j = 0; j < s.nc; ++j) {
+          LAUNCH(IPTTT_K_APPLY, gen_apply<T>(s, j, 1, S, snap_seq_stride, 0, ws, o, st), "apply launch");
+          LAUNCH(IPTTT_K_UPDATE,
+                 gen_update<T>(s, j, (const T *)ws.rt, Bp, (int64_t)d.d * Bp, ws, wst, S,
+                               snap_seq_stride, st),
+                 "update launch");
+        }
+      }
+    }
+  }
+  return IPTTT_OK;
+}
+
+ipttt_status check_call(ipttt_layer *h, const void *x, const void *e, const float *o) {
+  if (!h) return fail(IPTTT_E_INVALID, "handle is NULL");
+  if (!x || !e || !o) return fail(IPTTT_E_INVALID, "x, e and o must be non-NULL");
+  const size_t align = (size_t)elem_size(h->desc.in_dtype);
+  if (((uintptr_t)x % align) || ((uintptr_t)e % align) || ((uintptr_t)o % 4))
+    return fail(IPTTT_E_INVALID, "x / e / o misaligned for their dtype");
+  return IPTTT_OK;
+}
+
+ipttt_status dispatch(ipttt_layer *h, const void *x, const void *e, float *o, int slot0, int n_seq,
+                      int64_t L, int64_t seq_stride, hipStream_t st) {
+  if (h->desc.in_dtype == IPTTT_BF16)
+    return run_scan<__bf16>(h, (const __bf16 *)x, (const __bf16 *)e, o, slot0, n_seq, L, seq_stride,
+                            st);
+  return run_scan<float>(h, (const float *)x, (const float *)e, o, slot0, n_seq, L, seq_stride, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+ipttt_status ipttt_prefill_layer(ipttt_layer *h, const void *x, const void *e, float *o,
+                                 int32_t batch, int64_t seq_len, void *hip_stream) {
+  if (!h) return fail(IPTTT_E_INVALID, "handle is NULL");
+  if (batch < 0 || seq_len < 0) return fail(IPTTT_E_INVALID, "batch=%d seq_len=%lld must be >= 0", batch, (long long)seq_len);
+  if (batch > h->desc.max_batch)
+    return fail(IPTTT_E_INVALID, "batch=%d exceeds max_batch=%d", batch, h->desc.max_batch);
+  if (batch == 0 || seq_len == 0) return IPTTT_OK;
+  ipttt_status s = check_call(h, x, e, o);
+  if (s != IPTTT_OK) return s;
+  if (seq_len > ((int64_t)1 << 40) / h->desc.d) return fail(IPTTT_E_UNSUPPORTED, "seq_len too large");
+  for (int32_t i = 0; i < batch; ++i)
+    if (!h->was_reset[(size_t)i]) return fail(IPTTT_E_STATE, "sequence %d was never reset", i);
+  return dispatch(h, x, e, o, 0, batch, seq_len, seq_len * h->desc.d, (hipStream_t)hip_stream);
+}
+
+ipttt_status ipttt_prefill_packed(ipttt_layer *h, const void *x, const void *e, float *o,
+                                  int32_t slot, int64_t seq_len, const int64_t *doc_starts,
+                                  int32_t n_docs, void *hip_stream) {
+  if (!h) return fail(IPTTT_E_INVALID, "handle is NULL");
+  if (slot < 0 || slot >= h->desc.max_batch)
+    return fail(IPTTT_E_INVALID, "slot=%d outside [0, %d)", slot, h->desc.max_batch);
+  if (seq_len < 0 || n_docs < 0) return fail(IPTTT_E_INVALID, "seq_len and n_docs must be >= 0");
+  if (n_docs > 0 && !doc_starts) return fail(IPTTT_E_INVALID, "doc_starts is NULL");
+  for (int32_t i = 0; i < n_docs; ++i) {
+    if (doc_starts[i] <= 0 || doc_starts[i] >= seq_len)
+      return fail(IPTTT_E_INVALID, "doc_starts[%d]=%lld outside (0, %lld)", i, (long long)doc_starts[i],
+                  (long long)seq_len);
+    if (i > 0 && doc_starts[i] <= doc_starts[i - 1])
+      return fail(IPTTT_E_INVALID, "doc_starts must be strictly ascending");
+  }
+  if (seq_len == 0) return IPTTT_OK;
+  ipttt_status s = check_call(h, x, e, o);
+  if (s != IPTTT_OK) return s;
+  if (!h->was_reset[(size_t)slot]) return fail(IPTTT_E_STATE, "sequence %d was never reset", slot);
+  const ipttt_layer_desc &d = h->desc;
+  const size_t el = (size_t)elem_size(d.in_dtype);
+  hipStream_t st = (hipStream_t)hip_stream;
+  int64_t a = 0;
+  for (int32_t i = 0; i <= n_docs; ++i) {
+    const int64_t b = i < n_docs ? doc_starts[i] : seq_len;
+    if (i > 0)
+      TRY_HIP(hipMemcpyAsync(d.w_state + (size_t)slot * d.d * d.d_ff, d.w0,
+                             (size_t)d.d * d.d_ff * sizeof(float), hipMemcpyDeviceToDevice, st),
+              "reset copy");
+    s = dispatch(h, (const char *)x + (size_t)a * d.d * el, (const char *)e + (size_t)a * d.d * el,
+                 o + (size_t)a * d.d, slot, 1, b - a, (b - a) * d.d, st);
+    if (s != IPTTT_OK) return s;
+    a = b;
+  }
+  return IPTTT_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,252 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Bars (relative Frobenius error of O and of the final fast weight):
+  fp32 path: 1e-4      bf16-input / fp32-accumulate path: 2e-2
+Bitwise: run-to-run determinism, token-level causality, continuation across
+calls, slab splits, batch independence and reset.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from chunked_weight_mlp_amd import ipttt as B
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def rel_fro(a, b):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.load()
+
+
+def make_layer(w: wl.Workload, weights, flags=0, max_batch=None, slab_chunks=None,
+               workspace_bytes=None):
+    dev = {k: v.to(DEV) for k, v in weights.items()}
+    return B.Layer(**dev, chunk=w.chunk, eta=w.eta, update=w.update,
+                   max_batch=max_batch or w.n_seq, slab_chunks=slab_chunks,
+                   max_seq_len=w.seq_len, workspace_bytes=workspace_bytes, flags=flags)
+
+
+def gpu_run(layer, x, e, reset=True):
+    if reset:
+        layer.reset()
+    o = layer.prefill(x.to(DEV), e.to(DEV))
+    torch.cuda.synchronize()
+    return o
+
+
+def w_pages(layer, n):
+    """Final fast weights in the pages' orientation [n, F, d], float64."""
+    return layer.w_state[:n].detach().to("cpu", torch.float64).numpy().transpose(0, 2, 1)
+
+
+def oracle_run(w, x, e, weights, W_start=None):
+    ow = wl.to_oracle(weights)
+    X = x.to(torch.float64).numpy()
+    E = e.to(torch.float64).numpy()
+    return oracle.prefill(X, E, ow["W_g"], ow["W_u"], ow["conv_w"], ow["Proj"],
+                          ow["W_0"] if W_start is None else W_start, w.eta, w.chunk, update=w.update)
+
+
+def check_against_oracle(w, flags=0, n_seq=None, seq_len=None, slab_chunks=None, seed=0):
+    weights = wl.make_weights(w, seed_offset=seed)
+    x, e = wl.make_inputs(w, seq_len=seq_len, n_seq=n_seq, seed_offset=seed)
+    N, L = x.shape[0], x.shape[1]
+    say(f"[parity] {w.name} N={N} L={L} B={w.chunk} d={w.d} F={w.d_ff} {w.dtype} {w.update} "
+        f"flags={flags} slab={slab_chunks}")
+    layer = make_layer(w.replace(n_seq=N, seq_len=L), weights, flags=flags, slab_chunks=slab_chunks)
+    o = gpu_run(layer, x, e).to("cpu", torch.float64).numpy()
+    Wg = w_pages(layer, N)
+    O_ref, W_ref = oracle_run(w, x, e, weights)
+    eo, ew = rel_fro(o, O_ref), rel_fro(Wg, W_ref)
+    say(f"[parity]   rel_fro O={eo:.3e} W={ew:.3e} (tol {TOL[w.dtype]:.0e})")
+    assert np.isfinite(o).all()
+    assert eo <= TOL[w.dtype], eo
+    assert ew <= TOL[w.dtype], ew
+    return eo, ew
+
+
+TINY = wl.WORKLOADS["tiny_d64_f256_L1024_B128_fp32"]
+W4B = wl.WORKLOADS["qwen3_4b_L32k_B512"]
+W15 = wl.WORKLOADS["pretrain_1p5b_8x16k_B512_mse"]
+
+
+def test_tiny_fp32_full_size():
+    check_against_oracle(TINY)
+
+
+@pytest.mark.parametrize("L,Bc,N,update", [
+    (1000, 128, 2, "linear"),   # ragged last chunk, two sequences
+    (37, 5, 1, "linear"),       # chunk not a multiple of 32, ragged
+    (130, 64, 3, "mse"),
+    (1, 16, 1, "linear"),       # a single token
+    (70, 1, 1, "linear"),       # one token per chunk
+    (300, 300, 1, "mse"),       # single chunk
+    (200, 512, 1, "linear"),    # chunk longer than the sequence
+])
+def test_fp32_edges(L, Bc, N, update):
+    w = TINY.replace(chunk=Bc, update=update, eta=0.02 if update == "linear" else 0.01)
+    check_against_oracle(w, n_seq=N, seq_len=L)
+
+
+BF16_SMALL = wl.Workload("bf16_d256_f640", 2, 256, 640, 1000, 128, "bf16", 1e-2, "linear")
+
+
+@pytest.mark.parametrize("flags", [0, B.IPTTT_FLAG_GENERIC_KERNELS], ids=["mfma", "generic"])
+@pytest.mark.parametrize("update", ["linear", "mse"])
+@pytest.mark.parametrize("L,Bc", [(1000, 128), (777, 96), (2048, 1024), (64, 64)])
+def test_bf16_small_shapes(flags, update, L, Bc):
+    w = BF16_SMALL.replace(chunk=Bc, update=update, eta=1e-2 if update == "linear" else 2e-3)
+    check_against_oracle(w, flags=flags, seq_len=L)
+
+
+def test_bf16_multi_slab():
+    """A workspace for 3 chunks forces several passes over a 9-chunk sequence."""
+    check_against_oracle(BF16_SMALL.replace(chunk=64), seq_len=9 * 64 - 5, slab_chunks=3)
+
+
+def test_qwen3_4b_shape_two_chunks_and_tail():
+    check_against_oracle(W4B.replace(chunk=1024), n_seq=1, seq_len=2 * 1024 + 100)
+
+
+def test_pretrain_1p5b_mse_shape():
+    check_against_oracle(W15, n_seq=2, seq_len=512 + 512 + 37)
+
+
+@pytest.mark.parametrize("Bc", [64, 256, 512, 1024, 4096])
+def test_chunk_sweep_vs_prefix_form(Bc):
+    """4B-shaped layer at several chunk sizes against the oracle's prefix-sum form."""
+    w = wl.WORKLOADS[f"qwen3_4b_L64k_B{Bc}"]
+    L = 1024
+    weights = wl.make_weights(w)
+    x, e = wl.make_inputs(w, seq_len=L)
+    say(f"[sweep] B={Bc} L={L}")
+    layer = make_layer(w.replace(seq_len=L), weights)
+    o = gpu_run(layer, x, e).to("cpu", torch.float64).numpy()
+    ow = wl.to_oracle(weights)
+    O_ref, W_ref = oracle.prefill_prefix_form(x.double().numpy(), e.double().numpy(), ow["W_g"],
+                                              ow["W_u"], ow["conv_w"], ow["Proj"], ow["W_0"], w.eta, Bc)
+    eo, ew = rel_fro(o, O_ref), rel_fro(w_pages(layer, 1), W_ref)
+    say(f"[sweep]   rel_fro O={eo:.3e} W={ew:.3e}")
+    assert eo <= TOL["bf16"] and ew <= TOL["bf16"]
+
+
+def _bitwise_pair(layer_a, layer_b, x, e):
+    oa = gpu_run(layer_a, x, e)
+    ob = gpu_run(layer_b, x, e)
+    return oa, ob
+
+
+def test_determinism_and_reset():
+    w = BF16_SMALL.replace(seq_len=1000)
+    weights = wl.make_weights(w)
+    x, e = wl.make_inputs(w)
+    layer = make_layer(w, weights)
+    o1 = gpu_run(layer, x, e).clone()
+    w1 = layer.w_state.clone()
+    o2 = gpu_run(layer, x, e)   # reset puts W_0 back: same result bit for bit
+    assert torch.equal(o1, o2)
+    assert torch.equal(w1, layer.w_state)
+
+
+def test_causality_bitwise():
+    w = BF16_SMALL.replace(n_seq=1, seq_len=640, chunk=128)
+    weights = wl.make_weights(w)
+    x, e = wl.make_inputs(w)
+    layer = make_layer(w, weights)
+    o = gpu_run(layer, x, e).clone()
+    for p in (1, 127, 128, 129, 300):
+        x2, e2 = x.clone(), e.clone()
+        x2[:, p:] += 1.0
+        e2[:, p:] -= 1.0
+        o2 = gpu_run(layer, x2, e2)
+        assert torch.equal(o2[:, :p], o[:, :p]), p
+        assert not torch.equal(o2[:, p:], o[:, p:])
+    for k in range(4):  # target of chunk k is first used by chunk k+1
+        e3 = e.clone()
+        e3[:, k * 128:(k + 1) * 128] += 1.0
+        o3 = gpu_run(layer, x, e3)
+        assert torch.equal(o3[:, :(k + 1) * 128], o[:, :(k + 1) * 128]), k
+        assert not torch.equal(o3[:, (k + 1) * 128:], o[:, (k + 1) * 128:])
+
+
+@pytest.mark.parametrize("update", ["linear", "mse"])
+def test_continuation_bitwise(update):
+    w = BF16_SMALL.replace(n_seq=2, seq_len=5 * 128 + 50, update=update, eta=2e-3)
+    weights = wl.make_weights(w)
+    x, e = wl.make_inputs(w)
+    layer = make_layer(w, weights)
+    o = gpu_run(layer, x, e).clone()
+    wf = layer.w_state.clone()
+    layer.reset()
+    xd, ed = x.to(DEV), e.to(DEV)
+    o1 = layer.prefill(xd[:, :256].contiguous(), ed[:, :256].contiguous())
+    o2 = layer.prefill(xd[:, 256:].contiguous(), ed[:, 256:].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([o1, o2], 1), o)
+    assert torch.equal(layer.w_state, wf)
+
+
+def test_batch_independence_bitwise():
+    w = BF16_SMALL.replace(n_seq=3, seq_len=400)
+    weights = wl.make_weights(w)
+    x, e = wl.make_inputs(w)
+    layer = make_layer(w, weights)
+    o = gpu_run(layer, x, e).clone()
+    x2, e2 = x.clone(), e.clone()
+    x2[[0, 2]] += 0.5
+    e2[[0, 2]] -= 0.5
+    o2 = gpu_run(layer, x2, e2)
+    assert torch.equal(o2[1], o[1])
+
+
+def test_packed_documents():
+    w = BF16_SMALL.replace(n_seq=1, seq_len=900, chunk=128)
+    weights = wl.make_weights(w)
+    x, e = wl.make_inputs(w)
+    starts = [200, 333, 700]
+    layer = make_layer(w, weights)
+    layer.reset()
+    o = layer.prefill_packed(x[0].to(DEV), e[0].to(DEV), starts)
+    torch.cuda.synchronize()
+    ow = wl.to_oracle(weights)
+    O_ref, W_ref = oracle.prefill_with_resets(x[0].double().numpy(), e[0].double().numpy(), ow["W_g"],
+                                              ow["W_u"], ow["conv_w"], ow["Proj"], ow["W_0"], w.eta,
+                                              w.chunk, starts)
+    eo = rel_fro(o.double().cpu().numpy(), O_ref)
+    ew = rel_fro(w_pages(layer, 1)[0], W_ref)
+    say(f"[packed] rel_fro O={eo:.3e} W={ew:.3e}")
+    assert eo <= TOL["bf16"] and ew <= TOL["bf16"]
+
+
+def test_profile_records_every_kernel():
+    w = BF16_SMALL.replace(n_seq=1, seq_len=512)
+    weights = wl.make_weights(w)
+    x, e = wl.make_inputs(w)
+    layer = make_layer(w, weights)
+    layer.reset()
+    B.ipttt_profile_begin(layer.handle)
+    layer.prefill(x.to(DEV), e.to(DEV))
+    prof = B.ipttt_profile_end(layer.handle)
+    for k in ("gateup", "conv", "proj", "update", "apply"):
+        assert prof[k][0] >= 1 and prof[k][1] > 0, (k, prof)
