@@ -75,7 +75,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default=wl.HEADLINE, choices=sorted(wl.WORKLOADS))
     ap.add_argument("--slab-chunks", type=int, default=0, help="chunks per pass (0 = all)")
-    ap.add_argument("--cpu-chunks", type=int, default=8, help="chunks in the oracle sample")
+    ap.add_argument("--cpu-chunks", type=int, default=40, help="chunks in the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--generic", action="store_true", help="generic FMA kernels instead of MFMA")
     args = ap.parse_args()
