@@ -12,8 +12,8 @@ namespace ipttt {
 
 // Rows of a slab are chunk-padded: chunk j of the slab occupies rows
 // [j*Bp, j*Bp + B) and rows [j*Bp + B, (j+1)*Bp) are zero padding, so every
-// chunk starts on a 32-row boundary (one MFMA K-step of the update).
-constexpr int kChunkAlign = 32;
+// chunk starts on a 64-row boundary (one K step of the MFMA update).
+constexpr int kChunkAlign = 64;
 
 inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 
@@ -79,6 +79,8 @@ hipError_t gen_apply(const Slab &s, int j0, int nj, const T *snap, int64_t snap_
 bool mfma_supported(int d, int F);
 hipError_t mf_gateup(const Slab &s, const __bf16 *x, const Weights &w, const WsPtrs &ws,
                      hipStream_t st);
+hipError_t mf_conv(const Slab &s, const __bf16 *e, const Weights &w, const WsPtrs &ws,
+                   hipStream_t st);
 hipError_t mf_proj(const Slab &s, const Weights &w, const WsPtrs &ws, hipStream_t st);
 // Linear rule: for each chunk j of the slab, write snapshot S[j] = bf16(W) then
 // W += Zt_j^T-contract Vt_j; W stays in registers across the slab's chunks.

@@ -317,7 +317,7 @@ ipttt_status run_scan(ipttt_layer *h, const T *x, const T *e, float *o, int slot
     s.mse = mse;
     if (h->mfma) {
       LAUNCH(IPTTT_K_GATEUP, mf_gateup(s, (const __bf16 *)x, w, ws, st), "gate/up launch");
-      LAUNCH(IPTTT_K_CONV, gen_conv<T>(s, e, w, ws, st), "conv launch");
+      LAUNCH(IPTTT_K_CONV, mf_conv(s, (const __bf16 *)e, w, ws, st), "conv launch");
       LAUNCH(IPTTT_K_PROJ, mf_proj(s, w, ws, st), "proj launch");
       if (!mse) {
         LAUNCH(IPTTT_K_UPDATE, mf_update_scan(s, ws, wst, st), "update scan launch");
@@ -362,9 +362,10 @@ ipttt_status run_scan(ipttt_layer *h, const T *x, const T *e, float *o, int slot
 ipttt_status check_call(ipttt_layer *h, const void *x, const void *e, const float *o) {
   if (!h) return fail(IPTTT_E_INVALID, "handle is NULL");
   if (!x || !e || !o) return fail(IPTTT_E_INVALID, "x, e and o must be non-NULL");
-  const size_t align = (size_t)elem_size(h->desc.in_dtype);
+  // the MFMA path moves x and e in 16-byte vectors
+  const size_t align = h->mfma ? 16 : (size_t)elem_size(h->desc.in_dtype);
   if (((uintptr_t)x % align) || ((uintptr_t)e % align) || ((uintptr_t)o % 4))
-    return fail(IPTTT_E_INVALID, "x / e / o misaligned for their dtype");
+    return fail(IPTTT_E_INVALID, "x / e must be %zu-byte aligned and o 4-byte aligned", align);
   return IPTTT_OK;
 }
 

@@ -1,12 +1,14 @@
 // bf16 MFMA kernels of the fast-weight prefill for gfx950 (CDNA4).
 //
-// All four dense contractions share one block shape: 256 threads = 4 waves as
-// 2 x 2, a 256 x 128 output tile per block, 128 x 64 per wave as 8 x 4 tiles of
-// v_mfma_f32_16x16x32_bf16, K staged through LDS 32 at a time in two buffers.
+// All four dense contractions share one block structure, templated on the
+// wave grid and the K step (Cfg): WM x WN waves, each computing a 128 x 64
+// output tile as 8 x 4 tiles of v_mfma_f32_16x16x32_bf16, so a block covers
+// (128 WM) x (64 WN). K is staged through LDS BK at a time in two buffers;
+// the global loads of step s+1 are in flight while step s runs on MFMA.
 // Both operands are K-contiguous in memory ("NT"): a lane's MFMA operand is
-// 8 consecutive K values (one 16-byte LDS read). LDS rows are padded from 64 to
-// 80 bytes so that the 16-byte fragment reads of 8 (or 16) consecutive lanes
-// fall on distinct banks.
+// 8 consecutive K values (one 16-byte LDS read). LDS rows are padded by 16
+// bytes so that the 16-byte fragment reads of consecutive lanes, which walk
+// down 16 rows, fall on distinct banks.
 //
 // 16x16x32 operand layout used here: lane l supplies row (l % 16) of A and
 // column (l % 16) of B, each with K values 8*(l / 16) .. 8*(l / 16) + 7; the
@@ -14,35 +16,41 @@
 // consistent assignment of K values to (lane group, slot) gives the same sum.
 //
 // Kernels:
-//   k_gateup   Z = SiLU(X W_g) * (X W_u)   M = slab rows, N = d_ff (64 gate +
-//              64 up columns per block), K = d. Writes Z and Zt.
-//   k_proj     Vt = scale * (C Proj)^T       M = slab rows, N = d, K = d.
-//   k_apply    O = Z_j S_j                   M = chunk rows, N = d, K = d_ff,
-//              batched over (sequence, chunk); MSE also writes
+//   k_gateup   Z = SiLU(X W_g) * (X W_u)   M = slab rows, N = d_ff (half the
+//              block's B rows are gate rows, half up rows), K = d. Writes Z
+//              (token-major) and Zt (token-contiguous).
+//   k_proj     Vt = scale * (C Proj)^T     M = slab rows, N = d, K = d.
+//   k_apply    O = Z_j S_j                 M = chunk rows, N = d, K = d_ff,
+//              batched over (sequence, chunk); the MSE rule also writes
 //              Rt = eta (V - O)^T.
-//   k_update   W^T tile (256 d_ff x 128 d, fp32) held in the accumulators across
-//              the chunks of a slab: per chunk, optionally write the bf16
-//              snapshot S_j, then accumulate Zt_j . Vt_j over the chunk's tokens.
+//   k_update   W^T tile (BM d_ff rows x BN d columns, fp32) held in the
+//              accumulators across the chunks of a slab: per chunk, optionally
+//              write the bf16 snapshot S_j, then accumulate Zt_j . Vt_j over
+//              the chunk's tokens.
 #include "internal.h"
 
 namespace ipttt {
-namespace {
+namespace mfma {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 256, BN = 128, BK = 32;
-constexpr int PITCH = BK + 8;                 // LDS row pitch in bf16 (80 bytes)
-constexpr int NTHR = 256;
-constexpr int A_PIECES = BM * (BK / 8) / NTHR;  // 16-byte loads per thread per step (4)
-constexpr int B_PIECES = BN * (BK / 8) / NTHR;  // (2)
-constexpr int A_STAGE = BM * PITCH, B_STAGE = BN * PITCH;
-constexpr int MI = 8, NJ = 4;                 // 16x16 tiles per wave
-
-struct Smem {
-  __bf16 a[2][A_STAGE];
-  __bf16 b[2][B_STAGE];
+template <int WM_, int WN_, int BK_>
+struct Cfg {
+  static constexpr int WM = WM_, WN = WN_, BK = BK_;
+  static constexpr int MI = 8, NJ = 4;  // 16x16 tiles per wave: 128 x 64
+  static constexpr int BM = 128 * WM, BN = 64 * WN;
+  static constexpr int NTHR = 64 * WM * WN;
+  static constexpr int PITCH = BK + 8;  // LDS row pitch in bf16
+  static constexpr int KP = BK / 8;     // 16-byte pieces per row per step
+  static constexpr int RPP = NTHR / KP; // rows covered by one pass of all threads
+  static constexpr int A_PIECES = BM / RPP;
+  static constexpr int B_PIECES = BN / RPP;
+  static constexpr int A_STAGE = BM * PITCH, B_STAGE = BN * PITCH;
+  static constexpr int SMEM_ELEMS = 2 * (A_STAGE + B_STAGE);
+  static_assert(BK % 32 == 0 && BM % RPP == 0 && BN % RPP == 0, "bad tile config");
+  static_assert(SMEM_ELEMS * 2 <= 160 * 1024, "LDS overflow");
 };
 
 __device__ __forceinline__ uint4 ld16(const __bf16 *p) { return *(const uint4 *)p; }
@@ -54,71 +62,6 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   const int per = nblocks / 8, rem = nblocks % 8;
   const int x = bid % 8, q = bid / 8;
   return x * per + min(x, rem) + q;
-}
-
-// Per-thread loader state: the rows this thread copies into LDS (row index
-// (tid / 4) + 64 i) and the 8-element K offset (tid % 4).
-template <int NP>
-struct RowLoader {
-  const __bf16 *ptr[NP];  // row base (already offset to K = 0), nullptr = zero row
-  uint4 v[NP];
-  __device__ __forceinline__ void fetch(int k0, int q) {
-#pragma unroll
-    for (int i = 0; i < NP; ++i)
-      v[i] = ptr[i] ? ld16(ptr[i] + k0 + 8 * q) : make_uint4(0, 0, 0, 0);
-  }
-  __device__ __forceinline__ void stash(__bf16 *stage, int r0, int q) const {
-#pragma unroll
-    for (int i = 0; i < NP; ++i) *(uint4 *)(stage + (r0 + 64 * i) * PITCH + 8 * q) = v[i];
-  }
-};
-
-// One K-step of MFMAs for a wave: A rows arow0 + 16 i, B rows brow[j].
-__device__ __forceinline__ void mma_step(const __bf16 *As, const __bf16 *Bs, int arow0,
-                                         const int (&brow)[NJ], int lane, f32x4 (&acc)[MI][NJ]) {
-  const int r = lane & 15, kq = 8 * (lane >> 4);
-  bf16x8 a[MI], b[NJ];
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) b[j] = *(const bf16x8 *)(Bs + (brow[j] + r) * PITCH + kq);
-#pragma unroll
-  for (int i = 0; i < MI; ++i) a[i] = *(const bf16x8 *)(As + (arow0 + 16 * i + r) * PITCH + kq);
-#pragma unroll
-  for (int i = 0; i < MI; ++i)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-}
-
-// Full K loop over nk steps with double-buffered LDS.
-__device__ __forceinline__ void kloop(Smem &sm, RowLoader<A_PIECES> &la, RowLoader<B_PIECES> &lb,
-                                      int nk, int tid, int arow0, const int (&brow)[NJ],
-                                      f32x4 (&acc)[MI][NJ]) {
-  const int lane = tid & 63, r0 = tid >> 2, q = tid & 3;
-  la.fetch(0, q);
-  lb.fetch(0, q);
-  la.stash(sm.a[0], r0, q);
-  lb.stash(sm.b[0], r0, q);
-  __syncthreads();
-  for (int s = 0; s < nk; ++s) {
-    const int cur = s & 1;
-    if (s + 1 < nk) {
-      la.fetch((s + 1) * BK, q);
-      lb.fetch((s + 1) * BK, q);
-    }
-    mma_step(sm.a[cur], sm.b[cur], arow0, brow, lane, acc);
-    if (s + 1 < nk) {
-      la.stash(sm.a[cur ^ 1], r0, q);
-      lb.stash(sm.b[cur ^ 1], r0, q);
-    }
-    __syncthreads();
-  }
-}
-
-__device__ __forceinline__ void zero_acc(f32x4 (&acc)[MI][NJ]) {
-#pragma unroll
-  for (int i = 0; i < MI; ++i)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
 // Tile order inside a grid of (nm x nn) tiles: groups of GM row tiles, column
@@ -133,6 +76,85 @@ __device__ __forceinline__ void tile_of(int id, int nm, int nn, int &tm, int &tn
   tn = in / gm;
 }
 
+// Per-thread loader: the rows this thread copies into LDS (row (tid / KP) +
+// RPP i, 16-byte piece tid % KP). Rows outside the matrix point at a valid row
+// of it: every load is unconditional and nothing consumes the loaded value
+// before it is stored to LDS, so the loads of the next step stay in flight
+// behind the current step's MFMAs. The rows they feed are masked at the
+// epilogue (each output row or column depends only on its own operand row).
+template <class C, int NP>
+struct Loader {
+  const __bf16 *ptr[NP];
+  uint4 v[NP];
+  __device__ __forceinline__ void fetch(int k0, int q) {
+#pragma unroll
+    for (int i = 0; i < NP; ++i) v[i] = ld16(ptr[i] + k0 + 8 * q);
+  }
+  __device__ __forceinline__ void stash(__bf16 *stage, int r0, int q) const {
+#pragma unroll
+    for (int i = 0; i < NP; ++i) *(uint4 *)(stage + (r0 + C::RPP * i) * C::PITCH + 8 * q) = v[i];
+  }
+};
+
+template <class C>
+__device__ __forceinline__ void mma_stage(const __bf16 *As, const __bf16 *Bs, int arow0,
+                                          const int (&brow)[C::NJ], int lane,
+                                          f32x4 (&acc)[C::MI][C::NJ]) {
+  const int r = lane & 15, kq = 8 * (lane >> 4);
+#pragma unroll
+  for (int u = 0; u < C::BK / 32; ++u) {
+    bf16x8 a[C::MI], b[C::NJ];
+#pragma unroll
+    for (int j = 0; j < C::NJ; ++j)
+      b[j] = *(const bf16x8 *)(Bs + (brow[j] + r) * C::PITCH + 32 * u + kq);
+#pragma unroll
+    for (int i = 0; i < C::MI; ++i)
+      a[i] = *(const bf16x8 *)(As + (arow0 + 16 * i + r) * C::PITCH + 32 * u + kq);
+#pragma unroll
+    for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+      for (int j = 0; j < C::NJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  }
+}
+
+// Full K loop over nk steps of BK with double-buffered LDS.
+template <class C>
+__device__ __forceinline__ void kloop(__bf16 *smem, Loader<C, C::A_PIECES> &la,
+                                      Loader<C, C::B_PIECES> &lb, int nk, int tid, int arow0,
+                                      const int (&brow)[C::NJ], f32x4 (&acc)[C::MI][C::NJ]) {
+  // Stage addresses are formed arithmetically from the __shared__ base so the
+  // compiler keeps them in the LDS address space (ds_read / ds_write, not flat).
+  __bf16 *const Bbase = smem + 2 * C::A_STAGE;
+  const int lane = tid & 63, r0 = tid / C::KP, q = tid % C::KP;
+  la.fetch(0, q);
+  lb.fetch(0, q);
+  la.stash(smem, r0, q);
+  lb.stash(Bbase, r0, q);
+  __syncthreads();
+  for (int s = 0; s < nk; ++s) {
+    const int cur = s & 1;
+    if (s + 1 < nk) {
+      la.fetch((s + 1) * C::BK, q);
+      lb.fetch((s + 1) * C::BK, q);
+    }
+    mma_stage<C>(smem + cur * C::A_STAGE, Bbase + cur * C::B_STAGE, arow0, brow, lane, acc);
+    if (s + 1 < nk) {
+      la.stash(smem + (cur ^ 1) * C::A_STAGE, r0, q);
+      lb.stash(Bbase + (cur ^ 1) * C::B_STAGE, r0, q);
+    }
+    __syncthreads();
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void zero_acc(f32x4 (&acc)[C::MI][C::NJ]) {
+#pragma unroll
+  for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+    for (int j = 0; j < C::NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
 __device__ __forceinline__ int64_t slab_row_token(const Slab &s, int64_t p) {
   const int64_t j = p / s.Bp, i = p % s.Bp;
   if (i >= s.B || j >= s.nc) return -1;
@@ -141,47 +163,51 @@ __device__ __forceinline__ int64_t slab_row_token(const Slab &s, int64_t p) {
 }
 
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(NTHR) void k_gateup(Slab s, const __bf16 *__restrict__ x,
-                                                 const __bf16 *__restrict__ wg,
-                                                 const __bf16 *__restrict__ wu,
-                                                 __bf16 *__restrict__ z, __bf16 *__restrict__ zt) {
-  __shared__ Smem sm;
+template <class C>
+__global__ __launch_bounds__(C::NTHR) void k_gateup(Slab s, const __bf16 *__restrict__ x,
+                                                    const __bf16 *__restrict__ wg,
+                                                    const __bf16 *__restrict__ wu,
+                                                    __bf16 *__restrict__ z,
+                                                    __bf16 *__restrict__ zt) {
+  __shared__ __bf16 smem[C::SMEM_ELEMS];
+  constexpr int FT = C::BN / 2;  // d_ff columns per block
   const int P = s.nc * s.Bp;
-  const int nm = (P + BM - 1) / BM, nn = (s.F + 63) / 64;
+  const int nm = (P + C::BM - 1) / C::BM, nn = (s.F + FT - 1) / FT;
   const int per_seq = nm * nn;
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   const int n_seq = id / per_seq;
   int tm, tn;
   tile_of(id % per_seq, nm, nn, tm, tn);
-  const int m0 = tm * BM, f0 = tn * 64;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
-  const int r0 = tid >> 2;
+  const int m0 = tm * C::BM, f0 = tn * FT;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int r0 = tid / C::KP;
 
-  RowLoader<A_PIECES> la;
-  RowLoader<B_PIECES> lb;
+  Loader<C, C::A_PIECES> la;
+  Loader<C, C::B_PIECES> lb;
   const __bf16 *xs = x + n_seq * s.x_seq_stride;
 #pragma unroll
-  for (int i = 0; i < A_PIECES; ++i) {
-    const int p = m0 + r0 + 64 * i;
+  for (int i = 0; i < C::A_PIECES; ++i) {
+    const int p = m0 + r0 + C::RPP * i;
     const int64_t t = p < P ? slab_row_token(s, p) : -1;
-    la.ptr[i] = t >= 0 ? xs + t * s.d : nullptr;
+    la.ptr[i] = xs + (t >= 0 ? t : 0) * s.d;
   }
-  // B rows 0..63: gate rows f0.., 64..127: up rows f0..
 #pragma unroll
-  for (int i = 0; i < B_PIECES; ++i) {
-    const int rr = r0 + 64 * i;
-    const int f = f0 + (rr & 63);
-    lb.ptr[i] = f < s.F ? (rr < 64 ? wg : wu) + (int64_t)f * s.d : nullptr;
+  for (int i = 0; i < C::B_PIECES; ++i) {
+    const int rr = r0 + C::RPP * i;
+    const int f = f0 + (rr < FT ? rr : rr - FT);
+    const bool ok = f < s.F;
+    lb.ptr[i] = (rr < FT ? wg : wu) + (int64_t)(ok ? f : 0) * s.d;
   }
-  const int brow[NJ] = {wn * 32, wn * 32 + 16, 64 + wn * 32, 64 + wn * 32 + 16};
-  f32x4 acc[MI][NJ];
-  zero_acc(acc);
-  kloop(sm, la, lb, s.d / BK, tid, wm * 128, brow, acc);
+  const int brow[C::NJ] = {wn * 32, wn * 32 + 16, FT + wn * 32, FT + wn * 32 + 16};
+  f32x4 acc[C::MI][C::NJ];
+  zero_acc<C>(acc);
+  kloop<C>(smem, la, lb, s.d / C::BK, tid, wm * 128, brow, acc);
 
   __bf16 *zs = z + (int64_t)n_seq * s.Lp * s.F;
   __bf16 *zts = zt + (int64_t)n_seq * s.F * s.Lp;
 #pragma unroll
-  for (int i = 0; i < MI; ++i)
+  for (int i = 0; i < C::MI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int p = m0 + wm * 128 + 16 * i + 4 * (lane >> 4);
@@ -190,8 +216,10 @@ __global__ __launch_bounds__(NTHR) void k_gateup(Slab s, const __bf16 *__restric
         bf16x4 v;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
+          // chunk-padding rows (and tokens past the sequence end) are exact zeros
           const float g = acc[i][j][r], u = acc[i][j + 2][r];
-          v[r] = (__bf16)(g / (1.f + __expf(-g)) * u);
+          const bool real = slab_row_token(s, p + r) >= 0;
+          v[r] = (__bf16)(real ? g / (1.f + __expf(-g)) * u : 0.f);
         }
         *(bf16x4 *)(zts + (int64_t)f * s.Lp + p) = v;
 #pragma unroll
@@ -201,43 +229,45 @@ __global__ __launch_bounds__(NTHR) void k_gateup(Slab s, const __bf16 *__restric
 }
 
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(NTHR) void k_proj(Slab s, const __bf16 *__restrict__ c,
-                                               const __bf16 *__restrict__ proj,
-                                               __bf16 *__restrict__ vt, float scale) {
-  __shared__ Smem sm;
+template <class C>
+__global__ __launch_bounds__(C::NTHR) void k_proj(Slab s, const __bf16 *__restrict__ c,
+                                                  const __bf16 *__restrict__ proj,
+                                                  __bf16 *__restrict__ vt, float scale) {
+  __shared__ __bf16 smem[C::SMEM_ELEMS];
   const int P = s.nc * s.Bp;
-  const int nm = (P + BM - 1) / BM, nn = (s.d + BN - 1) / BN;
+  const int nm = (P + C::BM - 1) / C::BM, nn = (s.d + C::BN - 1) / C::BN;
   const int per_seq = nm * nn;
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   const int n_seq = id / per_seq;
   int tm, tn;
   tile_of(id % per_seq, nm, nn, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
-  const int r0 = tid >> 2;
-  RowLoader<A_PIECES> la;
-  RowLoader<B_PIECES> lb;
+  const int m0 = tm * C::BM, n0 = tn * C::BN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int r0 = tid / C::KP;
+  Loader<C, C::A_PIECES> la;
+  Loader<C, C::B_PIECES> lb;
   const __bf16 *cs = c + (int64_t)n_seq * s.Lp * s.d;
 #pragma unroll
-  for (int i = 0; i < A_PIECES; ++i) {
-    const int p = m0 + r0 + 64 * i;
-    la.ptr[i] = p < P ? cs + (int64_t)p * s.d : nullptr;
+  for (int i = 0; i < C::A_PIECES; ++i) {
+    const int p = m0 + r0 + C::RPP * i;
+    la.ptr[i] = cs + (int64_t)(p < P ? p : 0) * s.d;
   }
 #pragma unroll
-  for (int i = 0; i < B_PIECES; ++i) {
-    const int n = n0 + r0 + 64 * i;
-    lb.ptr[i] = n < s.d ? proj + (int64_t)n * s.d : nullptr;
+  for (int i = 0; i < C::B_PIECES; ++i) {
+    const int n = n0 + r0 + C::RPP * i;
+    lb.ptr[i] = proj + (int64_t)(n < s.d ? n : 0) * s.d;
   }
-  const int brow[NJ] = {wn * 64, wn * 64 + 16, wn * 64 + 32, wn * 64 + 48};
-  f32x4 acc[MI][NJ];
-  zero_acc(acc);
-  kloop(sm, la, lb, s.d / BK, tid, wm * 128, brow, acc);
+  const int brow[C::NJ] = {wn * 64, wn * 64 + 16, wn * 64 + 32, wn * 64 + 48};
+  f32x4 acc[C::MI][C::NJ];
+  zero_acc<C>(acc);
+  kloop<C>(smem, la, lb, s.d / C::BK, tid, wm * 128, brow, acc);
 
   __bf16 *vts = vt + (int64_t)n_seq * s.d * s.Lp;
 #pragma unroll
-  for (int i = 0; i < MI; ++i)
+  for (int i = 0; i < C::MI; ++i)
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
+    for (int j = 0; j < C::NJ; ++j) {
       const int p = m0 + wm * 128 + 16 * i + 4 * (lane >> 4);
       const int n = n0 + wn * 64 + 16 * j + (lane & 15);
       if (p < P && n < s.d) {
@@ -250,48 +280,53 @@ __global__ __launch_bounds__(NTHR) void k_proj(Slab s, const __bf16 *__restrict_
 }
 
 // ---------------------------------------------------------------------------
-// O rows of chunks [j0, j0 + nj) of every sequence: O_j = Z_j S_j^T-stored.
-__global__ __launch_bounds__(NTHR) void k_apply(Slab s, int j0, int nj, const __bf16 *__restrict__ z,
-                                                const __bf16 *__restrict__ snap,
-                                                int64_t snap_seq_stride, int64_t snap_chunk_stride,
-                                                float *__restrict__ o, const __bf16 *__restrict__ vt,
-                                                __bf16 *__restrict__ rt) {
-  __shared__ Smem sm;
-  const int nm = (s.Bp + BM - 1) / BM, nn = (s.d + BN - 1) / BN;
+// O rows of chunks [j0, j0 + nj) of every sequence: O_j = Z_j S_j (S_j stored
+// output-major, d rows of d_ff).
+template <class C>
+__global__ __launch_bounds__(C::NTHR) void k_apply(Slab s, int j0, int nj,
+                                                   const __bf16 *__restrict__ z,
+                                                   const __bf16 *__restrict__ snap,
+                                                   int64_t snap_seq_stride,
+                                                   int64_t snap_chunk_stride, float *__restrict__ o,
+                                                   const __bf16 *__restrict__ vt,
+                                                   __bf16 *__restrict__ rt) {
+  __shared__ __bf16 smem[C::SMEM_ELEMS];
+  const int nm = (s.Bp + C::BM - 1) / C::BM, nn = (s.d + C::BN - 1) / C::BN;
   const int per_chunk = nm * nn;
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   const int bz = id / per_chunk;
   const int n_seq = bz / nj, jl = bz % nj, j = j0 + jl;
   int tm, tn;
   tile_of(id % per_chunk, nm, nn, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
-  const int r0 = tid >> 2;
-  RowLoader<A_PIECES> la;
-  RowLoader<B_PIECES> lb;
+  const int m0 = tm * C::BM, n0 = tn * C::BN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int r0 = tid / C::KP;
+  Loader<C, C::A_PIECES> la;
+  Loader<C, C::B_PIECES> lb;
   const __bf16 *zs = z + (int64_t)n_seq * s.Lp * s.F + (int64_t)j * s.Bp * s.F;
   const __bf16 *ss = snap + n_seq * snap_seq_stride + jl * snap_chunk_stride;
 #pragma unroll
-  for (int i = 0; i < A_PIECES; ++i) {
-    const int m = m0 + r0 + 64 * i;
-    la.ptr[i] = m < s.Bp ? zs + (int64_t)m * s.F : nullptr;
+  for (int i = 0; i < C::A_PIECES; ++i) {
+    const int m = m0 + r0 + C::RPP * i;
+    la.ptr[i] = zs + (int64_t)(m < s.Bp ? m : 0) * s.F;
   }
 #pragma unroll
-  for (int i = 0; i < B_PIECES; ++i) {
-    const int n = n0 + r0 + 64 * i;
-    lb.ptr[i] = n < s.d ? ss + (int64_t)n * s.F : nullptr;
+  for (int i = 0; i < C::B_PIECES; ++i) {
+    const int n = n0 + r0 + C::RPP * i;
+    lb.ptr[i] = ss + (int64_t)(n < s.d ? n : 0) * s.F;
   }
-  const int brow[NJ] = {wn * 64, wn * 64 + 16, wn * 64 + 32, wn * 64 + 48};
-  f32x4 acc[MI][NJ];
-  zero_acc(acc);
-  kloop(sm, la, lb, s.F / BK, tid, wm * 128, brow, acc);
+  const int brow[C::NJ] = {wn * 64, wn * 64 + 16, wn * 64 + 32, wn * 64 + 48};
+  f32x4 acc[C::MI][C::NJ];
+  zero_acc<C>(acc);
+  kloop<C>(smem, la, lb, s.F / C::BK, tid, wm * 128, brow, acc);
 
   const int64_t chunk_tok0 = s.tok0 + (int64_t)j * s.B;
   float *os = o + n_seq * s.x_seq_stride;
 #pragma unroll
-  for (int i = 0; i < MI; ++i)
+  for (int i = 0; i < C::MI; ++i)
 #pragma unroll
-    for (int jj = 0; jj < NJ; ++jj) {
+    for (int jj = 0; jj < C::NJ; ++jj) {
       const int m = m0 + wm * 128 + 16 * i + 4 * (lane >> 4);
       const int n = n0 + wn * 64 + 16 * jj + (lane & 15);
       if (n >= s.d || m >= s.Bp) continue;
@@ -317,36 +352,36 @@ __global__ __launch_bounds__(NTHR) void k_apply(Slab s, int j0, int nj, const __
 
 // ---------------------------------------------------------------------------
 // W^T tile update: rows f (d_ff), columns c (d), K = tokens. The fp32 tile
-// lives in the accumulators for all chunks [j_first, j_first + n_chunks).
-// a_src = Zt (rows f, token-contiguous), b_src = Vt or Rt (rows c).
+// lives in the accumulators for chunks [j_first, j_first + n_chunks).
+// A operand = Zt (rows f, token-contiguous); B operand = Vt or Rt (rows c).
 // snap_each_chunk: write S[j] = bf16(W) before chunk j's accumulation;
 // snap_after: write S = bf16(W) after the last chunk.
-__global__ __launch_bounds__(NTHR) void k_update(Slab s, int j_first, int n_chunks,
-                                                 const __bf16 *__restrict__ zt,
-                                                 const __bf16 *__restrict__ bsrc, int64_t b_ld,
-                                                 int64_t b_seq_stride, int64_t b_chunk_stride,
-                                                 float *__restrict__ w, __bf16 *__restrict__ snap,
-                                                 int64_t snap_seq_stride, int64_t snap_chunk_stride,
-                                                 int snap_each_chunk, int snap_after) {
-  __shared__ Smem sm;
-  const int nm = (s.F + BM - 1) / BM, nn = (s.d + BN - 1) / BN;
+template <class C>
+__global__ __launch_bounds__(C::NTHR) void k_update(
+    Slab s, int j_first, int n_chunks, const __bf16 *__restrict__ zt,
+    const __bf16 *__restrict__ bsrc, int64_t b_ld, int64_t b_seq_stride, int64_t b_chunk_stride,
+    float *__restrict__ w, __bf16 *__restrict__ snap, int64_t snap_seq_stride,
+    int64_t snap_chunk_stride, int snap_each_chunk, int snap_after) {
+  __shared__ __bf16 smem[C::SMEM_ELEMS];
+  const int nm = (s.F + C::BM - 1) / C::BM, nn = (s.d + C::BN - 1) / C::BN;
   const int per_seq = nm * nn;
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   const int n_seq = id / per_seq;
   int tm, tn;
   tile_of(id % per_seq, nm, nn, tm, tn);
-  const int f0 = tm * BM, c0 = tn * BN;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
-  const int r0 = tid >> 2, q = tid & 3;
+  const int f0 = tm * C::BM, c0 = tn * C::BN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int r0 = tid / C::KP;
   const int64_t dF = (int64_t)s.d * s.F;
   float *ws = w + n_seq * dF;
 
   // accumulators <- W tile: lane holds W^T[c][f .. f+3]
-  f32x4 acc[MI][NJ];
+  f32x4 acc[C::MI][C::NJ];
 #pragma unroll
-  for (int i = 0; i < MI; ++i)
+  for (int i = 0; i < C::MI; ++i)
 #pragma unroll
-    for (int jj = 0; jj < NJ; ++jj) {
+    for (int jj = 0; jj < C::NJ; ++jj) {
       const int f = f0 + wm * 128 + 16 * i + 4 * (lane >> 4);
       const int c = c0 + wn * 64 + 16 * jj + (lane & 15);
       acc[i][jj] = (f < s.F && c < s.d) ? *(const f32x4 *)(ws + (int64_t)c * s.F + f)
@@ -354,9 +389,9 @@ __global__ __launch_bounds__(NTHR) void k_update(Slab s, int j_first, int n_chun
     }
   auto write_snap = [&](__bf16 *dst) {
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+    for (int i = 0; i < C::MI; ++i)
 #pragma unroll
-      for (int jj = 0; jj < NJ; ++jj) {
+      for (int jj = 0; jj < C::NJ; ++jj) {
         const int f = f0 + wm * 128 + 16 * i + 4 * (lane >> 4);
         const int c = c0 + wn * 64 + 16 * jj + (lane & 15);
         if (f < s.F && c < s.d) {
@@ -368,91 +403,206 @@ __global__ __launch_bounds__(NTHR) void k_update(Slab s, int j_first, int n_chun
       }
   };
 
-  RowLoader<A_PIECES> la;
-  RowLoader<B_PIECES> lb;
-  const int brow[NJ] = {wn * 64, wn * 64 + 16, wn * 64 + 32, wn * 64 + 48};
-  const int steps = s.Bp / BK;
+  Loader<C, C::A_PIECES> la;
+  Loader<C, C::B_PIECES> lb;
+  const int brow[C::NJ] = {wn * 64, wn * 64 + 16, wn * 64 + 32, wn * 64 + 48};
+  const int steps = s.Bp / C::BK;
+  const __bf16 *zts = zt + (int64_t)n_seq * s.F * s.Lp;
+  const __bf16 *bs = bsrc + n_seq * b_seq_stride;
   for (int jc = 0; jc < n_chunks; ++jc) {
     const int j = j_first + jc;
     if (snap_each_chunk) write_snap(snap + n_seq * snap_seq_stride + jc * snap_chunk_stride);
-#pragma unroll
-    for (int i = 0; i < A_PIECES; ++i) {
-      const int f = f0 + r0 + 64 * i;
-      la.ptr[i] = f < s.F ? zt + (int64_t)n_seq * s.F * s.Lp + (int64_t)f * s.Lp + (int64_t)j * s.Bp
-                          : nullptr;
+  #pragma unroll
+    for (int i = 0; i < C::A_PIECES; ++i) {
+      const int f = f0 + r0 + C::RPP * i;
+      la.ptr[i] = zts + (int64_t)(f < s.F ? f : 0) * s.Lp + (int64_t)j * s.Bp;
     }
 #pragma unroll
-    for (int i = 0; i < B_PIECES; ++i) {
-      const int c = c0 + r0 + 64 * i;
-      lb.ptr[i] = c < s.d ? bsrc + n_seq * b_seq_stride + (int64_t)c * b_ld + jc * b_chunk_stride
-                          : nullptr;
+    for (int i = 0; i < C::B_PIECES; ++i) {
+      const int c = c0 + r0 + C::RPP * i;
+      lb.ptr[i] = bs + (int64_t)(c < s.d ? c : 0) * b_ld + jc * b_chunk_stride;
     }
-    kloop(sm, la, lb, steps, tid, wm * 128, brow, acc);
+    kloop<C>(smem, la, lb, steps, tid, wm * 128, brow, acc);
   }
   if (snap_after) write_snap(snap + n_seq * snap_seq_stride);
 #pragma unroll
-  for (int i = 0; i < MI; ++i)
+  for (int i = 0; i < C::MI; ++i)
 #pragma unroll
-    for (int jj = 0; jj < NJ; ++jj) {
+    for (int jj = 0; jj < C::NJ; ++jj) {
       const int f = f0 + wm * 128 + 16 * i + 4 * (lane >> 4);
       const int c = c0 + wn * 64 + 16 * jj + (lane & 15);
       if (f < s.F && c < s.d) *(f32x4 *)(ws + (int64_t)c * s.F + f) = acc[i][jj];
     }
 }
 
-inline unsigned blocks(int64_t n) { return (unsigned)n; }
+// ---------------------------------------------------------------------------
+// Depthwise conv of the token embeddings, bf16 path: C[p][c] = sum_j w[c][j]
+// E[t + j][c] with E taken as 0 past the chunk's end (pad rows: 0). A thread
+// owns 8 channels (one 16-byte vector) over RUN consecutive rows of one chunk
+// and keeps the KC-row window in registers, so each E row is read about once.
+// Arithmetic in fp32, result rounded to bf16.
+constexpr int CONV_RUN = 16;
 
-}  // namespace
+template <int KC>
+__global__ __launch_bounds__(256) void k_conv(Slab s, const __bf16 *__restrict__ e,
+                                              const __bf16 *__restrict__ cw,
+                                              __bf16 *__restrict__ c) {
+  const int groups = s.d / 8;
+  const int64_t runs_per_seq = (int64_t)s.nc * (s.Bp / CONV_RUN);
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = runs_per_seq * groups * s.n_seq;
+  if (gid >= total) return;
+  const int g = (int)(gid % groups);
+  const int64_t run = (gid / groups) % runs_per_seq;
+  const int n_seq = (int)(gid / groups / runs_per_seq);
+  const int64_t p0 = run * CONV_RUN;
+  const int64_t j = p0 / s.Bp, i0 = p0 % s.Bp;
+  const int64_t cs = s.tok0 + j * s.B;                 // chunk's first token
+  const int64_t ce = min(cs + (int64_t)s.B, s.L);      // one past its last token
+  const int ch = 8 * g;
+  float w[KC][8];
+#pragma unroll
+  for (int q = 0; q < KC; ++q)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) w[q][k] = (float)cw[(ch + k) * KC + q];
+  const __bf16 *es = e + n_seq * s.x_seq_stride + ch;
+  bf16x8 win[CONV_RUN + KC - 1];
+#pragma unroll
+  for (int r = 0; r < CONV_RUN + KC - 1; ++r) {
+    const int64_t t = cs + i0 + r;
+    const bool in = (i0 + r < s.B) && t < ce;
+    win[r] = in ? *(const bf16x8 *)(es + t * s.d) : bf16x8{};
+  }
+  __bf16 *cp = c + (int64_t)n_seq * s.Lp * s.d + p0 * s.d + ch;
+#pragma unroll
+  for (int i = 0; i < CONV_RUN; ++i) {
+    const bool real = (i0 + i < s.B) && (cs + i0 + i < ce);
+    bf16x8 out;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      float a = 0.f;
+#pragma unroll
+      for (int q = 0; q < KC; ++q) a = fmaf(w[q][k], (float)win[i + q][k], a);
+      out[k] = (__bf16)(real ? a : 0.f);
+    }
+    *(bf16x8 *)(cp + (int64_t)i * s.d) = out;
+  }
+}
 
-bool mfma_supported(int d, int F) { return d % BK == 0 && F % BK == 0; }
-
-hipError_t mf_gateup(const Slab &s, const __bf16 *x, const Weights &w, const WsPtrs &ws,
-                     hipStream_t st) {
+// ---- launchers (templated on the block configuration) ---------------------
+template <class C>
+hipError_t launch_gateup(const Slab &s, const __bf16 *x, const Weights &w, const WsPtrs &ws,
+                         hipStream_t st) {
   const int64_t P = (int64_t)s.nc * s.Bp;
-  const int64_t nb = ((P + BM - 1) / BM) * ((s.F + 63) / 64) * s.n_seq;
-  hipLaunchKernelGGL(k_gateup, dim3(blocks(nb)), dim3(NTHR), 0, st, s, x, (const __bf16 *)w.w_gate,
-                     (const __bf16 *)w.w_up, (__bf16 *)ws.z, (__bf16 *)ws.zt);
+  const int64_t nb = ((P + C::BM - 1) / C::BM) * ((s.F + C::BN / 2 - 1) / (C::BN / 2)) * s.n_seq;
+  hipLaunchKernelGGL(k_gateup<C>, dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, x,
+                     (const __bf16 *)w.w_gate, (const __bf16 *)w.w_up, (__bf16 *)ws.z,
+                     (__bf16 *)ws.zt);
   return hipGetLastError();
 }
 
-hipError_t mf_proj(const Slab &s, const Weights &w, const WsPtrs &ws, hipStream_t st) {
+template <class C>
+hipError_t launch_proj(const Slab &s, const Weights &w, const WsPtrs &ws, hipStream_t st) {
   const int64_t P = (int64_t)s.nc * s.Bp;
-  const int64_t nb = ((P + BM - 1) / BM) * ((s.d + BN - 1) / BN) * s.n_seq;
-  hipLaunchKernelGGL(k_proj, dim3(blocks(nb)), dim3(NTHR), 0, st, s, (const __bf16 *)ws.c,
+  const int64_t nb = ((P + C::BM - 1) / C::BM) * ((s.d + C::BN - 1) / C::BN) * s.n_seq;
+  hipLaunchKernelGGL(k_proj<C>, dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, (const __bf16 *)ws.c,
                      (const __bf16 *)w.proj, (__bf16 *)ws.vt, s.mse ? 1.f : s.eta);
   return hipGetLastError();
 }
 
-hipError_t mf_apply(const Slab &s, int j0, int nj, const WsPtrs &ws, float *o, hipStream_t st) {
+template <class C>
+hipError_t launch_apply(const Slab &s, int j0, int nj, const WsPtrs &ws, float *o,
+                        hipStream_t st) {
   const int64_t dF = (int64_t)s.d * s.F;
   const int64_t snap_seq = s.mse ? dF : (int64_t)s.nc_cap * dF;
   const int64_t snap_chunk = s.mse ? 0 : dF;
   const __bf16 *snap = (const __bf16 *)ws.s + (s.mse ? 0 : (int64_t)j0 * dF);
-  const int64_t nb = ((s.Bp + BM - 1) / BM) * ((s.d + BN - 1) / BN) * (int64_t)nj * s.n_seq;
-  hipLaunchKernelGGL(k_apply, dim3(blocks(nb)), dim3(NTHR), 0, st, s, j0, nj,
+  const int64_t nb =
+      ((s.Bp + C::BM - 1) / C::BM) * ((s.d + C::BN - 1) / C::BN) * (int64_t)nj * s.n_seq;
+  hipLaunchKernelGGL(k_apply<C>, dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, j0, nj,
                      (const __bf16 *)ws.z, snap, snap_seq, snap_chunk, o, (const __bf16 *)ws.vt,
                      s.mse ? (__bf16 *)ws.rt : nullptr);
   return hipGetLastError();
 }
 
-hipError_t mf_update_scan(const Slab &s, const WsPtrs &ws, float *w_state, hipStream_t st) {
+template <class C>
+hipError_t launch_update_scan(const Slab &s, const WsPtrs &ws, float *w_state, hipStream_t st) {
   const int64_t dF = (int64_t)s.d * s.F;
-  const int64_t nb = ((s.F + BM - 1) / BM) * ((s.d + BN - 1) / BN) * s.n_seq;
-  // B operand: Vt rows c, chunk jc at column offset jc * Bp
-  hipLaunchKernelGGL(k_update, dim3(blocks(nb)), dim3(NTHR), 0, st, s, 0, s.nc,
+  const int64_t nb = ((s.F + C::BM - 1) / C::BM) * ((s.d + C::BN - 1) / C::BN) * s.n_seq;
+  // B operand: Vt rows c; chunk jc starts jc * Bp tokens along the row
+  hipLaunchKernelGGL(k_update<C>, dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, 0, s.nc,
                      (const __bf16 *)ws.zt, (const __bf16 *)ws.vt, s.Lp, (int64_t)s.d * s.Lp,
                      (int64_t)s.Bp, w_state, (__bf16 *)ws.s, (int64_t)s.nc_cap * dF, dF, 1, 0);
   return hipGetLastError();
 }
 
-hipError_t mf_update_one(const Slab &s, int j, const WsPtrs &ws, float *w_state, hipStream_t st) {
+template <class C>
+hipError_t launch_update_one(const Slab &s, int j, const WsPtrs &ws, float *w_state,
+                             hipStream_t st) {
   const int64_t dF = (int64_t)s.d * s.F;
-  const int64_t nb = ((s.F + BM - 1) / BM) * ((s.d + BN - 1) / BN) * s.n_seq;
+  const int64_t nb = ((s.F + C::BM - 1) / C::BM) * ((s.d + C::BN - 1) / C::BN) * s.n_seq;
   // B operand: Rt [n][d][Bp] of chunk j
-  hipLaunchKernelGGL(k_update, dim3(blocks(nb)), dim3(NTHR), 0, st, s, j, 1,
+  hipLaunchKernelGGL(k_update<C>, dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, j, 1,
                      (const __bf16 *)ws.zt, (const __bf16 *)ws.rt, (int64_t)s.Bp,
-                     (int64_t)s.d * s.Bp, (int64_t)0, w_state, (__bf16 *)ws.s, dF, (int64_t)0, 0, 1);
+                     (int64_t)s.d * s.Bp, (int64_t)0, w_state, (__bf16 *)ws.s, dF, (int64_t)0, 0,
+                     1);
   return hipGetLastError();
+}
+
+// Block shapes chosen by timing on MI355X at the 4B layer shape (d 2560,
+// d_ff 9728, 16 chunks of 1024): 8 waves over 256 x 256 with K steps of 64 for
+// the long-K products, 2 waves over 128 x 128 for the update (more, smaller
+// blocks: each one streams every chunk of the slab).
+using GateUpCfg = Cfg<2, 4, 64>;
+using ProjCfg = Cfg<2, 4, 32>;
+using ApplyCfg = Cfg<2, 4, 64>;
+using UpdateCfg = Cfg<1, 2, 64>;
+static_assert(kChunkAlign % UpdateCfg::BK == 0, "chunk pitch must be whole update K steps");
+
+template <int KC>
+hipError_t launch_conv(const Slab &s, const __bf16 *e, const Weights &w, const WsPtrs &ws,
+                       hipStream_t st) {
+  const int64_t total = (int64_t)s.nc * (s.Bp / CONV_RUN) * (s.d / 8) * s.n_seq;
+  hipLaunchKernelGGL(k_conv<KC>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, s, e,
+                     (const __bf16 *)w.conv_w, (__bf16 *)ws.c);
+  return hipGetLastError();
+}
+static_assert(kChunkAlign % CONV_RUN == 0, "conv runs must not cross a chunk");
+
+}  // namespace mfma
+
+bool mfma_supported(int d, int F) { return d % 64 == 0 && F % 64 == 0; }
+
+hipError_t mf_conv(const Slab &s, const __bf16 *e, const Weights &w, const WsPtrs &ws,
+                   hipStream_t st) {
+  switch (s.Kc) {
+    case 1: return mfma::launch_conv<1>(s, e, w, ws, st);
+    case 2: return mfma::launch_conv<2>(s, e, w, ws, st);
+    case 3: return mfma::launch_conv<3>(s, e, w, ws, st);
+    case 4: return mfma::launch_conv<4>(s, e, w, ws, st);
+    case 5: return mfma::launch_conv<5>(s, e, w, ws, st);
+    case 6: return mfma::launch_conv<6>(s, e, w, ws, st);
+    case 7: return mfma::launch_conv<7>(s, e, w, ws, st);
+    case 8: return mfma::launch_conv<8>(s, e, w, ws, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t mf_gateup(const Slab &s, const __bf16 *x, const Weights &w, const WsPtrs &ws,
+                     hipStream_t st) {
+  return mfma::launch_gateup<mfma::GateUpCfg>(s, x, w, ws, st);
+}
+hipError_t mf_proj(const Slab &s, const Weights &w, const WsPtrs &ws, hipStream_t st) {
+  return mfma::launch_proj<mfma::ProjCfg>(s, w, ws, st);
+}
+hipError_t mf_apply(const Slab &s, int j0, int nj, const WsPtrs &ws, float *o, hipStream_t st) {
+  return mfma::launch_apply<mfma::ApplyCfg>(s, j0, nj, ws, o, st);
+}
+hipError_t mf_update_scan(const Slab &s, const WsPtrs &ws, float *w_state, hipStream_t st) {
+  return mfma::launch_update_scan<mfma::UpdateCfg>(s, ws, w_state, st);
+}
+hipError_t mf_update_one(const Slab &s, int j, const WsPtrs &ws, float *w_state, hipStream_t st) {
+  return mfma::launch_update_one<mfma::UpdateCfg>(s, j, ws, w_state, st);
 }
 
 }  // namespace ipttt

@@ -119,7 +119,8 @@ ipttt_status ipttt_init(const ipttt_layer_desc *desc, ipttt_layer **out);
  * w_state. batch == 0 or seq_len == 0 is a successful no-op. Fails with
  * IPTTT_E_STATE if a slot in range was never reset, IPTTT_E_WORKSPACE if the
  * workspace cannot hold one chunk of `batch` sequences, IPTTT_E_INVALID for
- * batch > max_batch, null or misaligned pointers. */
+ * batch > max_batch, null or misaligned pointers (x and e must be 16-byte
+ * aligned on the bf16 MFMA path, element-aligned otherwise; o 4-byte). */
 ipttt_status ipttt_prefill_layer(ipttt_layer *h, const void *x, const void *e, float *o,
                                  int32_t batch, int64_t seq_len, void *hip_stream);
 
