@@ -36,11 +36,12 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-template <int WM_, int WN_, int BK_>
+template <int WM_, int WN_, int BK_, int NJ_ = 4>
 struct Cfg {
   static constexpr int WM = WM_, WN = WN_, BK = BK_;
-  static constexpr int MI = 8, NJ = 4;  // 16x16 tiles per wave: 128 x 64
-  static constexpr int BM = 128 * WM, BN = 64 * WN;
+  static constexpr int MI = 8, NJ = NJ_;  // 16x16 tiles per wave: 128 x (16 NJ)
+  static constexpr int WTN = 16 * NJ;     // wave tile width
+  static constexpr int BM = 128 * WM, BN = WTN * WN;
   static constexpr int NTHR = 64 * WM * WN;
   static constexpr int PITCH = BK + 8;  // LDS row pitch in bf16
   static constexpr int KP = BK / 8;     // 16-byte pieces per row per step
@@ -199,7 +200,14 @@ __global__ __launch_bounds__(C::NTHR) void k_gateup(Slab s, const __bf16 *__rest
     const bool ok = f < s.F;
     lb.ptr[i] = (rr < FT ? wg : wu) + (int64_t)(ok ? f : 0) * s.d;
   }
-  const int brow[C::NJ] = {wn * 32, wn * 32 + 16, FT + wn * 32, FT + wn * 32 + 16};
+  // a wave's first NJ/2 B tiles are gate rows, the other NJ/2 the matching up rows
+  constexpr int HJ = C::NJ / 2;
+  int brow[C::NJ];
+#pragma unroll
+  for (int j = 0; j < HJ; ++j) {
+    brow[j] = wn * 16 * HJ + 16 * j;
+    brow[j + HJ] = FT + wn * 16 * HJ + 16 * j;
+  }
   f32x4 acc[C::MI][C::NJ];
   zero_acc<C>(acc);
   kloop<C>(smem, la, lb, s.d / C::BK, tid, wm * 128, brow, acc);
@@ -209,15 +217,15 @@ __global__ __launch_bounds__(C::NTHR) void k_gateup(Slab s, const __bf16 *__rest
 #pragma unroll
   for (int i = 0; i < C::MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < HJ; ++j) {
       const int p = m0 + wm * 128 + 16 * i + 4 * (lane >> 4);
-      const int f = f0 + wn * 32 + 16 * j + (lane & 15);
+      const int f = f0 + wn * 16 * HJ + 16 * j + (lane & 15);
       if (p < P && f < s.F) {
         bf16x4 v;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           // chunk-padding rows (and tokens past the sequence end) are exact zeros
-          const float g = acc[i][j][r], u = acc[i][j + 2][r];
+          const float g = acc[i][j][r], u = acc[i][j + HJ][r];
           const bool real = slab_row_token(s, p + r) >= 0;
           v[r] = (__bf16)(real ? g / (1.f + __expf(-g)) * u : 0.f);
         }
@@ -258,7 +266,9 @@ __global__ __launch_bounds__(C::NTHR) void k_proj(Slab s, const __bf16 *__restri
     const int n = n0 + r0 + C::RPP * i;
     lb.ptr[i] = proj + (int64_t)(n < s.d ? n : 0) * s.d;
   }
-  const int brow[C::NJ] = {wn * 64, wn * 64 + 16, wn * 64 + 32, wn * 64 + 48};
+  int brow[C::NJ];
+#pragma unroll
+  for (int j = 0; j < C::NJ; ++j) brow[j] = wn * C::WTN + 16 * j;
   f32x4 acc[C::MI][C::NJ];
   zero_acc<C>(acc);
   kloop<C>(smem, la, lb, s.d / C::BK, tid, wm * 128, brow, acc);
@@ -269,7 +279,7 @@ __global__ __launch_bounds__(C::NTHR) void k_proj(Slab s, const __bf16 *__restri
 #pragma unroll
     for (int j = 0; j < C::NJ; ++j) {
       const int p = m0 + wm * 128 + 16 * i + 4 * (lane >> 4);
-      const int n = n0 + wn * 64 + 16 * j + (lane & 15);
+      const int n = n0 + wn * C::WTN + 16 * j + (lane & 15);
       if (p < P && n < s.d) {
         bf16x4 v;
 #pragma unroll
@@ -316,7 +326,9 @@ __global__ __launch_bounds__(C::NTHR) void k_apply(Slab s, int j0, int nj,
     const int n = n0 + r0 + C::RPP * i;
     lb.ptr[i] = ss + (int64_t)(n < s.d ? n : 0) * s.F;
   }
-  const int brow[C::NJ] = {wn * 64, wn * 64 + 16, wn * 64 + 32, wn * 64 + 48};
+  int brow[C::NJ];
+#pragma unroll
+  for (int j = 0; j < C::NJ; ++j) brow[j] = wn * C::WTN + 16 * j;
   f32x4 acc[C::MI][C::NJ];
   zero_acc<C>(acc);
   kloop<C>(smem, la, lb, s.F / C::BK, tid, wm * 128, brow, acc);
@@ -328,7 +340,7 @@ __global__ __launch_bounds__(C::NTHR) void k_apply(Slab s, int j0, int nj,
 #pragma unroll
     for (int jj = 0; jj < C::NJ; ++jj) {
       const int m = m0 + wm * 128 + 16 * i + 4 * (lane >> 4);
-      const int n = n0 + wn * 64 + 16 * jj + (lane & 15);
+      const int n = n0 + wn * C::WTN + 16 * jj + (lane & 15);
       if (n >= s.d || m >= s.Bp) continue;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -383,7 +395,7 @@ __global__ __launch_bounds__(C::NTHR) void k_update(
 #pragma unroll
     for (int jj = 0; jj < C::NJ; ++jj) {
       const int f = f0 + wm * 128 + 16 * i + 4 * (lane >> 4);
-      const int c = c0 + wn * 64 + 16 * jj + (lane & 15);
+      const int c = c0 + wn * C::WTN + 16 * jj + (lane & 15);
       acc[i][jj] = (f < s.F && c < s.d) ? *(const f32x4 *)(ws + (int64_t)c * s.F + f)
                                          : f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -393,7 +405,7 @@ __global__ __launch_bounds__(C::NTHR) void k_update(
 #pragma unroll
       for (int jj = 0; jj < C::NJ; ++jj) {
         const int f = f0 + wm * 128 + 16 * i + 4 * (lane >> 4);
-        const int c = c0 + wn * 64 + 16 * jj + (lane & 15);
+        const int c = c0 + wn * C::WTN + 16 * jj + (lane & 15);
         if (f < s.F && c < s.d) {
           bf16x4 v;
 #pragma unroll
@@ -405,7 +417,9 @@ __global__ __launch_bounds__(C::NTHR) void k_update(
 
   Loader<C, C::A_PIECES> la;
   Loader<C, C::B_PIECES> lb;
-  const int brow[C::NJ] = {wn * 64, wn * 64 + 16, wn * 64 + 32, wn * 64 + 48};
+  int brow[C::NJ];
+#pragma unroll
+  for (int j = 0; j < C::NJ; ++j) brow[j] = wn * C::WTN + 16 * j;
   const int steps = s.Bp / C::BK;
   const __bf16 *zts = zt + (int64_t)n_seq * s.F * s.Lp;
   const __bf16 *bs = bsrc + n_seq * b_seq_stride;
@@ -430,7 +444,7 @@ __global__ __launch_bounds__(C::NTHR) void k_update(
 #pragma unroll
     for (int jj = 0; jj < C::NJ; ++jj) {
       const int f = f0 + wm * 128 + 16 * i + 4 * (lane >> 4);
-      const int c = c0 + wn * 64 + 16 * jj + (lane & 15);
+      const int c = c0 + wn * C::WTN + 16 * jj + (lane & 15);
       if (f < s.F && c < s.d) *(f32x4 *)(ws + (int64_t)c * s.F + f) = acc[i][jj];
     }
 }
