@@ -37,11 +37,12 @@ struct WsLayout {
   size_t z, zt, c, vt, s, rt, total;
 };
 
-WsLayout ws_layout(int elem, int n_seq, int d, int F, int Bp, int nc_cap, int mse);
+// need_z: the token-major copy of Z (read by the generic apply only).
+WsLayout ws_layout(int elem, int n_seq, int d, int F, int Bp, int nc_cap, int mse, int need_z);
 
 // Pointers into the workspace for one call.
 struct WsPtrs {
-  void *z;   // [n][Lp][F]      Z, token-major
+  void *z;   // [n][Lp][F]      Z, token-major (generic path only)
   void *zt;  // [n][F][Lp]      Z transposed (token-contiguous)
   void *c;   // [n][Lp][d]      conv output
   void *vt;  // [n][d][Lp]      target V transposed; eta*V for the linear rule

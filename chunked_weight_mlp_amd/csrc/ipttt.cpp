@@ -131,7 +131,7 @@ struct ProfScope {
 
 namespace ipttt {
 
-WsLayout ws_layout(int elem, int n_seq, int d, int F, int Bp, int nc_cap, int mse) {
+WsLayout ws_layout(int elem, int n_seq, int d, int F, int Bp, int nc_cap, int mse, int need_z) {
   WsLayout w{};
   const size_t Lp = (size_t)nc_cap * Bp;
   size_t off = 0;
@@ -140,7 +140,7 @@ WsLayout ws_layout(int elem, int n_seq, int d, int F, int Bp, int nc_cap, int ms
     off += (size_t)round_up((int64_t)bytes, 256);
     return o;
   };
-  w.z = take((size_t)n_seq * Lp * F * elem);
+  w.z = take(need_z ? (size_t)n_seq * Lp * F * elem : 0);
   w.zt = take((size_t)n_seq * F * Lp * elem);
   w.c = take((size_t)n_seq * Lp * d * elem);
   w.vt = take((size_t)n_seq * d * Lp * elem);
@@ -174,7 +174,8 @@ size_t ipttt_workspace_bytes(const ipttt_layer_desc *desc, int32_t batch, int32_
   g_last_error = saved;
   if (s != IPTTT_OK || batch < 1 || slab_chunks < 1) return 0;
   return ipttt::ws_layout(elem_size(desc->in_dtype), batch, desc->d, desc->d_ff,
-                          chunk_pitch(desc->chunk), slab_chunks, desc->update == IPTTT_UPDATE_MSE)
+                          chunk_pitch(desc->chunk), slab_chunks, desc->update == IPTTT_UPDATE_MSE,
+                          !use_mfma(desc))
       .total;
 }
 
@@ -280,18 +281,18 @@ ipttt_status run_scan(ipttt_layer *h, const T *x, const T *e, float *o, int slot
   const int64_t K = (L + B - 1) / B;
   // largest slab that fits the workspace
   int64_t lo = 1, hi = K;
-  if (ws_layout(elem, n_seq, d.d, d.d_ff, Bp, 1, mse).total > d.workspace_bytes)
+  if (ws_layout(elem, n_seq, d.d, d.d_ff, Bp, 1, mse, !h->mfma).total > d.workspace_bytes)
     return fail(IPTTT_E_WORKSPACE, "workspace_bytes=%zu cannot hold one chunk of %d sequences (%zu)",
-                d.workspace_bytes, n_seq, ws_layout(elem, n_seq, d.d, d.d_ff, Bp, 1, mse).total);
+                d.workspace_bytes, n_seq, ws_layout(elem, n_seq, d.d, d.d_ff, Bp, 1, mse, !h->mfma).total);
   while (lo < hi) {
     const int64_t mid = (lo + hi + 1) / 2;
-    if (ws_layout(elem, n_seq, d.d, d.d_ff, Bp, (int)mid, mse).total <= d.workspace_bytes)
+    if (ws_layout(elem, n_seq, d.d, d.d_ff, Bp, (int)mid, mse, !h->mfma).total <= d.workspace_bytes)
       lo = mid;
     else
       hi = mid - 1;
   }
   const int nc_cap = (int)lo;
-  const WsLayout lay = ws_layout(elem, n_seq, d.d, d.d_ff, Bp, nc_cap, mse);
+  const WsLayout lay = ws_layout(elem, n_seq, d.d, d.d_ff, Bp, nc_cap, mse, !h->mfma);
   char *base = (char *)d.workspace;
   WsPtrs ws{base + lay.z, base + lay.zt, base + lay.c, base + lay.vt, base + lay.s, base + lay.rt};
   Weights w{d.w_gate, d.w_up, d.proj, d.conv_w};

@@ -17,12 +17,12 @@
 //
 // Kernels:
 //   k_gateup   Z = SiLU(X W_g) * (X W_u)   M = slab rows, N = d_ff (half the
-//              block's B rows are gate rows, half up rows), K = d. Writes Z
-//              (token-major) and Zt (token-contiguous).
+//              block's B rows are gate rows, half up rows), K = d. Writes Zt
+//              (rows of d_ff, token-contiguous), the only copy of Z.
 //   k_proj     Vt = scale * (C Proj)^T     M = slab rows, N = d, K = d.
 //   k_apply    O = Z_j S_j                 M = chunk rows, N = d, K = d_ff,
-//              batched over (sequence, chunk); the MSE rule also writes
-//              Rt = eta (V - O)^T.
+//              batched over (sequence, chunk); A comes from Zt through LDS
+//              transpose reads. The MSE rule also writes Rt = eta (V - O)^T.
 //   k_update   W^T tile (BM d_ff rows x BN d columns, fp32) held in the
 //              accumulators across the chunks of a slab: per chunk, optionally
 //              write the bf16 snapshot S_j, then accumulate Zt_j . Vt_j over
@@ -50,7 +50,14 @@ struct Cfg {
   static constexpr int B_PIECES = BN / RPP;
   static constexpr int A_STAGE = BM * PITCH, B_STAGE = BN * PITCH;
   static constexpr int SMEM_ELEMS = 2 * (A_STAGE + B_STAGE);
+  // A held K-major in LDS ([BK rows of K][BM columns of M], for an A operand
+  // that is stored M-contiguous in memory): rows padded by 32 bytes.
+  static constexpr int PITCH_T = BM + 16;
+  static constexpr int AT_PIECES = BK * (BM / 8) / NTHR;
+  static constexpr int AT_STAGE = BK * PITCH_T;
+  static constexpr int SMEM_T_ELEMS = 2 * (AT_STAGE + B_STAGE);
   static_assert(BK % 32 == 0 && BM % RPP == 0 && BN % RPP == 0, "bad tile config");
+  static_assert((BK * (BM / 8)) % NTHR == 0, "bad transposed-A tile config");
   static_assert(SMEM_ELEMS * 2 <= 160 * 1024, "LDS overflow");
 };
 
@@ -148,6 +155,90 @@ __device__ __forceinline__ void kloop(__bf16 *smem, Loader<C, C::A_PIECES> &la,
   }
 }
 
+// ---- A operand stored M-contiguous (K-major rows) ---------------------------
+// The tile is copied into LDS as BK rows of BM elements; each MFMA A fragment
+// (row m = lane % 16, K values 8 g .. 8 g + 7 for g = lane / 16) is assembled
+// from two ds_read_b64_tr_b16. That instruction works on groups of 16 lanes:
+// lane i of a group receives element (i % 4) of the 8-byte chunk read by lane
+// 4 j + i / 4 of the group, for j = 0..3. Source lane p therefore points at K
+// row (p / 4) and M columns 4 (p % 4) .. + 3 of a 4 x 16 block, and lane i gets
+// that block's column i: 4 consecutive K values of M row i.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+template <class C>
+struct LoaderT {
+  const __bf16 *ptr[C::AT_PIECES];  // K row start, already offset to this thread's M piece
+  int64_t ld;                       // elements between K rows
+  uint4 v[C::AT_PIECES];
+  __device__ __forceinline__ void fetch(int k0) {
+#pragma unroll
+    for (int i = 0; i < C::AT_PIECES; ++i) v[i] = ld16(ptr[i] + (int64_t)k0 * ld);
+  }
+  __device__ __forceinline__ void stash(__bf16 *stage, int tid) const {
+#pragma unroll
+    for (int i = 0; i < C::AT_PIECES; ++i) {
+      const int id = tid + i * C::NTHR;
+      *(uint4 *)(stage + (id / (C::BM / 8)) * C::PITCH_T + 8 * (id % (C::BM / 8))) = v[i];
+    }
+  }
+};
+
+__device__ __forceinline__ v4i16 ds_read_tr16(const __bf16 *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)p);
+}
+
+template <class C>
+__device__ __forceinline__ void mma_stage_t(const __bf16 *At, const __bf16 *Bs, int arow0,
+                                            const int (&brow)[C::NJ], int lane,
+                                            f32x4 (&acc)[C::MI][C::NJ]) {
+  const int r = lane & 15, kq = 8 * (lane >> 4);
+  const int tr_row = kq + r / 4, tr_col = 4 * (r % 4);
+#pragma unroll
+  for (int u = 0; u < C::BK / 32; ++u) {
+    bf16x8 a[C::MI], b[C::NJ];
+#pragma unroll
+    for (int j = 0; j < C::NJ; ++j)
+      b[j] = *(const bf16x8 *)(Bs + (brow[j] + r) * C::PITCH + 32 * u + kq);
+#pragma unroll
+    for (int i = 0; i < C::MI; ++i) {
+      const __bf16 *base = At + (32 * u + tr_row) * C::PITCH_T + arow0 + 16 * i + tr_col;
+      const v4i16 lo = ds_read_tr16(base), hi = ds_read_tr16(base + 4 * C::PITCH_T);
+      a[i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+#pragma unroll
+    for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+      for (int j = 0; j < C::NJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void kloop_t(__bf16 *smem, LoaderT<C> &la, Loader<C, C::B_PIECES> &lb,
+                                        int nk, int tid, int arow0, const int (&brow)[C::NJ],
+                                        f32x4 (&acc)[C::MI][C::NJ]) {
+  __bf16 *const Bbase = smem + 2 * C::AT_STAGE;
+  const int lane = tid & 63, r0 = tid / C::KP, q = tid % C::KP;
+  la.fetch(0);
+  lb.fetch(0, q);
+  la.stash(smem, tid);
+  lb.stash(Bbase, r0, q);
+  __syncthreads();
+  for (int s = 0; s < nk; ++s) {
+    const int cur = s & 1;
+    if (s + 1 < nk) {
+      la.fetch((s + 1) * C::BK);
+      lb.fetch((s + 1) * C::BK, q);
+    }
+    mma_stage_t<C>(smem + cur * C::AT_STAGE, Bbase + cur * C::B_STAGE, arow0, brow, lane, acc);
+    if (s + 1 < nk) {
+      la.stash(smem + (cur ^ 1) * C::AT_STAGE, tid);
+      lb.stash(Bbase + (cur ^ 1) * C::B_STAGE, r0, q);
+    }
+    __syncthreads();
+  }
+}
+
 template <class C>
 __device__ __forceinline__ void zero_acc(f32x4 (&acc)[C::MI][C::NJ]) {
 #pragma unroll
@@ -168,7 +259,6 @@ template <class C>
 __global__ __launch_bounds__(C::NTHR) void k_gateup(Slab s, const __bf16 *__restrict__ x,
                                                     const __bf16 *__restrict__ wg,
                                                     const __bf16 *__restrict__ wu,
-                                                    __bf16 *__restrict__ z,
                                                     __bf16 *__restrict__ zt) {
   __shared__ __bf16 smem[C::SMEM_ELEMS];
   constexpr int FT = C::BN / 2;  // d_ff columns per block
@@ -212,7 +302,6 @@ __global__ __launch_bounds__(C::NTHR) void k_gateup(Slab s, const __bf16 *__rest
   zero_acc<C>(acc);
   kloop<C>(smem, la, lb, s.d / C::BK, tid, wm * 128, brow, acc);
 
-  __bf16 *zs = z + (int64_t)n_seq * s.Lp * s.F;
   __bf16 *zts = zt + (int64_t)n_seq * s.F * s.Lp;
 #pragma unroll
   for (int i = 0; i < C::MI; ++i)
@@ -230,8 +319,6 @@ __global__ __launch_bounds__(C::NTHR) void k_gateup(Slab s, const __bf16 *__rest
           v[r] = (__bf16)(real ? g / (1.f + __expf(-g)) * u : 0.f);
         }
         *(bf16x4 *)(zts + (int64_t)f * s.Lp + p) = v;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) zs[(int64_t)(p + r) * s.F + f] = v[r];
       }
     }
 }
@@ -294,13 +381,13 @@ __global__ __launch_bounds__(C::NTHR) void k_proj(Slab s, const __bf16 *__restri
 // output-major, d rows of d_ff).
 template <class C>
 __global__ __launch_bounds__(C::NTHR) void k_apply(Slab s, int j0, int nj,
-                                                   const __bf16 *__restrict__ z,
+                                                   const __bf16 *__restrict__ zt,
                                                    const __bf16 *__restrict__ snap,
                                                    int64_t snap_seq_stride,
                                                    int64_t snap_chunk_stride, float *__restrict__ o,
                                                    const __bf16 *__restrict__ vt,
                                                    __bf16 *__restrict__ rt) {
-  __shared__ __bf16 smem[C::SMEM_ELEMS];
+  __shared__ __bf16 smem[C::SMEM_T_ELEMS];
   const int nm = (s.Bp + C::BM - 1) / C::BM, nn = (s.d + C::BN - 1) / C::BN;
   const int per_chunk = nm * nn;
   const int id = xcd_remap(blockIdx.x, gridDim.x);
@@ -312,14 +399,19 @@ __global__ __launch_bounds__(C::NTHR) void k_apply(Slab s, int j0, int nj,
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WN, wn = wave % C::WN;
   const int r0 = tid / C::KP;
-  Loader<C, C::A_PIECES> la;
+  // A = Z_j read from Zt (token-contiguous rows of d_ff): K row f, M columns
+  // = the chunk's slab rows j Bp + m. Columns past the slab's rows (a chunk
+  // shorter than the tile) are clamped in bounds; their outputs are dropped.
+  LoaderT<C> la;
   Loader<C, C::B_PIECES> lb;
-  const __bf16 *zs = z + (int64_t)n_seq * s.Lp * s.F + (int64_t)j * s.Bp * s.F;
+  const __bf16 *zts = zt + (int64_t)n_seq * s.F * s.Lp;
   const __bf16 *ss = snap + n_seq * snap_seq_stride + jl * snap_chunk_stride;
+  la.ld = s.Lp;
 #pragma unroll
-  for (int i = 0; i < C::A_PIECES; ++i) {
-    const int m = m0 + r0 + C::RPP * i;
-    la.ptr[i] = zs + (int64_t)(m < s.Bp ? m : 0) * s.F;
+  for (int i = 0; i < C::AT_PIECES; ++i) {
+    const int id = tid + i * C::NTHR;
+    const int64_t col = min((int64_t)j * s.Bp + m0 + 8 * (id % (C::BM / 8)), s.Lp - 8);
+    la.ptr[i] = zts + (int64_t)(id / (C::BM / 8)) * s.Lp + col;
   }
 #pragma unroll
   for (int i = 0; i < C::B_PIECES; ++i) {
@@ -331,7 +423,7 @@ __global__ __launch_bounds__(C::NTHR) void k_apply(Slab s, int j0, int nj,
   for (int j = 0; j < C::NJ; ++j) brow[j] = wn * C::WTN + 16 * j;
   f32x4 acc[C::MI][C::NJ];
   zero_acc<C>(acc);
-  kloop<C>(smem, la, lb, s.F / C::BK, tid, wm * 128, brow, acc);
+  kloop_t<C>(smem, la, lb, s.F / C::BK, tid, wm * 128, brow, acc);
 
   const int64_t chunk_tok0 = s.tok0 + (int64_t)j * s.B;
   float *os = o + n_seq * s.x_seq_stride;
@@ -510,8 +602,7 @@ hipError_t launch_gateup(const Slab &s, const __bf16 *x, const Weights &w, const
   const int64_t P = (int64_t)s.nc * s.Bp;
   const int64_t nb = ((P + C::BM - 1) / C::BM) * ((s.F + C::BN / 2 - 1) / (C::BN / 2)) * s.n_seq;
   hipLaunchKernelGGL(k_gateup<C>, dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, x,
-                     (const __bf16 *)w.w_gate, (const __bf16 *)w.w_up, (__bf16 *)ws.z,
-                     (__bf16 *)ws.zt);
+                     (const __bf16 *)w.w_gate, (const __bf16 *)w.w_up, (__bf16 *)ws.zt);
   return hipGetLastError();
 }
 
@@ -534,7 +625,7 @@ hipError_t launch_apply(const Slab &s, int j0, int nj, const WsPtrs &ws, float *
   const int64_t nb =
       ((s.Bp + C::BM - 1) / C::BM) * ((s.d + C::BN - 1) / C::BN) * (int64_t)nj * s.n_seq;
   hipLaunchKernelGGL(k_apply<C>, dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, j0, nj,
-                     (const __bf16 *)ws.z, snap, snap_seq, snap_chunk, o, (const __bf16 *)ws.vt,
+                     (const __bf16 *)ws.zt, snap, snap_seq, snap_chunk, o, (const __bf16 *)ws.vt,
                      s.mse ? (__bf16 *)ws.rt : nullptr);
   return hipGetLastError();
 }
@@ -570,6 +661,7 @@ hipError_t launch_update_one(const Slab &s, int j, const WsPtrs &ws, float *w_st
 using GateUpCfg = Cfg<2, 4, 64>;
 using ProjCfg = Cfg<2, 4, 32>;
 using ApplyCfg = Cfg<2, 4, 64>;
+using ApplySmallCfg = Cfg<1, 2, 64>;  // when ApplyCfg would leave most CUs idle
 using UpdateCfg = Cfg<1, 2, 64>;
 static_assert(kChunkAlign % UpdateCfg::BK == 0, "chunk pitch must be whole update K steps");
 
@@ -610,7 +702,11 @@ hipError_t mf_proj(const Slab &s, const Weights &w, const WsPtrs &ws, hipStream_
   return mfma::launch_proj<mfma::ProjCfg>(s, w, ws, st);
 }
 hipError_t mf_apply(const Slab &s, int j0, int nj, const WsPtrs &ws, float *o, hipStream_t st) {
-  return mfma::launch_apply<mfma::ApplyCfg>(s, j0, nj, ws, o, st);
+  using C = mfma::ApplyCfg;
+  const int64_t big_blocks =
+      ((s.Bp + C::BM - 1) / C::BM) * ((s.d + C::BN - 1) / C::BN) * (int64_t)nj * s.n_seq;
+  if (big_blocks < 512) return mfma::launch_apply<mfma::ApplySmallCfg>(s, j0, nj, ws, o, st);
+  return mfma::launch_apply<C>(s, j0, nj, ws, o, st);
 }
 hipError_t mf_update_scan(const Slab &s, const WsPtrs &ws, float *w_state, hipStream_t st) {
   return mfma::launch_update_scan<mfma::UpdateCfg>(s, ws, w_state, st);
