@@ -6,9 +6,9 @@
 // (128 WM) x (64 WN). K is staged through LDS BK at a time in two buffers;
 // the global loads of step s+1 are in flight while step s runs on MFMA.
 // Both operands are K-contiguous in memory ("NT"): a lane's MFMA operand is
-// 8 consecutive K values (one 16-byte LDS read). LDS rows are padded by 16
-// bytes so that the 16-byte fragment reads of consecutive lanes, which walk
-// down 16 rows, fall on distinct banks.
+// 8 consecutive K values (one 16-byte LDS read). LDS rows are padded (PAD
+// elements) so that the 16-byte fragment reads of consecutive lanes, which walk
+// down 16 rows, spread over the banks; the padding is picked by measurement.
 //
 // 16x16x32 operand layout used here: lane l supplies row (l % 16) of A and
 // column (l % 16) of B, each with K values 8*(l / 16) .. 8*(l / 16) + 7; the
@@ -36,14 +36,14 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-template <int WM_, int WN_, int BK_, int NJ_ = 4>
+template <int WM_, int WN_, int BK_, int NJ_ = 4, int PAD_ = 8, int PADT_ = 16>
 struct Cfg {
   static constexpr int WM = WM_, WN = WN_, BK = BK_;
   static constexpr int MI = 8, NJ = NJ_;  // 16x16 tiles per wave: 128 x (16 NJ)
   static constexpr int WTN = 16 * NJ;     // wave tile width
   static constexpr int BM = 128 * WM, BN = WTN * WN;
   static constexpr int NTHR = 64 * WM * WN;
-  static constexpr int PITCH = BK + 8;  // LDS row pitch in bf16
+  static constexpr int PITCH = BK + PAD_;  // LDS row pitch in bf16
   static constexpr int KP = BK / 8;     // 16-byte pieces per row per step
   static constexpr int RPP = NTHR / KP; // rows covered by one pass of all threads
   static constexpr int A_PIECES = BM / RPP;
@@ -52,13 +52,13 @@ struct Cfg {
   static constexpr int SMEM_ELEMS = 2 * (A_STAGE + B_STAGE);
   // A held K-major in LDS ([BK rows of K][BM columns of M], for an A operand
   // that is stored M-contiguous in memory): rows padded by 32 bytes.
-  static constexpr int PITCH_T = BM + 16;
+  static constexpr int PITCH_T = BM + PADT_;
   static constexpr int AT_PIECES = BK * (BM / 8) / NTHR;
   static constexpr int AT_STAGE = BK * PITCH_T;
   static constexpr int SMEM_T_ELEMS = 2 * (AT_STAGE + B_STAGE);
   static_assert(BK % 32 == 0 && BM % RPP == 0 && BN % RPP == 0, "bad tile config");
+  static_assert(PAD_ % 8 == 0 && PADT_ % 4 == 0, "LDS rows must keep 16 / 8-byte alignment");
   static_assert((BK * (BM / 8)) % NTHR == 0, "bad transposed-A tile config");
-  static_assert(SMEM_ELEMS * 2 <= 160 * 1024, "LDS overflow");
 };
 
 __device__ __forceinline__ uint4 ld16(const __bf16 *p) { return *(const uint4 *)p; }
@@ -260,6 +260,7 @@ __global__ __launch_bounds__(C::NTHR) void k_gateup(Slab s, const __bf16 *__rest
                                                     const __bf16 *__restrict__ wg,
                                                     const __bf16 *__restrict__ wu,
                                                     __bf16 *__restrict__ zt) {
+  static_assert(C::SMEM_ELEMS * 2 <= 160 * 1024, "LDS overflow");
   __shared__ __bf16 smem[C::SMEM_ELEMS];
   constexpr int FT = C::BN / 2;  // d_ff columns per block
   const int P = s.nc * s.Bp;
@@ -328,6 +329,7 @@ template <class C>
 __global__ __launch_bounds__(C::NTHR) void k_proj(Slab s, const __bf16 *__restrict__ c,
                                                   const __bf16 *__restrict__ proj,
                                                   __bf16 *__restrict__ vt, float scale) {
+  static_assert(C::SMEM_ELEMS * 2 <= 160 * 1024, "LDS overflow");
   __shared__ __bf16 smem[C::SMEM_ELEMS];
   const int P = s.nc * s.Bp;
   const int nm = (P + C::BM - 1) / C::BM, nn = (s.d + C::BN - 1) / C::BN;
@@ -387,6 +389,7 @@ __global__ __launch_bounds__(C::NTHR) void k_apply(Slab s, int j0, int nj,
                                                    int64_t snap_chunk_stride, float *__restrict__ o,
                                                    const __bf16 *__restrict__ vt,
                                                    __bf16 *__restrict__ rt) {
+  static_assert(C::SMEM_T_ELEMS * 2 <= 160 * 1024, "LDS overflow");
   __shared__ __bf16 smem[C::SMEM_T_ELEMS];
   const int nm = (s.Bp + C::BM - 1) / C::BM, nn = (s.d + C::BN - 1) / C::BN;
   const int per_chunk = nm * nn;
@@ -466,6 +469,7 @@ __global__ __launch_bounds__(C::NTHR) void k_update(
     const __bf16 *__restrict__ bsrc, int64_t b_ld, int64_t b_seq_stride, int64_t b_chunk_stride,
     float *__restrict__ w, __bf16 *__restrict__ snap, int64_t snap_seq_stride,
     int64_t snap_chunk_stride, int snap_each_chunk, int snap_after) {
+  static_assert(C::SMEM_ELEMS * 2 <= 160 * 1024, "LDS overflow");
   __shared__ __bf16 smem[C::SMEM_ELEMS];
   const int nm = (s.F + C::BM - 1) / C::BM, nn = (s.d + C::BN - 1) / C::BN;
   const int per_seq = nm * nn;
@@ -654,15 +658,16 @@ hipError_t launch_update_one(const Slab &s, int j, const WsPtrs &ws, float *w_st
   return hipGetLastError();
 }
 
-// Block shapes chosen by timing on MI355X at the 4B layer shape (d 2560,
-// d_ff 9728, 16 chunks of 1024): 8 waves over 256 x 256 with K steps of 64 for
-// the long-K products, 2 waves over 128 x 128 for the update (more, smaller
-// blocks: each one streams every chunk of the slab).
-using GateUpCfg = Cfg<2, 4, 64>;
-using ProjCfg = Cfg<2, 4, 32>;
-using ApplyCfg = Cfg<2, 4, 64>;
-using ApplySmallCfg = Cfg<1, 2, 64>;  // when ApplyCfg would leave most CUs idle
-using UpdateCfg = Cfg<1, 2, 64>;
+// Block shapes and LDS row paddings chosen by timing on MI355X at the 4B layer
+// shape (d 2560, d_ff 9728, 16 chunks of 1024): 8 waves over 256 x 256 with K
+// steps of 64 for the long-K products, 2 waves over 128 x 128 for the update
+// (more, smaller blocks: each one streams every chunk of the slab). Rows padded
+// by 32 bytes measured faster than by 16 on this LDS.
+using GateUpCfg = Cfg<2, 4, 64, 4, 16>;
+using ProjCfg = Cfg<2, 4, 32, 4, 16>;
+using ApplyCfg = Cfg<2, 4, 64, 4, 16, 8>;
+using ApplySmallCfg = Cfg<1, 2, 64, 4, 16, 8>;  // when ApplyCfg would leave most CUs idle
+using UpdateCfg = Cfg<1, 2, 64, 4, 16>;
 static_assert(kChunkAlign % UpdateCfg::BK == 0, "chunk pitch must be whole update K steps");
 
 template <int KC>
