@@ -23,6 +23,65 @@ import torch  # noqa: E402
 import workloads as wl  # noqa: E402
 
 METRIC = "fast-weight prefill tokens/s per MLP layer at L=128k,B=1024; % MFMA/HBM roofline"
+KERNEL_SRC = os.path.join(ROOT, "chunked_weight_mlp_amd", "csrc", "kernels_mfma.hip")
+KERNEL_TAGS = {"gateup": "k_gateup", "conv": "k_conv", "proj": "k_proj", "update": "k_update",
+               "apply": "k_apply", "copy": "copyBuffer"}
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def traffic_path(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+
+
+def summarize_traffic(workload: str, fetch_csv: str, write_csv: str) -> dict:
+    """HBM bytes per launch of each kernel from two rocprofv3 --pmc runs of this
+    benchmark (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each scaled by
+    what the same counter reads for the reset's plain device copy of W_0
+    (d * d_ff * 4 bytes read and written) in the same run."""
+    import csv
+    w = wl.WORKLOADS[workload]
+    copy_bytes = w.d * w.d_ff * 4
+
+    def per_kernel(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            for k, tag in KERNEL_TAGS.items():
+                if tag in r["Kernel_Name"]:
+                    vals.setdefault(k, []).append(float(r["Counter_Value"]) * 1024.0)
+        return {k: sum(v) / len(v) for k, v in vals.items()}
+
+    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    f_fetch, f_write = copy_bytes / fetch["copy"], copy_bytes / write["copy"]
+    out = {"workload": workload, "kernel_source_sha": kernel_source_hash(),
+           "calibration": {"copy_bytes": copy_bytes, "fetch_factor": round(f_fetch, 4),
+                           "write_factor": round(f_write, 4)},
+           "bytes_per_launch": {}}
+    for k in fetch:
+        if k == "copy" or k not in write:
+            continue
+        out["bytes_per_launch"][k] = {"fetch": round(fetch[k] * f_fetch),
+                                      "write": round(write[k] * f_write),
+                                      "total": round(fetch[k] * f_fetch + write[k] * f_write)}
+    return out
+
+
+def load_traffic(workload: str, kernel: str):
+    """Traffic of `kernel` if a summary exists for this workload and the kernels
+    have not changed since the counters were taken; else None."""
+    path = traffic_path(workload)
+    if not os.path.exists(path):
+        return None
+    t = json.load(open(path))
+    if t.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    b = t["bytes_per_launch"].get(kernel)
+    return None if b is None else b["total"]
 PEAK = {"bf16": 2500.0, "f32": 157.3}  # dense TFLOP/s (MFMA bf16, fp32)
 HBM_PEAK = 8000.0                       # GB/s
 
@@ -78,7 +137,17 @@ def main():
     ap.add_argument("--cpu-chunks", type=int, default=40, help="chunks in the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--generic", action="store_true", help="generic FMA kernels instead of MFMA")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc "
+                         "counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) and exit")
     args = ap.parse_args()
+
+    if args.traffic_from:
+        t = summarize_traffic(args.workload, *args.traffic_from)
+        with open(traffic_path(args.workload), "w") as fh:
+            json.dump(t, fh, indent=1)
+        print(json.dumps(t))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
@@ -160,11 +229,15 @@ def main():
     if intensity >= ridge:
         ach = dom_fl / dom_avg_s / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK[w.dtype], "unit": "TFLOP/s",
-                "frac": round(ach / PEAK[w.dtype], 4), "traffic": None, "kernel": dom}
+                "frac": round(ach / PEAK[w.dtype], 4)}
     else:
         ach = dom_by / dom_avg_s / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK, 4), "traffic": None, "kernel": dom}
+                "frac": round(ach / HBM_PEAK, 4)}
+    # measured HBM bytes per launch (rocprofv3 counters, profiles/traffic_*.json)
+    roof["traffic"] = None if args.generic else load_traffic(w.name, dom)
+    roof["algorithmic_bytes"] = round(dom_by)
+    roof["kernel"] = dom
 
     out = {
         "metric": METRIC,

@@ -1,19 +1,15 @@
 // bf16 MFMA kernels of the fast-weight prefill for gfx950 (CDNA4).
 //
 // All four dense contractions share one block structure, templated on the
-// wave grid and the K step (Cfg): WM x WN waves, each computing a 128 x 64
-// output tile as 8 x 4 tiles of v_mfma_f32_16x16x32_bf16, so a block covers
-// (128 WM) x (64 WN). K is staged through LDS BK at a time in two buffers;
-// the global loads of step s+1 are in flight while step s runs on MFMA.
-// Both operands are K-contiguous in memory ("NT"): a lane's MFMA operand is
-// 8 consecutive K values (one 16-byte LDS read). LDS rows are padded (PAD
-// elements) so that the 16-byte fragment reads of consecutive lanes, which walk
-// down 16 rows, spread over the banks; the padding is picked by measurement.
-//
-// 16x16x32 operand layout used here: lane l supplies row (l % 16) of A and
-// column (l % 16) of B, each with K values 8*(l / 16) .. 8*(l / 16) + 7; the
-// result lane l holds rows 4*(l / 16) + r, r = 0..3, of column (l % 16). Any
-// consistent assignment of K values to (lane group, slot) gives the same sum.
+// wave grid, the K step and the MFMA shape (Cfg): WM x WN waves, each computing
+// a 128 x 64 output tile from FM x FM MFMA tiles (v_mfma_f32_32x32x16_bf16 or
+// v_mfma_f32_16x16x32_bf16), so a block covers (128 WM) x (64 WN). K is staged
+// through LDS BK at a time in two buffers; the global loads of step s+1 are in
+// flight while step s runs on MFMA. Both operands are K-contiguous in memory
+// ("NT"): a lane's MFMA operand is 8 consecutive K values (one 16-byte LDS
+// read). LDS rows are padded (PAD elements) so that the fragment reads of
+// consecutive lanes, which walk down consecutive rows, spread over the banks;
+// shapes and paddings were picked by timing on MI355X.
 //
 // Kernels:
 //   k_gateup   Z = SiLU(X W_g) * (X W_u)   M = slab rows, N = d_ff (half the
@@ -27,6 +23,7 @@
 //              accumulators across the chunks of a slab: per chunk, optionally
 //              write the bf16 snapshot S_j, then accumulate Zt_j . Vt_j over
 //              the chunk's tokens.
+//   k_conv     depthwise conv of E, vector loads, sliding window.
 #include "internal.h"
 
 namespace ipttt {
@@ -35,23 +32,77 @@ namespace mfma {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
 
-template <int WM_, int WN_, int BK_, int NJ_ = 4, int PAD_ = 8, int PADT_ = 16>
+// MFMA tile shapes. Operand: lane l supplies row orow(l) of A (column of B) and
+// K values okoff(l) .. okoff(l) + 7 of one MFMA K step (K wide). Result: the
+// lane holds NG groups of 4 consecutive rows, group g starting at row
+// rrow(l, g), all in column rcol(l). Any consistent assignment of K values to
+// (lane, slot) gives the same sum; the row and column maps are the hardware's.
+template <int FM>
+struct Mfma;
+template <>
+struct Mfma<16> {
+  typedef f32x4 acc_t;
+  static constexpr int K = 32, NG = 1;
+  __device__ static __forceinline__ acc_t mma(bf16x8 a, bf16x8 b, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ int orow(int l) { return l & 15; }
+  __device__ static __forceinline__ int okoff(int l) { return 8 * (l >> 4); }
+  __device__ static __forceinline__ int rrow(int l, int) { return 4 * (l >> 4); }
+  __device__ static __forceinline__ int rcol(int l) { return l & 15; }
+  // transposed-A source address of lane l (see mma_stage_t)
+  __device__ static __forceinline__ int tr_row(int l) { return 8 * (l >> 4) + (l & 15) / 4; }
+  __device__ static __forceinline__ int tr_col(int l) { return 4 * (l & 3); }
+};
+template <>
+struct Mfma<32> {
+  typedef f32x16 acc_t;
+  static constexpr int K = 16, NG = 4;
+  __device__ static __forceinline__ acc_t mma(bf16x8 a, bf16x8 b, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ int orow(int l) { return l & 31; }
+  __device__ static __forceinline__ int okoff(int l) { return 8 * (l >> 5); }
+  __device__ static __forceinline__ int rrow(int l, int g) { return 8 * g + 4 * (l >> 5); }
+  __device__ static __forceinline__ int rcol(int l) { return l & 31; }
+  __device__ static __forceinline__ int tr_row(int l) { return 8 * (l >> 5) + (l & 15) / 4; }
+  __device__ static __forceinline__ int tr_col(int l) { return 16 * ((l >> 4) & 1) + 4 * (l & 3); }
+};
+
+__device__ __forceinline__ f32x4 get4(const f32x4 &a, int) { return a; }
+__device__ __forceinline__ f32x4 get4(const f32x16 &a, int g) {
+  return f32x4{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
+}
+__device__ __forceinline__ void set4(f32x4 &a, int, f32x4 v) { a = v; }
+__device__ __forceinline__ void set4(f32x16 &a, int g, f32x4 v) {
+  a[4 * g] = v[0];
+  a[4 * g + 1] = v[1];
+  a[4 * g + 2] = v[2];
+  a[4 * g + 3] = v[3];
+}
+
+template <int WM_, int WN_, int BK_, int FM_ = 32, int PAD_ = 16, int PADT_ = 8, int OCC_ = 1>
 struct Cfg {
-  static constexpr int WM = WM_, WN = WN_, BK = BK_;
-  static constexpr int MI = 8, NJ = NJ_;  // 16x16 tiles per wave: 128 x (16 NJ)
-  static constexpr int WTN = 16 * NJ;     // wave tile width
-  static constexpr int BM = 128 * WM, BN = WTN * WN;
+  static constexpr int WM = WM_, WN = WN_, BK = BK_, FM = FM_;
+  static constexpr int OCC = OCC_;  // waves per SIMD the register allocation must allow
+  using M = Mfma<FM>;
+  using acc_t = typename M::acc_t;
+  static constexpr int WTM = 128, WTN = 64;  // wave tile
+  static constexpr int MI = WTM / FM, NJ = WTN / FM;
+  static constexpr int BM = WTM * WM, BN = WTN * WN;
   static constexpr int NTHR = 64 * WM * WN;
   static constexpr int PITCH = BK + PAD_;  // LDS row pitch in bf16
-  static constexpr int KP = BK / 8;     // 16-byte pieces per row per step
-  static constexpr int RPP = NTHR / KP; // rows covered by one pass of all threads
+  static constexpr int KP = BK / 8;        // 16-byte pieces per row per step
+  static constexpr int RPP = NTHR / KP;    // rows covered by one pass of all threads
   static constexpr int A_PIECES = BM / RPP;
   static constexpr int B_PIECES = BN / RPP;
   static constexpr int A_STAGE = BM * PITCH, B_STAGE = BN * PITCH;
   static constexpr int SMEM_ELEMS = 2 * (A_STAGE + B_STAGE);
-  // A held K-major in LDS ([BK rows of K][BM columns of M], for an A operand
-  // that is stored M-contiguous in memory): rows padded by 32 bytes.
+  // A held K-major in LDS ([BK rows of K][BM columns of M]) for an A operand
+  // stored M-contiguous in memory.
   static constexpr int PITCH_T = BM + PADT_;
   static constexpr int AT_PIECES = BK * (BM / 8) / NTHR;
   static constexpr int AT_STAGE = BK * PITCH_T;
@@ -107,64 +158,34 @@ struct Loader {
 template <class C>
 __device__ __forceinline__ void mma_stage(const __bf16 *As, const __bf16 *Bs, int arow0,
                                           const int (&brow)[C::NJ], int lane,
-                                          f32x4 (&acc)[C::MI][C::NJ]) {
-  const int r = lane & 15, kq = 8 * (lane >> 4);
+                                          typename C::acc_t (&acc)[C::MI][C::NJ]) {
+  using M = typename C::M;
+  const int r = M::orow(lane), kq = M::okoff(lane);
 #pragma unroll
-  for (int u = 0; u < C::BK / 32; ++u) {
+  for (int u = 0; u < C::BK / M::K; ++u) {
     bf16x8 a[C::MI], b[C::NJ];
 #pragma unroll
     for (int j = 0; j < C::NJ; ++j)
-      b[j] = *(const bf16x8 *)(Bs + (brow[j] + r) * C::PITCH + 32 * u + kq);
+      b[j] = *(const bf16x8 *)(Bs + (brow[j] + r) * C::PITCH + M::K * u + kq);
 #pragma unroll
     for (int i = 0; i < C::MI; ++i)
-      a[i] = *(const bf16x8 *)(As + (arow0 + 16 * i + r) * C::PITCH + 32 * u + kq);
+      a[i] = *(const bf16x8 *)(As + (arow0 + C::FM * i + r) * C::PITCH + M::K * u + kq);
 #pragma unroll
     for (int i = 0; i < C::MI; ++i)
 #pragma unroll
-      for (int j = 0; j < C::NJ; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-  }
-}
-
-// Full K loop over nk steps of BK with double-buffered LDS.
-template <class C>
-__device__ __forceinline__ void kloop(__bf16 *smem, Loader<C, C::A_PIECES> &la,
-                                      Loader<C, C::B_PIECES> &lb, int nk, int tid, int arow0,
-                                      const int (&brow)[C::NJ], f32x4 (&acc)[C::MI][C::NJ]) {
-  // Stage addresses are formed arithmetically from the __shared__ base so the
-  // compiler keeps them in the LDS address space (ds_read / ds_write, not flat).
-  __bf16 *const Bbase = smem + 2 * C::A_STAGE;
-  const int lane = tid & 63, r0 = tid / C::KP, q = tid % C::KP;
-  la.fetch(0, q);
-  lb.fetch(0, q);
-  la.stash(smem, r0, q);
-  lb.stash(Bbase, r0, q);
-  __syncthreads();
-  for (int s = 0; s < nk; ++s) {
-    const int cur = s & 1;
-    if (s + 1 < nk) {
-      la.fetch((s + 1) * C::BK, q);
-      lb.fetch((s + 1) * C::BK, q);
-    }
-    mma_stage<C>(smem + cur * C::A_STAGE, Bbase + cur * C::B_STAGE, arow0, brow, lane, acc);
-    if (s + 1 < nk) {
-      la.stash(smem + (cur ^ 1) * C::A_STAGE, r0, q);
-      lb.stash(Bbase + (cur ^ 1) * C::B_STAGE, r0, q);
-    }
-    __syncthreads();
+      for (int j = 0; j < C::NJ; ++j) acc[i][j] = M::mma(a[i], b[j], acc[i][j]);
   }
 }
 
 // ---- A operand stored M-contiguous (K-major rows) ---------------------------
 // The tile is copied into LDS as BK rows of BM elements; each MFMA A fragment
-// (row m = lane % 16, K values 8 g .. 8 g + 7 for g = lane / 16) is assembled
-// from two ds_read_b64_tr_b16. That instruction works on groups of 16 lanes:
-// lane i of a group receives element (i % 4) of the 8-byte chunk read by lane
-// 4 j + i / 4 of the group, for j = 0..3. Source lane p therefore points at K
-// row (p / 4) and M columns 4 (p % 4) .. + 3 of a 4 x 16 block, and lane i gets
-// that block's column i: 4 consecutive K values of M row i.
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-
+// (8 consecutive K values of one M row per lane) is assembled from two
+// ds_read_b64_tr_b16. That instruction works on groups of 16 lanes: lane i of
+// a group receives element (i % 4) of the 8-byte chunk read by lane 4 j + i / 4
+// of the group, for j = 0..3. Source lane p therefore points at K row (p / 4)
+// and M columns 4 (p % 4) .. + 3 of a 4 x 16 block, and lane i gets that
+// block's column i: 4 consecutive K values of M row i (tr_row / tr_col place
+// each 16-lane group on the rows and K values its MFMA operand needs).
 template <class C>
 struct LoaderT {
   const __bf16 *ptr[C::AT_PIECES];  // K row start, already offset to this thread's M piece
@@ -190,33 +211,63 @@ __device__ __forceinline__ v4i16 ds_read_tr16(const __bf16 *p) {
 template <class C>
 __device__ __forceinline__ void mma_stage_t(const __bf16 *At, const __bf16 *Bs, int arow0,
                                             const int (&brow)[C::NJ], int lane,
-                                            f32x4 (&acc)[C::MI][C::NJ]) {
-  const int r = lane & 15, kq = 8 * (lane >> 4);
-  const int tr_row = kq + r / 4, tr_col = 4 * (r % 4);
+                                            typename C::acc_t (&acc)[C::MI][C::NJ]) {
+  using M = typename C::M;
+  const int r = M::orow(lane), kq = M::okoff(lane);
+  const int trr = M::tr_row(lane), trc = M::tr_col(lane);
 #pragma unroll
-  for (int u = 0; u < C::BK / 32; ++u) {
+  for (int u = 0; u < C::BK / M::K; ++u) {
     bf16x8 a[C::MI], b[C::NJ];
 #pragma unroll
     for (int j = 0; j < C::NJ; ++j)
-      b[j] = *(const bf16x8 *)(Bs + (brow[j] + r) * C::PITCH + 32 * u + kq);
+      b[j] = *(const bf16x8 *)(Bs + (brow[j] + r) * C::PITCH + M::K * u + kq);
 #pragma unroll
     for (int i = 0; i < C::MI; ++i) {
-      const __bf16 *base = At + (32 * u + tr_row) * C::PITCH_T + arow0 + 16 * i + tr_col;
+      const __bf16 *base = At + (M::K * u + trr) * C::PITCH_T + arow0 + C::FM * i + trc;
       const v4i16 lo = ds_read_tr16(base), hi = ds_read_tr16(base + 4 * C::PITCH_T);
       a[i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
 #pragma unroll
     for (int i = 0; i < C::MI; ++i)
 #pragma unroll
-      for (int j = 0; j < C::NJ; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < C::NJ; ++j) acc[i][j] = M::mma(a[i], b[j], acc[i][j]);
+  }
+}
+
+// Full K loop over nk steps of BK with double-buffered LDS. Stage addresses are
+// formed arithmetically from the __shared__ base so the compiler keeps them in
+// the LDS address space (ds_read / ds_write, not flat).
+template <class C>
+__device__ __forceinline__ void kloop(__bf16 *smem, Loader<C, C::A_PIECES> &la,
+                                      Loader<C, C::B_PIECES> &lb, int nk, int tid, int arow0,
+                                      const int (&brow)[C::NJ],
+                                      typename C::acc_t (&acc)[C::MI][C::NJ]) {
+  __bf16 *const Bbase = smem + 2 * C::A_STAGE;
+  const int lane = tid & 63, r0 = tid / C::KP, q = tid % C::KP;
+  la.fetch(0, q);
+  lb.fetch(0, q);
+  la.stash(smem, r0, q);
+  lb.stash(Bbase, r0, q);
+  __syncthreads();
+  for (int s = 0; s < nk; ++s) {
+    const int cur = s & 1;
+    if (s + 1 < nk) {
+      la.fetch((s + 1) * C::BK, q);
+      lb.fetch((s + 1) * C::BK, q);
+    }
+    mma_stage<C>(smem + cur * C::A_STAGE, Bbase + cur * C::B_STAGE, arow0, brow, lane, acc);
+    if (s + 1 < nk) {
+      la.stash(smem + (cur ^ 1) * C::A_STAGE, r0, q);
+      lb.stash(Bbase + (cur ^ 1) * C::B_STAGE, r0, q);
+    }
+    __syncthreads();
   }
 }
 
 template <class C>
 __device__ __forceinline__ void kloop_t(__bf16 *smem, LoaderT<C> &la, Loader<C, C::B_PIECES> &lb,
                                         int nk, int tid, int arow0, const int (&brow)[C::NJ],
-                                        f32x4 (&acc)[C::MI][C::NJ]) {
+                                        typename C::acc_t (&acc)[C::MI][C::NJ]) {
   __bf16 *const Bbase = smem + 2 * C::AT_STAGE;
   const int lane = tid & 63, r0 = tid / C::KP, q = tid % C::KP;
   la.fetch(0);
@@ -240,11 +291,11 @@ __device__ __forceinline__ void kloop_t(__bf16 *smem, LoaderT<C> &la, Loader<C, 
 }
 
 template <class C>
-__device__ __forceinline__ void zero_acc(f32x4 (&acc)[C::MI][C::NJ]) {
+__device__ __forceinline__ void zero_acc(typename C::acc_t (&acc)[C::MI][C::NJ]) {
 #pragma unroll
   for (int i = 0; i < C::MI; ++i)
 #pragma unroll
-    for (int j = 0; j < C::NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < C::NJ; ++j) acc[i][j] = typename C::acc_t{};
 }
 
 __device__ __forceinline__ int64_t slab_row_token(const Slab &s, int64_t p) {
@@ -256,12 +307,12 @@ __device__ __forceinline__ int64_t slab_row_token(const Slab &s, int64_t p) {
 
 // ---------------------------------------------------------------------------
 template <class C>
-__global__ __launch_bounds__(C::NTHR) void k_gateup(Slab s, const __bf16 *__restrict__ x,
-                                                    const __bf16 *__restrict__ wg,
-                                                    const __bf16 *__restrict__ wu,
-                                                    __bf16 *__restrict__ zt) {
+__global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC))) void k_gateup(
+    Slab s, const __bf16 *__restrict__ x, const __bf16 *__restrict__ wg,
+    const __bf16 *__restrict__ wu, __bf16 *__restrict__ zt) {
   static_assert(C::SMEM_ELEMS * 2 <= 160 * 1024, "LDS overflow");
   __shared__ __bf16 smem[C::SMEM_ELEMS];
+  using M = typename C::M;
   constexpr int FT = C::BN / 2;  // d_ff columns per block
   const int P = s.nc * s.Bp;
   const int nm = (P + C::BM - 1) / C::BM, nn = (s.F + FT - 1) / FT;
@@ -284,6 +335,7 @@ __global__ __launch_bounds__(C::NTHR) void k_gateup(Slab s, const __bf16 *__rest
     const int64_t t = p < P ? slab_row_token(s, p) : -1;
     la.ptr[i] = xs + (t >= 0 ? t : 0) * s.d;
   }
+  // B rows [0, FT): gate rows f0.., [FT, 2 FT): the matching up rows
 #pragma unroll
   for (int i = 0; i < C::B_PIECES; ++i) {
     const int rr = r0 + C::RPP * i;
@@ -293,44 +345,48 @@ __global__ __launch_bounds__(C::NTHR) void k_gateup(Slab s, const __bf16 *__rest
   }
   // a wave's first NJ/2 B tiles are gate rows, the other NJ/2 the matching up rows
   constexpr int HJ = C::NJ / 2;
+  constexpr int WF = C::WTN / 2;  // d_ff columns per wave
   int brow[C::NJ];
 #pragma unroll
   for (int j = 0; j < HJ; ++j) {
-    brow[j] = wn * 16 * HJ + 16 * j;
-    brow[j + HJ] = FT + wn * 16 * HJ + 16 * j;
+    brow[j] = wn * WF + C::FM * j;
+    brow[j + HJ] = FT + wn * WF + C::FM * j;
   }
-  f32x4 acc[C::MI][C::NJ];
+  typename C::acc_t acc[C::MI][C::NJ];
   zero_acc<C>(acc);
-  kloop<C>(smem, la, lb, s.d / C::BK, tid, wm * 128, brow, acc);
+  kloop<C>(smem, la, lb, s.d / C::BK, tid, wm * C::WTM, brow, acc);
 
   __bf16 *zts = zt + (int64_t)n_seq * s.F * s.Lp;
 #pragma unroll
   for (int i = 0; i < C::MI; ++i)
 #pragma unroll
-    for (int j = 0; j < HJ; ++j) {
-      const int p = m0 + wm * 128 + 16 * i + 4 * (lane >> 4);
-      const int f = f0 + wn * 16 * HJ + 16 * j + (lane & 15);
-      if (p < P && f < s.F) {
-        bf16x4 v;
+    for (int j = 0; j < HJ; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          // chunk-padding rows (and tokens past the sequence end) are exact zeros
-          const float g = acc[i][j][r], u = acc[i][j + HJ][r];
-          const bool real = slab_row_token(s, p + r) >= 0;
-          v[r] = (__bf16)(real ? g / (1.f + __expf(-g)) * u : 0.f);
+      for (int g = 0; g < M::NG; ++g) {
+        const int p = m0 + wm * C::WTM + C::FM * i + M::rrow(lane, g);
+        const int f = f0 + wn * WF + C::FM * j + M::rcol(lane);
+        if (p < P && f < s.F) {
+          const f32x4 gv = get4(acc[i][j], g), uv = get4(acc[i][j + HJ], g);
+          bf16x4 v;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            // chunk-padding rows (and tokens past the sequence end) are exact zeros
+            const bool real = slab_row_token(s, p + r) >= 0;
+            v[r] = (__bf16)(real ? gv[r] / (1.f + __expf(-gv[r])) * uv[r] : 0.f);
+          }
+          *(bf16x4 *)(zts + (int64_t)f * s.Lp + p) = v;
         }
-        *(bf16x4 *)(zts + (int64_t)f * s.Lp + p) = v;
       }
-    }
 }
 
 // ---------------------------------------------------------------------------
 template <class C>
-__global__ __launch_bounds__(C::NTHR) void k_proj(Slab s, const __bf16 *__restrict__ c,
-                                                  const __bf16 *__restrict__ proj,
-                                                  __bf16 *__restrict__ vt, float scale) {
+__global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC))) void k_proj(
+    Slab s, const __bf16 *__restrict__ c, const __bf16 *__restrict__ proj,
+    __bf16 *__restrict__ vt, float scale) {
   static_assert(C::SMEM_ELEMS * 2 <= 160 * 1024, "LDS overflow");
   __shared__ __bf16 smem[C::SMEM_ELEMS];
+  using M = typename C::M;
   const int P = s.nc * s.Bp;
   const int nm = (P + C::BM - 1) / C::BM, nn = (s.d + C::BN - 1) / C::BN;
   const int per_seq = nm * nn;
@@ -357,40 +413,41 @@ __global__ __launch_bounds__(C::NTHR) void k_proj(Slab s, const __bf16 *__restri
   }
   int brow[C::NJ];
 #pragma unroll
-  for (int j = 0; j < C::NJ; ++j) brow[j] = wn * C::WTN + 16 * j;
-  f32x4 acc[C::MI][C::NJ];
+  for (int j = 0; j < C::NJ; ++j) brow[j] = wn * C::WTN + C::FM * j;
+  typename C::acc_t acc[C::MI][C::NJ];
   zero_acc<C>(acc);
-  kloop<C>(smem, la, lb, s.d / C::BK, tid, wm * 128, brow, acc);
+  kloop<C>(smem, la, lb, s.d / C::BK, tid, wm * C::WTM, brow, acc);
 
   __bf16 *vts = vt + (int64_t)n_seq * s.d * s.Lp;
 #pragma unroll
   for (int i = 0; i < C::MI; ++i)
 #pragma unroll
-    for (int j = 0; j < C::NJ; ++j) {
-      const int p = m0 + wm * 128 + 16 * i + 4 * (lane >> 4);
-      const int n = n0 + wn * C::WTN + 16 * j + (lane & 15);
-      if (p < P && n < s.d) {
-        bf16x4 v;
+    for (int j = 0; j < C::NJ; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = (__bf16)(scale * acc[i][j][r]);
-        *(bf16x4 *)(vts + (int64_t)n * s.Lp + p) = v;
+      for (int g = 0; g < M::NG; ++g) {
+        const int p = m0 + wm * C::WTM + C::FM * i + M::rrow(lane, g);
+        const int n = n0 + wn * C::WTN + C::FM * j + M::rcol(lane);
+        if (p < P && n < s.d) {
+          const f32x4 a4 = get4(acc[i][j], g);
+          bf16x4 v;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = (__bf16)(scale * a4[r]);
+          *(bf16x4 *)(vts + (int64_t)n * s.Lp + p) = v;
+        }
       }
-    }
 }
 
 // ---------------------------------------------------------------------------
 // O rows of chunks [j0, j0 + nj) of every sequence: O_j = Z_j S_j (S_j stored
 // output-major, d rows of d_ff).
 template <class C>
-__global__ __launch_bounds__(C::NTHR) void k_apply(Slab s, int j0, int nj,
-                                                   const __bf16 *__restrict__ zt,
-                                                   const __bf16 *__restrict__ snap,
-                                                   int64_t snap_seq_stride,
-                                                   int64_t snap_chunk_stride, float *__restrict__ o,
-                                                   const __bf16 *__restrict__ vt,
-                                                   __bf16 *__restrict__ rt) {
+__global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC))) void k_apply(
+    Slab s, int j0, int nj, const __bf16 *__restrict__ zt, const __bf16 *__restrict__ snap,
+    int64_t snap_seq_stride, int64_t snap_chunk_stride, float *__restrict__ o,
+    const __bf16 *__restrict__ vt, __bf16 *__restrict__ rt) {
   static_assert(C::SMEM_T_ELEMS * 2 <= 160 * 1024, "LDS overflow");
   __shared__ __bf16 smem[C::SMEM_T_ELEMS];
+  using M = typename C::M;
   const int nm = (s.Bp + C::BM - 1) / C::BM, nn = (s.d + C::BN - 1) / C::BN;
   const int per_chunk = nm * nn;
   const int id = xcd_remap(blockIdx.x, gridDim.x);
@@ -401,7 +458,6 @@ __global__ __launch_bounds__(C::NTHR) void k_apply(Slab s, int j0, int nj,
   const int m0 = tm * C::BM, n0 = tn * C::BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WN, wn = wave % C::WN;
-  const int r0 = tid / C::KP;
   // A = Z_j read from Zt (token-contiguous rows of d_ff): K row f, M columns
   // = the chunk's slab rows j Bp + m. Columns past the slab's rows (a chunk
   // shorter than the tile) are clamped in bounds; their outputs are dropped.
@@ -412,10 +468,11 @@ __global__ __launch_bounds__(C::NTHR) void k_apply(Slab s, int j0, int nj,
   la.ld = s.Lp;
 #pragma unroll
   for (int i = 0; i < C::AT_PIECES; ++i) {
-    const int id = tid + i * C::NTHR;
-    const int64_t col = min((int64_t)j * s.Bp + m0 + 8 * (id % (C::BM / 8)), s.Lp - 8);
-    la.ptr[i] = zts + (int64_t)(id / (C::BM / 8)) * s.Lp + col;
+    const int id2 = tid + i * C::NTHR;
+    const int64_t col = min((int64_t)j * s.Bp + m0 + 8 * (id2 % (C::BM / 8)), s.Lp - 8);
+    la.ptr[i] = zts + (int64_t)(id2 / (C::BM / 8)) * s.Lp + col;
   }
+  const int r0 = tid / C::KP;
 #pragma unroll
   for (int i = 0; i < C::B_PIECES; ++i) {
     const int n = n0 + r0 + C::RPP * i;
@@ -423,38 +480,41 @@ __global__ __launch_bounds__(C::NTHR) void k_apply(Slab s, int j0, int nj,
   }
   int brow[C::NJ];
 #pragma unroll
-  for (int j = 0; j < C::NJ; ++j) brow[j] = wn * C::WTN + 16 * j;
-  f32x4 acc[C::MI][C::NJ];
+  for (int jj = 0; jj < C::NJ; ++jj) brow[jj] = wn * C::WTN + C::FM * jj;
+  typename C::acc_t acc[C::MI][C::NJ];
   zero_acc<C>(acc);
-  kloop_t<C>(smem, la, lb, s.F / C::BK, tid, wm * 128, brow, acc);
+  kloop_t<C>(smem, la, lb, s.F / C::BK, tid, wm * C::WTM, brow, acc);
 
   const int64_t chunk_tok0 = s.tok0 + (int64_t)j * s.B;
   float *os = o + n_seq * s.x_seq_stride;
 #pragma unroll
   for (int i = 0; i < C::MI; ++i)
 #pragma unroll
-    for (int jj = 0; jj < C::NJ; ++jj) {
-      const int m = m0 + wm * 128 + 16 * i + 4 * (lane >> 4);
-      const int n = n0 + wn * C::WTN + 16 * jj + (lane & 15);
-      if (n >= s.d || m >= s.Bp) continue;
+    for (int jj = 0; jj < C::NJ; ++jj)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t t = chunk_tok0 + m + r;
-        if (m + r < s.B && t < s.L) os[t * s.d + n] = acc[i][jj][r];
-      }
-      if (rt) {
-        const bf16x4 v = *(const bf16x4 *)(vt + (int64_t)n_seq * s.d * s.Lp + (int64_t)n * s.Lp +
-                                           (int64_t)j * s.Bp + m);
-        bf16x4 rv;
+      for (int g = 0; g < M::NG; ++g) {
+        const int m = m0 + wm * C::WTM + C::FM * i + M::rrow(lane, g);
+        const int n = n0 + wn * C::WTN + C::FM * jj + M::rcol(lane);
+        if (n >= s.d || m >= s.Bp) continue;
+        const f32x4 a4 = get4(acc[i][jj], g);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int64_t t = chunk_tok0 + m + r;
-          const bool valid = m + r < s.B && t < s.L;
-          rv[r] = (__bf16)(valid ? s.eta * ((float)v[r] - acc[i][jj][r]) : 0.f);
+          if (m + r < s.B && t < s.L) os[t * s.d + n] = a4[r];
         }
-        *(bf16x4 *)(rt + (int64_t)n_seq * s.d * s.Bp + (int64_t)n * s.Bp + m) = rv;
+        if (rt) {
+          const bf16x4 v = *(const bf16x4 *)(vt + (int64_t)n_seq * s.d * s.Lp + (int64_t)n * s.Lp +
+                                             (int64_t)j * s.Bp + m);
+          bf16x4 rv;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int64_t t = chunk_tok0 + m + r;
+            const bool valid = m + r < s.B && t < s.L;
+            rv[r] = (__bf16)(valid ? s.eta * ((float)v[r] - a4[r]) : 0.f);
+          }
+          *(bf16x4 *)(rt + (int64_t)n_seq * s.d * s.Bp + (int64_t)n * s.Bp + m) = rv;
+        }
       }
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -464,13 +524,14 @@ __global__ __launch_bounds__(C::NTHR) void k_apply(Slab s, int j0, int nj,
 // snap_each_chunk: write S[j] = bf16(W) before chunk j's accumulation;
 // snap_after: write S = bf16(W) after the last chunk.
 template <class C>
-__global__ __launch_bounds__(C::NTHR) void k_update(
+__global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC))) void k_update(
     Slab s, int j_first, int n_chunks, const __bf16 *__restrict__ zt,
     const __bf16 *__restrict__ bsrc, int64_t b_ld, int64_t b_seq_stride, int64_t b_chunk_stride,
     float *__restrict__ w, __bf16 *__restrict__ snap, int64_t snap_seq_stride,
     int64_t snap_chunk_stride, int snap_each_chunk, int snap_after) {
   static_assert(C::SMEM_ELEMS * 2 <= 160 * 1024, "LDS overflow");
   __shared__ __bf16 smem[C::SMEM_ELEMS];
+  using M = typename C::M;
   const int nm = (s.F + C::BM - 1) / C::BM, nn = (s.d + C::BN - 1) / C::BN;
   const int per_seq = nm * nn;
   const int id = xcd_remap(blockIdx.x, gridDim.x);
@@ -484,45 +545,51 @@ __global__ __launch_bounds__(C::NTHR) void k_update(
   const int64_t dF = (int64_t)s.d * s.F;
   float *ws = w + n_seq * dF;
 
-  // accumulators <- W tile: lane holds W^T[c][f .. f+3]
-  f32x4 acc[C::MI][C::NJ];
+  // accumulators <- W tile: each group of 4 accumulator rows is W^T[c][f .. f+3]
+  typename C::acc_t acc[C::MI][C::NJ];
 #pragma unroll
   for (int i = 0; i < C::MI; ++i)
 #pragma unroll
-    for (int jj = 0; jj < C::NJ; ++jj) {
-      const int f = f0 + wm * 128 + 16 * i + 4 * (lane >> 4);
-      const int c = c0 + wn * C::WTN + 16 * jj + (lane & 15);
-      acc[i][jj] = (f < s.F && c < s.d) ? *(const f32x4 *)(ws + (int64_t)c * s.F + f)
-                                         : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int jj = 0; jj < C::NJ; ++jj)
+#pragma unroll
+      for (int g = 0; g < M::NG; ++g) {
+        const int f = f0 + wm * C::WTM + C::FM * i + M::rrow(lane, g);
+        const int c = c0 + wn * C::WTN + C::FM * jj + M::rcol(lane);
+        set4(acc[i][jj], g,
+             (f < s.F && c < s.d) ? *(const f32x4 *)(ws + (int64_t)c * s.F + f)
+                                  : f32x4{0.f, 0.f, 0.f, 0.f});
+      }
   auto write_snap = [&](__bf16 *dst) {
 #pragma unroll
     for (int i = 0; i < C::MI; ++i)
 #pragma unroll
-      for (int jj = 0; jj < C::NJ; ++jj) {
-        const int f = f0 + wm * 128 + 16 * i + 4 * (lane >> 4);
-        const int c = c0 + wn * C::WTN + 16 * jj + (lane & 15);
-        if (f < s.F && c < s.d) {
-          bf16x4 v;
+      for (int jj = 0; jj < C::NJ; ++jj)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = (__bf16)acc[i][jj][r];
-          *(bf16x4 *)(dst + (int64_t)c * s.F + f) = v;
+        for (int g = 0; g < M::NG; ++g) {
+          const int f = f0 + wm * C::WTM + C::FM * i + M::rrow(lane, g);
+          const int c = c0 + wn * C::WTN + C::FM * jj + M::rcol(lane);
+          if (f < s.F && c < s.d) {
+            const f32x4 a4 = get4(acc[i][jj], g);
+            bf16x4 v;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = (__bf16)a4[r];
+            *(bf16x4 *)(dst + (int64_t)c * s.F + f) = v;
+          }
         }
-      }
   };
 
   Loader<C, C::A_PIECES> la;
   Loader<C, C::B_PIECES> lb;
   int brow[C::NJ];
 #pragma unroll
-  for (int j = 0; j < C::NJ; ++j) brow[j] = wn * C::WTN + 16 * j;
+  for (int jj = 0; jj < C::NJ; ++jj) brow[jj] = wn * C::WTN + C::FM * jj;
   const int steps = s.Bp / C::BK;
   const __bf16 *zts = zt + (int64_t)n_seq * s.F * s.Lp;
   const __bf16 *bs = bsrc + n_seq * b_seq_stride;
   for (int jc = 0; jc < n_chunks; ++jc) {
     const int j = j_first + jc;
     if (snap_each_chunk) write_snap(snap + n_seq * snap_seq_stride + jc * snap_chunk_stride);
-  #pragma unroll
+#pragma unroll
     for (int i = 0; i < C::A_PIECES; ++i) {
       const int f = f0 + r0 + C::RPP * i;
       la.ptr[i] = zts + (int64_t)(f < s.F ? f : 0) * s.Lp + (int64_t)j * s.Bp;
@@ -532,17 +599,19 @@ __global__ __launch_bounds__(C::NTHR) void k_update(
       const int c = c0 + r0 + C::RPP * i;
       lb.ptr[i] = bs + (int64_t)(c < s.d ? c : 0) * b_ld + jc * b_chunk_stride;
     }
-    kloop<C>(smem, la, lb, steps, tid, wm * 128, brow, acc);
+    kloop<C>(smem, la, lb, steps, tid, wm * C::WTM, brow, acc);
   }
   if (snap_after) write_snap(snap + n_seq * snap_seq_stride);
 #pragma unroll
   for (int i = 0; i < C::MI; ++i)
 #pragma unroll
-    for (int jj = 0; jj < C::NJ; ++jj) {
-      const int f = f0 + wm * 128 + 16 * i + 4 * (lane >> 4);
-      const int c = c0 + wn * C::WTN + 16 * jj + (lane & 15);
-      if (f < s.F && c < s.d) *(f32x4 *)(ws + (int64_t)c * s.F + f) = acc[i][jj];
-    }
+    for (int jj = 0; jj < C::NJ; ++jj)
+#pragma unroll
+      for (int g = 0; g < M::NG; ++g) {
+        const int f = f0 + wm * C::WTM + C::FM * i + M::rrow(lane, g);
+        const int c = c0 + wn * C::WTN + C::FM * jj + M::rcol(lane);
+        if (f < s.F && c < s.d) *(f32x4 *)(ws + (int64_t)c * s.F + f) = get4(acc[i][jj], g);
+      }
 }
 
 // ---------------------------------------------------------------------------
@@ -567,8 +636,8 @@ __global__ __launch_bounds__(256) void k_conv(Slab s, const __bf16 *__restrict__
   const int n_seq = (int)(gid / groups / runs_per_seq);
   const int64_t p0 = run * CONV_RUN;
   const int64_t j = p0 / s.Bp, i0 = p0 % s.Bp;
-  const int64_t cs = s.tok0 + j * s.B;                 // chunk's first token
-  const int64_t ce = min(cs + (int64_t)s.B, s.L);      // one past its last token
+  const int64_t cs = s.tok0 + j * s.B;               // chunk's first token
+  const int64_t ce = min(cs + (int64_t)s.B, s.L);    // one past its last token
   const int ch = 8 * g;
   float w[KC][8];
 #pragma unroll
@@ -658,18 +727,6 @@ hipError_t launch_update_one(const Slab &s, int j, const WsPtrs &ws, float *w_st
   return hipGetLastError();
 }
 
-// Block shapes and LDS row paddings chosen by timing on MI355X at the 4B layer
-// shape (d 2560, d_ff 9728, 16 chunks of 1024): 8 waves over 256 x 256 with K
-// steps of 64 for the long-K products, 2 waves over 128 x 128 for the update
-// (more, smaller blocks: each one streams every chunk of the slab). Rows padded
-// by 32 bytes measured faster than by 16 on this LDS.
-using GateUpCfg = Cfg<2, 4, 64, 4, 16>;
-using ProjCfg = Cfg<2, 4, 32, 4, 16>;
-using ApplyCfg = Cfg<2, 4, 64, 4, 16, 8>;
-using ApplySmallCfg = Cfg<1, 2, 64, 4, 16, 8>;  // when ApplyCfg would leave most CUs idle
-using UpdateCfg = Cfg<1, 2, 64, 4, 16>;
-static_assert(kChunkAlign % UpdateCfg::BK == 0, "chunk pitch must be whole update K steps");
-
 template <int KC>
 hipError_t launch_conv(const Slab &s, const __bf16 *e, const Weights &w, const WsPtrs &ws,
                        hipStream_t st) {
@@ -679,6 +736,15 @@ hipError_t launch_conv(const Slab &s, const __bf16 *e, const Weights &w, const W
   return hipGetLastError();
 }
 static_assert(kChunkAlign % CONV_RUN == 0, "conv runs must not cross a chunk");
+
+// Block shapes, MFMA shapes and LDS row paddings chosen by timing on MI355X at
+// the 4B layer shape (d 2560, d_ff 9728, 16 chunks of 1024).
+using GateUpCfg = Cfg<2, 4, 64, 16, 16, 8>;
+using ProjCfg = Cfg<2, 4, 32, 16, 16, 8>;
+using ApplyCfg = Cfg<2, 4, 64, 16, 16, 8>;
+using ApplySmallCfg = Cfg<1, 2, 64, 16, 16, 8>;  // when ApplyCfg would leave most CUs idle
+using UpdateCfg = Cfg<1, 2, 64, 16, 16, 8>;
+static_assert(kChunkAlign % UpdateCfg::BK == 0, "chunk pitch must be whole update K steps");
 
 }  // namespace mfma
 
@@ -698,7 +764,6 @@ hipError_t mf_conv(const Slab &s, const __bf16 *e, const Weights &w, const WsPtr
   }
   return hipErrorInvalidValue;
 }
-
 hipError_t mf_gateup(const Slab &s, const __bf16 *x, const Weights &w, const WsPtrs &ws,
                      hipStream_t st) {
   return mfma::launch_gateup<mfma::GateUpCfg>(s, x, w, ws, st);
