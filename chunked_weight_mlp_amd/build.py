@@ -9,7 +9,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libipttt.so")
-SOURCES = ["ipttt.cpp", "kernels_generic.hip", "kernels_mfma.hip"]
+SOURCES = ["ipttt.cpp", "kernels_generic.hip", "kernels_mfma.hip", "kernels_decode.hip"]
 ARCH = "gfx950"
 
 

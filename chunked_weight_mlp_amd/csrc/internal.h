@@ -76,6 +76,16 @@ template <typename T>
 hipError_t gen_apply(const Slab &s, int j0, int nj, const T *snap, int64_t snap_seq_stride,
                      int64_t snap_chunk_stride, const WsPtrs &ws, float *o, hipStream_t st);
 
+// ---- decode (one token per sequence) -----------------------------------------
+// z[b][f] = T(SiLU(x_b . W_g[f]) * (x_b . W_u[f])) for b < batch; x_b = x + b * x_stride.
+template <typename T>
+hipError_t dec_gateup(const T *x, int64_t x_stride, int batch, int d, int F, const T *wg,
+                      const T *wu, T *z, hipStream_t st);
+// o[b][c] = sum_f z[b][f] * T(W[b][c][f]) (W stored [batch][d][F] fp32).
+template <typename T>
+hipError_t dec_apply(const T *z, const float *w, int batch, int d, int F, float *o,
+                     hipStream_t st);
+
 // ---- MFMA kernels (bf16 storage, gfx950) ----------------------------------
 bool mfma_supported(int d, int F);
 hipError_t mf_gateup(const Slab &s, const __bf16 *x, const Weights &w, const WsPtrs &ws,

@@ -269,7 +269,8 @@ namespace {
 
 // Runs the scan over `L` tokens of `n_seq` sequences whose state slots start
 // at `slot0`. x / e / o point at token 0 of the first sequence; sequences are
-// `seq_stride` elements apart.
+// `seq_stride` elements apart. o == nullptr runs the updates only (the
+// outputs of those tokens were produced elsewhere, e.g. token by token).
 template <typename T>
 ipttt_status run_scan(ipttt_layer *h, const T *x, const T *e, float *o, int slot0, int n_seq,
                       int64_t L, int64_t seq_stride, hipStream_t st) {
@@ -322,7 +323,7 @@ ipttt_status run_scan(ipttt_layer *h, const T *x, const T *e, float *o, int slot
       LAUNCH(IPTTT_K_PROJ, mf_proj(s, w, ws, st), "proj launch");
       if (!mse) {
         LAUNCH(IPTTT_K_UPDATE, mf_update_scan(s, ws, wst, st), "update scan launch");
-        LAUNCH(IPTTT_K_APPLY, mf_apply(s, 0, s.nc, ws, o, st), "apply launch");
+        if (o) LAUNCH(IPTTT_K_APPLY, mf_apply(s, 0, s.nc, ws, o, st), "apply launch");
       } else {
         if (k0 == 0) LAUNCH(IPTTT_K_SNAPSHOT, gen_snapshot<T>(s, wst, (T *)ws.s, snap_seq_stride, st), "snapshot launch");
         for (int j = 0; j < s.nc; ++j) {
@@ -344,7 +345,7 @@ ipttt_status run_scan(ipttt_layer *h, const T *x, const T *e, float *o, int slot
                                (int64_t)d.d * s.Lp, ws, wst, next, snap_seq_stride, st),
                  "update launch");
         }
-        LAUNCH(IPTTT_K_APPLY, gen_apply<T>(s, 0, s.nc, S, snap_seq_stride, dF, ws, o, st), "apply launch");
+        if (o) LAUNCH(IPTTT_K_APPLY, gen_apply<T>(s, 0, s.nc, S, snap_seq_stride, dF, ws, o, st), "apply launch");
       } else {
         if (k0 == 0) LAUNCH(IPTTT_K_SNAPSHOT, gen_snapshot<T>(s, wst, S, snap_seq_stride, st), "snapshot launch");
         for (int j = 0; j < s.nc; ++j) {
@@ -395,6 +396,50 @@ ipttt_status ipttt_prefill_layer(ipttt_layer *h, const void *x, const void *e, f
   for (int32_t i = 0; i < batch; ++i)
     if (!h->was_reset[(size_t)i]) return fail(IPTTT_E_STATE, "sequence %d was never reset", i);
   return dispatch(h, x, e, o, 0, batch, seq_len, seq_len * h->desc.d, (hipStream_t)hip_stream);
+}
+
+ipttt_status ipttt_decode_step(ipttt_layer *h, const void *x, const void *e, int64_t seq_stride,
+                               int32_t pos, float *o, int32_t batch, void *hip_stream) {
+  if (!h) return fail(IPTTT_E_INVALID, "handle is NULL");
+  const ipttt_layer_desc &d = h->desc;
+  if (batch < 0 || batch > d.max_batch)
+    return fail(IPTTT_E_INVALID, "batch=%d outside [0, %d]", batch, d.max_batch);
+  if (pos < 0 || pos >= d.chunk)
+    return fail(IPTTT_E_INVALID, "pos=%d outside [0, chunk=%d)", pos, d.chunk);
+  if (batch == 0) return IPTTT_OK;
+  ipttt_status s = check_call(h, x, e, o);
+  if (s != IPTTT_OK) return s;
+  if (batch > 1 && seq_stride < (int64_t)(pos + 1) * d.d)
+    return fail(IPTTT_E_INVALID, "seq_stride=%lld shorter than the %d rows of the chunk so far",
+                (long long)seq_stride, pos + 1);
+  if (seq_stride % 8) return fail(IPTTT_E_INVALID, "seq_stride must be a multiple of 8 elements");
+  for (int32_t i = 0; i < batch; ++i)
+    if (!h->was_reset[(size_t)i]) return fail(IPTTT_E_STATE, "sequence %d was never reset", i);
+  const size_t el = (size_t)elem_size(d.in_dtype);
+  if ((size_t)batch * d.d_ff * el > d.workspace_bytes)
+    return fail(IPTTT_E_WORKSPACE, "workspace too small for %d decode activations", batch);
+  hipStream_t st = (hipStream_t)hip_stream;
+  const char *xt = (const char *)x + (size_t)pos * d.d * el;
+  if (d.in_dtype == IPTTT_BF16) {
+    __bf16 *z = (__bf16 *)d.workspace;
+    LAUNCH(IPTTT_K_GATEUP,
+           ipttt::dec_gateup<__bf16>((const __bf16 *)xt, seq_stride, batch, d.d, d.d_ff,
+                                     (const __bf16 *)d.w_gate, (const __bf16 *)d.w_up, z, st),
+           "decode gate/up launch");
+    LAUNCH(IPTTT_K_APPLY, ipttt::dec_apply<__bf16>(z, d.w_state, batch, d.d, d.d_ff, o, st),
+           "decode apply launch");
+  } else {
+    float *z = (float *)d.workspace;
+    LAUNCH(IPTTT_K_GATEUP,
+           ipttt::dec_gateup<float>((const float *)xt, seq_stride, batch, d.d, d.d_ff,
+                                    (const float *)d.w_gate, (const float *)d.w_up, z, st),
+           "decode gate/up launch");
+    LAUNCH(IPTTT_K_APPLY, ipttt::dec_apply<float>(z, d.w_state, batch, d.d, d.d_ff, o, st),
+           "decode apply launch");
+  }
+  if (pos + 1 == d.chunk)  // chunk complete: its update, as prefill would run it
+    return dispatch(h, x, e, nullptr, 0, batch, d.chunk, seq_stride, st);
+  return IPTTT_OK;
 }
 
 ipttt_status ipttt_prefill_packed(ipttt_layer *h, const void *x, const void *e, float *o,

@@ -202,7 +202,7 @@ struct ApplyOp {  // O rows of chunk j = sum_f Z[p][f] S_j[c][f]; mse: Rt = eta 
     const int n = bz / nj, j = j0 + bz % nj;
     const int64_t t = s.tok0 + (int64_t)j * s.B + m;
     const bool valid = m < s.B && t < s.L;
-    if (valid) o[n * s.x_seq_stride + t * s.d + c] = acc;
+    if (valid && o) o[n * s.x_seq_stride + t * s.d + c] = acc;
     if (rt) {
       float r = 0.f;
       if (valid) r = s.eta * (to_f(vt[(int64_t)n * s.d * s.Lp + (int64_t)c * s.Lp + (int64_t)j * s.Bp + m]) - acc);

@@ -84,9 +84,11 @@ __device__ __forceinline__ void set4(f32x16 &a, int g, f32x4 v) {
   a[4 * g + 3] = v[3];
 }
 
-template <int WM_, int WN_, int BK_, int FM_ = 32, int PAD_ = 16, int PADT_ = 8, int OCC_ = 1>
+template <int WM_, int WN_, int BK_, int FM_ = 32, int PAD_ = 16, int PADT_ = 8, int OCC_ = 1,
+          int GM_ = 8>
 struct Cfg {
   static constexpr int WM = WM_, WN = WN_, BK = BK_, FM = FM_;
+  static constexpr int GM = GM_;  // row tiles per group in the tile order (tile_of)
   static constexpr int OCC = OCC_;  // waves per SIMD the register allocation must allow
   using M = Mfma<FM>;
   using acc_t = typename M::acc_t;
@@ -125,8 +127,8 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
 
 // Tile order inside a grid of (nm x nn) tiles: groups of GM row tiles, column
 // tile slowest within a group, so neighbouring blocks share both operands.
+template <int GM>
 __device__ __forceinline__ void tile_of(int id, int nm, int nn, int &tm, int &tn) {
-  constexpr int GM = 8;
   const int group = id / (GM * nn);
   const int first = group * GM;
   const int gm = min(GM, nm - first);
@@ -320,7 +322,7 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   const int n_seq = id / per_seq;
   int tm, tn;
-  tile_of(id % per_seq, nm, nn, tm, tn);
+  tile_of<C::GM>(id % per_seq, nm, nn, tm, tn);
   const int m0 = tm * C::BM, f0 = tn * FT;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WN, wn = wave % C::WN;
@@ -393,7 +395,7 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   const int n_seq = id / per_seq;
   int tm, tn;
-  tile_of(id % per_seq, nm, nn, tm, tn);
+  tile_of<C::GM>(id % per_seq, nm, nn, tm, tn);
   const int m0 = tm * C::BM, n0 = tn * C::BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WN, wn = wave % C::WN;
@@ -454,7 +456,7 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
   const int bz = id / per_chunk;
   const int n_seq = bz / nj, jl = bz % nj, j = j0 + jl;
   int tm, tn;
-  tile_of(id % per_chunk, nm, nn, tm, tn);
+  tile_of<C::GM>(id % per_chunk, nm, nn, tm, tn);
   const int m0 = tm * C::BM, n0 = tn * C::BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WN, wn = wave % C::WN;
@@ -486,7 +488,7 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
   kloop_t<C>(smem, la, lb, s.F / C::BK, tid, wm * C::WTM, brow, acc);
 
   const int64_t chunk_tok0 = s.tok0 + (int64_t)j * s.B;
-  float *os = o + n_seq * s.x_seq_stride;
+  float *os = o ? o + n_seq * s.x_seq_stride : nullptr;  // nullptr: residual only
 #pragma unroll
   for (int i = 0; i < C::MI; ++i)
 #pragma unroll
@@ -500,7 +502,7 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int64_t t = chunk_tok0 + m + r;
-          if (m + r < s.B && t < s.L) os[t * s.d + n] = a4[r];
+          if (os && m + r < s.B && t < s.L) os[t * s.d + n] = a4[r];
         }
         if (rt) {
           const bf16x4 v = *(const bf16x4 *)(vt + (int64_t)n_seq * s.d * s.Lp + (int64_t)n * s.Lp +
@@ -537,7 +539,7 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   const int n_seq = id / per_seq;
   int tm, tn;
-  tile_of(id % per_seq, nm, nn, tm, tn);
+  tile_of<C::GM>(id % per_seq, nm, nn, tm, tn);
   const int f0 = tm * C::BM, c0 = tn * C::BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WN, wn = wave % C::WN;
@@ -743,7 +745,7 @@ using GateUpCfg = Cfg<2, 4, 64, 16, 16, 8>;
 using ProjCfg = Cfg<2, 4, 32, 16, 16, 8>;
 using ApplyCfg = Cfg<2, 4, 64, 16, 16, 8>;
 using ApplySmallCfg = Cfg<1, 2, 64, 16, 16, 8>;  // when ApplyCfg would leave most CUs idle
-using UpdateCfg = Cfg<1, 2, 64, 16, 16, 8>;
+using UpdateCfg = Cfg<1, 2, 64, 16, 16, 8, 1, 16>;
 static_assert(kChunkAlign % UpdateCfg::BK == 0, "chunk pitch must be whole update K steps");
 
 }  // namespace mfma

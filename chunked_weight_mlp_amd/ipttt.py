@@ -29,6 +29,7 @@ IPTTT_FLAG_GENERIC_KERNELS = 1
 
 EXPORTS = (
     "ipttt_workspace_bytes", "ipttt_init", "ipttt_prefill_layer", "ipttt_prefill_packed",
+    "ipttt_decode_step",
     "ipttt_reset_fast_weights", "ipttt_profile_begin", "ipttt_profile_end", "ipttt_destroy",
     "ipttt_status_str", "ipttt_last_error",
 )
@@ -86,6 +87,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ipttt_prefill_layer.restype = ctypes.c_int
     lib.ipttt_prefill_packed.argtypes = [vp, vp, vp, vp, i32, i64, ctypes.POINTER(i64), i32, vp]
     lib.ipttt_prefill_packed.restype = ctypes.c_int
+    lib.ipttt_decode_step.argtypes = [vp, vp, vp, i64, i32, vp, i32, vp]
+    lib.ipttt_decode_step.restype = ctypes.c_int
     lib.ipttt_reset_fast_weights.argtypes = [vp, i32, i32, vp]
     lib.ipttt_reset_fast_weights.restype = ctypes.c_int
     lib.ipttt_profile_begin.argtypes = [vp]
@@ -152,6 +155,11 @@ def ipttt_prefill_packed(h, x, e, o, slot: int, seq_len: int, doc_starts, stream
     arr = (ctypes.c_int64 * max(1, len(starts)))(*starts)
     _check(load().ipttt_prefill_packed(h, _ptr(x), _ptr(e), _ptr(o), slot, seq_len, arr,
                                        len(starts), _stream(stream)))
+
+
+def ipttt_decode_step(h, x, e, seq_stride: int, pos: int, o, batch: int, stream=None) -> None:
+    _check(load().ipttt_decode_step(h, _ptr(x), _ptr(e), seq_stride, pos, _ptr(o), batch,
+                                    _stream(stream)))
 
 
 def ipttt_reset_fast_weights(h, first_seq: int, n_seq: int, stream=None) -> None:
@@ -235,6 +243,16 @@ class Layer:
         if o is None:
             o = torch.empty(x.shape, dtype=torch.float32, device=x.device)
         ipttt_prefill_packed(self.handle, x, e, o, slot, x.shape[0], doc_starts, stream)
+        return o
+
+    def decode_step(self, x_chunk, e_chunk, pos: int, o=None, stream=None):
+        """x_chunk, e_chunk: [batch, B, d] buffers of the chunk in progress whose
+        rows 0..pos are filled (the new token at row pos); returns o [batch, d]."""
+        if o is None:
+            o = torch.empty((x_chunk.shape[0], x_chunk.shape[2]), dtype=torch.float32,
+                            device=x_chunk.device)
+        ipttt_decode_step(self.handle, x_chunk, e_chunk, x_chunk.shape[1] * x_chunk.shape[2], pos, o,
+                          x_chunk.shape[0], stream)
         return o
 
     def close(self) -> None:

@@ -135,6 +135,22 @@ ipttt_status ipttt_prefill_packed(ipttt_layer *h, const void *x, const void *e, 
                                   int32_t slot, int64_t seq_len, const int64_t *doc_starts,
                                   int32_t n_docs, void *hip_stream);
 
+/* Decode: one new token for each of sequences 0..batch-1, all at the same
+ * position inside their current chunk (the step after prefill while the fast
+ * weight keeps adapting, explainer page §6). The caller keeps the chunk in
+ * progress: x and e point at its first token for sequence 0, sequence i's
+ * chunk starts seq_stride elements later, rows are d apart, and rows
+ * 0..pos hold the chunk so far with the new token at row pos (0 <= pos < B).
+ * Writes o[batch][d] fp32 = z W_k for the new token, where z is its gated
+ * activation and W_k the fast weight of the chunk (the last update happened
+ * at the chunk's start). When pos == B - 1 the chunk is complete and its
+ * update W_{k+1} = W_k + eta Z^T V (or the MSE rule) runs from rows 0..B-1,
+ * exactly as prefill would. The chunk must start on a chunk boundary of the
+ * scan (after a reset, a completed chunk, or a prefill call). Same
+ * validation and error codes as ipttt_prefill_layer. */
+ipttt_status ipttt_decode_step(ipttt_layer *h, const void *x, const void *e, int64_t seq_stride,
+                               int32_t pos, float *o, int32_t batch, void *hip_stream);
+
 /* w_state[s] := w0 bitwise for s in first_seq..first_seq+n_seq-1 (document
  * boundary, explainer page §3.2) and marks those slots as reset. */
 ipttt_status ipttt_reset_fast_weights(ipttt_layer *h, int32_t first_seq, int32_t n_seq,

@@ -207,3 +207,30 @@ def test_null_handle(lib):
     assert lib.ipttt_prefill_layer(None, None, None, None, 1, 1, None) == B.IPTTT_E_INVALID
     assert lib.ipttt_reset_fast_weights(None, 0, 1, None) == B.IPTTT_E_INVALID
     assert lib.ipttt_prefill_packed(None, None, None, None, 0, 1, None, 0, None) == B.IPTTT_E_INVALID
+
+
+def test_decode_errors_before_device_work(lib):
+    mem = FakeMem()
+    desc = make_desc(mem)
+    h = B.ipttt_init(desc)
+    x, e, o = mem.ptr(), mem.ptr(), mem.ptr()
+    try:
+        for pos in (-1, 128):
+            with pytest.raises(B.IptttError) as ei:
+                B.ipttt_decode_step(h, x, e, 128 * 64, pos, o, 1, stream=0)
+            assert ei.value.status == B.IPTTT_E_INVALID and "pos" in str(ei.value)
+        with pytest.raises(B.IptttError) as ei:
+            B.ipttt_decode_step(h, x, e, 128 * 64, 0, o, 3, stream=0)
+        assert ei.value.status == B.IPTTT_E_INVALID
+        with pytest.raises(B.IptttError) as ei:
+            B.ipttt_decode_step(h, x, e, 64, 5, o, 2, stream=0)   # stride shorter than the chunk so far
+        assert ei.value.status == B.IPTTT_E_INVALID
+        with pytest.raises(B.IptttError) as ei:
+            B.ipttt_decode_step(h, x, e, 128 * 64, 3, o, 1, stream=0)
+        assert ei.value.status == B.IPTTT_E_STATE
+        with pytest.raises(B.IptttError) as ei:
+            B.ipttt_decode_step(h, None, e, 128 * 64, 3, o, 1, stream=0)
+        assert ei.value.status == B.IPTTT_E_INVALID
+        B.ipttt_decode_step(h, x, e, 128 * 64, 3, o, 0, stream=0)   # empty batch: no-op
+    finally:
+        B.ipttt_destroy(h)

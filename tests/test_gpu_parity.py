@@ -250,3 +250,44 @@ def test_profile_records_every_kernel():
     prof = B.ipttt_profile_end(layer.handle)
     for k in ("gateup", "conv", "proj", "update", "apply"):
         assert prof[k][0] >= 1 and prof[k][1] > 0, (k, prof)
+
+
+@pytest.mark.parametrize("dtype,update", [("bf16", "linear"), ("bf16", "mse"), ("f32", "linear")])
+def test_decode_token_by_token(dtype, update):
+    """Decode T tokens one at a time (two sequences), with an earlier prefill of
+    one chunk: outputs of every token and the weight after the last completed
+    chunk against the oracle's token-at-a-time continuation."""
+    Bc, d, F = 64, 256, 640
+    w = wl.Workload("decode", 2, d, F, 64 + 2 * Bc + 9, Bc, dtype, 1e-2 if update == "linear" else 2e-3,
+                    update)
+    weights = wl.make_weights(w)
+    x, e = wl.make_inputs(w)
+    layer = make_layer(w, weights)
+    layer.reset()
+    xd, ed = x.to(DEV), e.to(DEV)
+    o_pre = layer.prefill(xd[:, :64].contiguous(), ed[:, :64].contiguous())
+    xc = torch.zeros((2, Bc, d), dtype=xd.dtype, device=DEV)
+    ec = torch.zeros_like(xc)
+    outs = []
+    for t in range(64, w.seq_len):
+        pos = (t - 64) % Bc
+        xc[:, pos] = xd[:, t]
+        ec[:, pos] = ed[:, t]
+        outs.append(layer.decode_step(xc, ec, pos))
+    torch.cuda.synchronize()
+    o_dec = torch.stack(outs, 1).double().cpu().numpy()
+    ow = wl.to_oracle(weights)
+    X, E = x.double().numpy(), e.double().numpy()
+    tol = TOL[dtype]
+    W_ref = []
+    for n in range(2):
+        O_ref, W_after = oracle.decode_steps(X[n], E[n], ow["W_g"], ow["W_u"], ow["conv_w"], ow["Proj"],
+                                             ow["W_0"], w.eta, Bc, update=update)
+        eo = rel_fro(o_dec[n], O_ref[64:])
+        ep = rel_fro(o_pre[n].double().cpu().numpy(), O_ref[:64])
+        say(f"[decode] {dtype} {update} seq {n}: rel_fro O(decode)={eo:.3e} O(prefill)={ep:.3e}")
+        assert eo <= tol and ep <= tol
+        W_ref.append(W_after)
+    ew = rel_fro(w_pages(layer, 2), np.stack(W_ref))
+    say(f"[decode] {dtype} {update}: rel_fro W={ew:.3e}")
+    assert ew <= tol
