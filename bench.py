@@ -25,7 +25,7 @@ import workloads as wl  # noqa: E402
 METRIC = "fast-weight prefill tokens/s per MLP layer at L=128k,B=1024; % MFMA/HBM roofline"
 KERNEL_SRC = os.path.join(ROOT, "chunked_weight_mlp_amd", "csrc", "kernels_mfma.hip")
 KERNEL_TAGS = {"gateup": "k_gateup", "conv": "k_conv", "proj": "k_proj", "update": "k_update",
-               "apply": "k_apply", "copy": "copyBuffer"}
+               "apply": "k_apply", "gram": "k_gram", "copy": "copyBuffer"}
 
 
 def kernel_source_hash() -> str:
@@ -86,20 +86,36 @@ PEAK = {"bf16": 2500.0, "f32": 157.3}  # dense TFLOP/s (MFMA bf16, fp32)
 HBM_PEAK = 8000.0                       # GB/s
 
 
-def kernel_work(w: wl.Workload, tokens: int):
+def group_chunks(w: wl.Workload, requested: int, generic: bool) -> int:
+    """Chunks per W snapshot, as the library picks them: groups of about 1024
+    chunk-padded rows on the bf16 MFMA path with the linear rule, else 1."""
+    if w.update != "linear" or w.dtype != "bf16" or generic:
+        return 1
+    return requested or max(1, 1024 // (-(-w.chunk // 64) * 64))
+
+
+def kernel_work(w: wl.Workload, tokens: int, G: int = 1):
     """Algorithmic FLOPs and HBM bytes of one launch of each kernel over `tokens`
-    tokens (all sequences of one pass). Bytes count each operand once."""
+    tokens (all sequences of one pass), with one W snapshot per G chunks. Bytes
+    count each operand once. The apply counts the method's product Z W only; the
+    Gram kernel's work (and the apply's use of it) is what the chunk-parallel
+    form spends to skip snapshots, reported for its own rate."""
     d, F, Kc = w.d, w.d_ff, w.conv_k
     el = 2 if w.dtype == "bf16" else 4
     chunks = -(-tokens // w.chunk)
-    return {
+    groups = -(-chunks // G)
+    rows = G * (-(-w.chunk // 64) * 64)
+    work = {
         "gateup": (4 * d * F * tokens, el * (tokens * d + 2 * F * d + 2 * tokens * F)),
         "conv": (2 * Kc * d * tokens, el * (2 * tokens * d + Kc * d)),
         "proj": (2 * d * d * tokens, el * (2 * tokens * d + d * d)),
-        # linear scan: Z^T and V read once, W read and written once, a bf16 copy of W per chunk
-        "update": (2 * d * F * tokens, el * tokens * (F + d) + 8 * F * d + el * chunks * F * d),
-        "apply": (2 * d * F * tokens, el * tokens * F + el * chunks * F * d + 4 * tokens * d),
+        # linear scan: Z^T and V read once, W read and written once, a bf16 copy of W per group
+        "update": (2 * d * F * tokens, el * tokens * (F + d) + 8 * F * d + el * groups * F * d),
+        "apply": (2 * d * F * tokens, el * tokens * F + el * groups * F * d + 4 * tokens * d),
     }
+    if G > 1:  # block-causal Z Z^T: about half of each group's rows x rows x F
+        work["gram"] = (rows * F * tokens, el * tokens * F + el * tokens * rows // 2)
+    return work
 
 
 def cpu_baseline(w: wl.Workload, x, e, weights, n_chunks: int):
@@ -137,6 +153,8 @@ def main():
     ap.add_argument("--cpu-chunks", type=int, default=40, help="chunks in the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--generic", action="store_true", help="generic FMA kernels instead of MFMA")
+    ap.add_argument("--group-chunks", type=int, default=0,
+                    help="chunks per W snapshot of the linear scan (0 = library choice, 1 = plain)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc "
                          "counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) and exit")
@@ -171,7 +189,7 @@ def main():
     xd, ed = x.to(dev), e.to(dev)
     slab = args.slab_chunks or w.n_chunks
     layer = ipttt.Layer(**wdev, chunk=w.chunk, eta=w.eta, update=w.update, max_batch=w.n_seq,
-                        slab_chunks=slab,
+                        slab_chunks=slab, group_chunks=args.group_chunks,
                         flags=ipttt.IPTTT_FLAG_GENERIC_KERNELS if args.generic else 0)
     o = torch.empty(xd.shape, dtype=torch.float32, device=dev)
 
@@ -204,9 +222,12 @@ def main():
           flush=True)
 
     # per-kernel live durations and the dominant kernel's roofline
+    G = min(group_chunks(w, args.group_chunks, args.generic), slab)
+    if slab < w.n_chunks:
+        slab = slab // G * G   # the library runs whole groups per pass
     passes = -(-w.n_chunks // slab)
     tok_per_pass = w.n_seq * min(w.seq_len, slab * w.chunk)
-    work = kernel_work(w, tok_per_pass)
+    work = kernel_work(w, tok_per_pass, G)
     kernels = {}
     for k, (n, ms) in prof.items():
         if n == 0:
@@ -254,7 +275,8 @@ def main():
         "data": "synthetic (seeded Gaussian inputs and weights of the workload's shape)",
         "config": {"workload": w.name, "d": w.d, "d_ff": w.d_ff, "seq_len": w.seq_len,
                    "chunk": w.chunk, "batch": w.n_seq, "update": w.update, "eta": w.eta,
-                   "chunks_per_pass": slab, "kernels": "generic" if args.generic else "mfma"},
+                   "chunks_per_pass": slab, "chunks_per_snapshot": G,
+                   "kernels": "generic" if args.generic else "mfma"},
         "tflops": round(w.flops_per_token() * tokens / (ms_step * 1e-3) / 1e12, 2),
         "roofline": roof,
         "kernels": kernels,

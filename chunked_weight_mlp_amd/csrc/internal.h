@@ -24,6 +24,8 @@ struct Slab {
   int B, Bp;        // chunk, padded chunk pitch
   int nc;           // chunks in this slab
   int nc_cap;       // chunks the workspace is laid out for (row pitch = nc_cap*Bp)
+  int G;            // chunks per group sharing one W snapshot (1: one per chunk)
+  int ng_cap;       // groups the workspace is laid out for = ceil(nc_cap / G)
   int64_t Lp;       // padded rows per sequence in the workspace = nc_cap * Bp
   int64_t tok0;     // first token of the slab within each sequence
   int64_t L;        // tokens per sequence in the call
@@ -34,11 +36,16 @@ struct Slab {
 
 // Byte offsets of the workspace buffers (all 256-byte aligned).
 struct WsLayout {
-  size_t z, zt, c, vt, s, rt, total;
+  size_t z, zt, c, vt, s, rt, p, total;
 };
 
+// Largest rows per chunk group (G * Bp) of the chunk-parallel scan.
+constexpr int kMaxGroupRows = 4096;
+
 // need_z: the token-major copy of Z (read by the generic apply only).
-WsLayout ws_layout(int elem, int n_seq, int d, int F, int Bp, int nc_cap, int mse, int need_z);
+// G: chunks per snapshot group (linear rule; 1 for MSE and the generic path).
+WsLayout ws_layout(int elem, int n_seq, int d, int F, int Bp, int nc_cap, int G, int mse,
+                   int need_z);
 
 // Pointers into the workspace for one call.
 struct WsPtrs {
@@ -46,8 +53,9 @@ struct WsPtrs {
   void *zt;  // [n][F][Lp]      Z transposed (token-contiguous)
   void *c;   // [n][Lp][d]      conv output
   void *vt;  // [n][d][Lp]      target V transposed; eta*V for the linear rule
-  void *s;   // linear: [n][nc_cap][d][F] W snapshot per chunk; mse: [n][d][F]
+  void *s;   // linear: [n][ng_cap][d][F] W snapshot per group; mse: [n][d][F]
   void *rt;  // mse: [n][d][Bp] eta*(V - O) of the current chunk, transposed
+  void *p;   // G > 1: [n][ng_cap][G Bp][G Bp] block-causal Gram, P^T[s][m] = z_m . z_s
 };
 
 struct Weights {
@@ -93,13 +101,19 @@ hipError_t mf_gateup(const Slab &s, const __bf16 *x, const Weights &w, const WsP
 hipError_t mf_conv(const Slab &s, const __bf16 *e, const Weights &w, const WsPtrs &ws,
                    hipStream_t st);
 hipError_t mf_proj(const Slab &s, const Weights &w, const WsPtrs &ws, hipStream_t st);
-// Linear rule: for each chunk j of the slab, write snapshot S[j] = bf16(W) then
-// W += Zt_j^T-contract Vt_j; W stays in registers across the slab's chunks.
+// Linear rule: for each group q of G chunks of the slab, write snapshot
+// S[q] = bf16(W) then W += sum over the group's tokens of z_t^T (eta v_t); W
+// stays in registers across the slab.
 hipError_t mf_update_scan(const Slab &s, const WsPtrs &ws, float *w_state, hipStream_t st);
+// G > 1: masked Gram of every group of the slab, P^T[s][m] = z_m . z_s when
+// token s lies in an earlier chunk of the group than token m, else 0.
+hipError_t mf_gram(const Slab &s, const WsPtrs &ws, hipStream_t st);
 // MSE rule, one chunk j: W += Rt Zt_j^T-contract, snapshot S = bf16(new W).
 hipError_t mf_update_one(const Slab &s, int j, const WsPtrs &ws, float *w_state,
                          hipStream_t st);
-hipError_t mf_apply(const Slab &s, int j0, int nj, const WsPtrs &ws, float *o,
+// O rows of groups [q0, q0 + nq) (G = 1: chunks): O = Z S_q, plus P (eta V)
+// when G > 1; the MSE rule (G = 1, nq = 1) also writes Rt.
+hipError_t mf_apply(const Slab &s, int q0, int nq, const WsPtrs &ws, float *o,
                     hipStream_t st);
 
 }  // namespace ipttt

@@ -1,19 +1,25 @@
 // Host side of libipttt: argument validation, workspace planning and the
 // chunk-scan launch sequence. Kernels live in kernels_*.hip.
 //
-// Linear rule, per slab of chunks (all sequences of the call at once):
+// Linear rule, per slab of chunks (all sequences of the call at once), the
+// chunks taken in groups of G (G = 1: plain chunk scan):
 //   gate/up -> Z, Zt;  conv -> C;  proj -> Vt = eta * V
-//   update scan: snapshot S_j = W before chunk j, then W += eta Z_j^T V_j
-//   apply (batched over chunks): O_j = Z_j S_j
-// The update of one W tile never needs another tile, and the apply of chunk j
-// needs only the snapshot S_j, so applying every chunk after the scan is the
-// same computation as applying each chunk before its update.
+//   update scan: snapshot S_q = W before group q, then W += eta Z_q^T V_q
+//   Gram (G > 1): P_q = block-causal Z_q Z_q^T (token s of an earlier chunk
+//   of the group than token t, else 0)
+//   apply (batched over groups): O_q = Z_q S_q + P_q (eta V_q)
+// The update of one W tile never needs another tile, and the apply of group q
+// needs only S_q and the group's own Z and V, so applying every group after
+// the scan is the same computation as applying each chunk before its update:
+// for chunk k of group q, W_k = S_q + eta sum over the group's earlier chunks
+// of Z_j^T V_j, and Z_k W_k expands to the two terms above.
 // MSE rule, per chunk: apply with S = W (current) -> O_j and Rt = eta (V - O_j);
 // update W += Z_j^T Rt and refresh S.
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <new>
 #include <string>
 #include <vector>
@@ -70,6 +76,12 @@ ipttt_status check_sizes(const ipttt_layer_desc *d) {
   if (!(d->eta == d->eta) || d->eta > 3.0e38f || d->eta < -3.0e38f)
     return fail(IPTTT_E_INVALID, "eta is not finite");
   if (d->flags & ~IPTTT_FLAG_GENERIC_KERNELS) return fail(IPTTT_E_INVALID, "unknown flags 0x%x", d->flags);
+  if (d->group_chunks < 0) return fail(IPTTT_E_INVALID, "group_chunks=%d must be >= 0", d->group_chunks);
+  if ((int64_t)d->group_chunks * ipttt::round_up(d->chunk, ipttt::kChunkAlign) > ipttt::kMaxGroupRows)
+    return fail(IPTTT_E_UNSUPPORTED, "group_chunks=%d: %d chunk-padded rows per group exceed %d",
+                d->group_chunks,
+                (int)(d->group_chunks * ipttt::round_up(d->chunk, ipttt::kChunkAlign)),
+                ipttt::kMaxGroupRows);
   return IPTTT_OK;
 }
 
@@ -78,6 +90,19 @@ int chunk_pitch(int B) { return (int)ipttt::round_up(B, ipttt::kChunkAlign); }
 bool use_mfma(const ipttt_layer_desc *d) {
   return d->in_dtype == IPTTT_BF16 && !(d->flags & IPTTT_FLAG_GENERIC_KERNELS) &&
          ipttt::mfma_supported(d->d, d->d_ff);
+}
+
+// Chunk-padded rows per group when the descriptor leaves the choice to the
+// library: enough to give the apply full-height tiles and cut the W snapshots
+// to one per 1024 rows.
+constexpr int kDefaultGroupRows = 1024;
+
+// Chunks per group of the chunk-parallel scan (bf16 MFMA path, linear rule);
+// 1 elsewhere. A slab of n chunks uses min(G, n).
+int group_chunks(const ipttt_layer_desc *d) {
+  if (!use_mfma(d) || d->update != IPTTT_UPDATE_LINEAR) return 1;
+  if (d->group_chunks > 0) return d->group_chunks;
+  return std::max(1, kDefaultGroupRows / chunk_pitch(d->chunk));
 }
 
 ipttt_status hip_status(hipError_t e, const char *what) {
@@ -131,9 +156,11 @@ struct ProfScope {
 
 namespace ipttt {
 
-WsLayout ws_layout(int elem, int n_seq, int d, int F, int Bp, int nc_cap, int mse, int need_z) {
+WsLayout ws_layout(int elem, int n_seq, int d, int F, int Bp, int nc_cap, int G, int mse,
+                   int need_z) {
   WsLayout w{};
   const size_t Lp = (size_t)nc_cap * Bp;
+  const size_t ng = (size_t)(nc_cap + G - 1) / G, RG = (size_t)G * Bp;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -144,8 +171,9 @@ WsLayout ws_layout(int elem, int n_seq, int d, int F, int Bp, int nc_cap, int ms
   w.zt = take((size_t)n_seq * F * Lp * elem);
   w.c = take((size_t)n_seq * Lp * d * elem);
   w.vt = take((size_t)n_seq * d * Lp * elem);
-  w.s = take((size_t)n_seq * (mse ? 1 : nc_cap) * d * F * elem);
+  w.s = take((size_t)n_seq * (mse ? 1 : ng) * d * F * elem);
   w.rt = mse ? take((size_t)n_seq * d * Bp * elem) : off;
+  w.p = G > 1 ? take((size_t)n_seq * ng * RG * RG * elem) : off;
   w.total = off;
   return w;
 }
@@ -174,8 +202,9 @@ size_t ipttt_workspace_bytes(const ipttt_layer_desc *desc, int32_t batch, int32_
   g_last_error = saved;
   if (s != IPTTT_OK || batch < 1 || slab_chunks < 1) return 0;
   return ipttt::ws_layout(elem_size(desc->in_dtype), batch, desc->d, desc->d_ff,
-                          chunk_pitch(desc->chunk), slab_chunks, desc->update == IPTTT_UPDATE_MSE,
-                          !use_mfma(desc))
+                          chunk_pitch(desc->chunk), slab_chunks,
+                          std::min(group_chunks(desc), (int)slab_chunks),
+                          desc->update == IPTTT_UPDATE_MSE, !use_mfma(desc))
       .total;
 }
 
@@ -280,22 +309,31 @@ ipttt_status run_scan(ipttt_layer *h, const T *x, const T *e, float *o, int slot
   const int mse = d.update == IPTTT_UPDATE_MSE;
   const int B = d.chunk, Bp = chunk_pitch(B);
   const int64_t K = (L + B - 1) / B;
-  // largest slab that fits the workspace
+  const int G_max = group_chunks(&d);
+  // workspace of a slab of n chunks (its groups hold min(G_max, n) chunks);
+  // non-decreasing in n, so the largest slab that fits is found by bisection
+  auto layout = [&](int64_t n) {
+    return ws_layout(elem, n_seq, d.d, d.d_ff, Bp, (int)n, (int)std::min<int64_t>(G_max, n), mse,
+                     !h->mfma);
+  };
   int64_t lo = 1, hi = K;
-  if (ws_layout(elem, n_seq, d.d, d.d_ff, Bp, 1, mse, !h->mfma).total > d.workspace_bytes)
+  if (layout(1).total > d.workspace_bytes)
     return fail(IPTTT_E_WORKSPACE, "workspace_bytes=%zu cannot hold one chunk of %d sequences (%zu)",
-                d.workspace_bytes, n_seq, ws_layout(elem, n_seq, d.d, d.d_ff, Bp, 1, mse, !h->mfma).total);
+                d.workspace_bytes, n_seq, layout(1).total);
   while (lo < hi) {
     const int64_t mid = (lo + hi + 1) / 2;
-    if (ws_layout(elem, n_seq, d.d, d.d_ff, Bp, (int)mid, mse, !h->mfma).total <= d.workspace_bytes)
+    if (layout(mid).total <= d.workspace_bytes)
       lo = mid;
     else
       hi = mid - 1;
   }
-  const int nc_cap = (int)lo;
-  const WsLayout lay = ws_layout(elem, n_seq, d.d, d.d_ff, Bp, nc_cap, mse, !h->mfma);
+  const int G = (int)std::min<int64_t>(G_max, lo);
+  // slabs of whole groups unless one slab covers the call
+  const int nc_cap = (int)(lo < K ? lo / G * G : lo);
+  const WsLayout lay = ws_layout(elem, n_seq, d.d, d.d_ff, Bp, nc_cap, G, mse, !h->mfma);
   char *base = (char *)d.workspace;
-  WsPtrs ws{base + lay.z, base + lay.zt, base + lay.c, base + lay.vt, base + lay.s, base + lay.rt};
+  WsPtrs ws{base + lay.z,  base + lay.zt, base + lay.c, base + lay.vt,
+            base + lay.s,  base + lay.rt, base + lay.p};
   Weights w{d.w_gate, d.w_up, d.proj, d.conv_w};
   float *wst = d.w_state + (size_t)slot0 * d.d * d.d_ff;
   const int64_t dF = (int64_t)d.d * d.d_ff;
@@ -311,6 +349,8 @@ ipttt_status run_scan(ipttt_layer *h, const T *x, const T *e, float *o, int slot
     s.Bp = Bp;
     s.nc = (int)std::min<int64_t>(nc_cap, K - k0);
     s.nc_cap = nc_cap;
+    s.G = G;
+    s.ng_cap = (nc_cap + G - 1) / G;
     s.Lp = (int64_t)nc_cap * Bp;
     s.tok0 = k0 * B;
     s.L = L;
@@ -323,7 +363,10 @@ ipttt_status run_scan(ipttt_layer *h, const T *x, const T *e, float *o, int slot
       LAUNCH(IPTTT_K_PROJ, mf_proj(s, w, ws, st), "proj launch");
       if (!mse) {
         LAUNCH(IPTTT_K_UPDATE, mf_update_scan(s, ws, wst, st), "update scan launch");
-        if (o) LAUNCH(IPTTT_K_APPLY, mf_apply(s, 0, s.nc, ws, o, st), "apply launch");
+        if (o) {
+          if (G > 1) LAUNCH(IPTTT_K_GRAM, mf_gram(s, ws, st), "Gram launch");
+          LAUNCH(IPTTT_K_APPLY, mf_apply(s, 0, (s.nc + G - 1) / G, ws, o, st), "apply launch");
+        }
       } else {
         if (k0 == 0) LAUNCH(IPTTT_K_SNAPSHOT, gen_snapshot<T>(s, wst, (T *)ws.s, snap_seq_stride, st), "snapshot launch");
         for (int j = 0; j < s.nc; ++j) {

@@ -16,13 +16,17 @@
 //              block's B rows are gate rows, half up rows), K = d. Writes Zt
 //              (rows of d_ff, token-contiguous), the only copy of Z.
 //   k_proj     Vt = scale * (C Proj)^T     M = slab rows, N = d, K = d.
-//   k_apply    O = Z_j S_j                 M = chunk rows, N = d, K = d_ff,
-//              batched over (sequence, chunk); A comes from Zt through LDS
-//              transpose reads. The MSE rule also writes Rt = eta (V - O)^T.
+//   k_apply    O = Z_q S_q (+ P_q (eta V_q))  M = rows of a group of G
+//              chunks, N = d, K = d_ff (then the group's earlier tokens),
+//              batched over (sequence, group); A comes from Zt (then P^T)
+//              through LDS transpose reads. The MSE rule (G = 1) also writes
+//              Rt = eta (V - O)^T.
+//   k_gram     P^T = block-causal Z_q Z_q^T of each group (G > 1), both
+//              operands read transposed; only the tiles the apply reads.
 //   k_update   W^T tile (BM d_ff rows x BN d columns, fp32) held in the
-//              accumulators across the chunks of a slab: per chunk, optionally
-//              write the bf16 snapshot S_j, then accumulate Zt_j . Vt_j over
-//              the chunk's tokens.
+//              accumulators across the chunks of a slab: per group of G
+//              chunks, optionally write the bf16 snapshot S_q, then
+//              accumulate Zt . Vt over the group's tokens.
 //   k_conv     depthwise conv of E, vector loads, sliding window.
 #include "internal.h"
 
@@ -109,9 +113,14 @@ struct Cfg {
   static constexpr int AT_PIECES = BK * (BM / 8) / NTHR;
   static constexpr int AT_STAGE = BK * PITCH_T;
   static constexpr int SMEM_T_ELEMS = 2 * (AT_STAGE + B_STAGE);
+  // both operands K-major ([BK rows of K][BM or BN columns])
+  static constexpr int PITCH_TB = BN + PADT_;
+  static constexpr int BT_STAGE = BK * PITCH_TB;
+  static constexpr int SMEM_TT_ELEMS = 2 * (AT_STAGE + BT_STAGE);
   static_assert(BK % 32 == 0 && BM % RPP == 0 && BN % RPP == 0, "bad tile config");
   static_assert(PAD_ % 8 == 0 && PADT_ % 4 == 0, "LDS rows must keep 16 / 8-byte alignment");
-  static_assert((BK * (BM / 8)) % NTHR == 0, "bad transposed-A tile config");
+  static_assert((BK * (BM / 8)) % NTHR == 0 && (BK * (BN / 8)) % NTHR == 0,
+                "bad transposed tile config");
 };
 
 __device__ __forceinline__ uint4 ld16(const __bf16 *p) { return *(const uint4 *)p; }
@@ -188,21 +197,25 @@ __device__ __forceinline__ void mma_stage(const __bf16 *As, const __bf16 *Bs, in
 // and M columns 4 (p % 4) .. + 3 of a 4 x 16 block, and lane i gets that
 // block's column i: 4 consecutive K values of M row i (tr_row / tr_col place
 // each 16-lane group on the rows and K values its MFMA operand needs).
-template <class C>
+// COLS = BM for the A operand, BN for a B operand stored N-contiguous (its
+// fragments are read the same way, the MFMA B layout mirroring A's).
+template <class C, int COLS>
 struct LoaderT {
-  const __bf16 *ptr[C::AT_PIECES];  // K row start, already offset to this thread's M piece
-  int64_t ld;                       // elements between K rows
-  uint4 v[C::AT_PIECES];
+  static constexpr int NP = C::BK * (COLS / 8) / C::NTHR;
+  static constexpr int PITCH = COLS + (C::PITCH_T - C::BM);
+  const __bf16 *ptr[NP];  // piece i's K row start, offset to its columns
+  int64_t ld;             // elements between K rows
+  uint4 v[NP];
+  // the K row and first column of piece i of thread tid within a step
+  __device__ static __forceinline__ int krow(int tid, int i) { return (tid + i * C::NTHR) / (COLS / 8); }
+  __device__ static __forceinline__ int col(int tid, int i) { return 8 * ((tid + i * C::NTHR) % (COLS / 8)); }
   __device__ __forceinline__ void fetch(int k0) {
 #pragma unroll
-    for (int i = 0; i < C::AT_PIECES; ++i) v[i] = ld16(ptr[i] + (int64_t)k0 * ld);
+    for (int i = 0; i < NP; ++i) v[i] = ld16(ptr[i] + (int64_t)k0 * ld);
   }
   __device__ __forceinline__ void stash(__bf16 *stage, int tid) const {
 #pragma unroll
-    for (int i = 0; i < C::AT_PIECES; ++i) {
-      const int id = tid + i * C::NTHR;
-      *(uint4 *)(stage + (id / (C::BM / 8)) * C::PITCH_T + 8 * (id % (C::BM / 8))) = v[i];
-    }
+    for (int i = 0; i < NP; ++i) *(uint4 *)(stage + krow(tid, i) * PITCH + col(tid, i)) = v[i];
   }
 };
 
@@ -210,7 +223,18 @@ __device__ __forceinline__ v4i16 ds_read_tr16(const __bf16 *p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)p);
 }
 
-template <class C>
+// One MFMA operand fragment (8 K values of one row) from a K-major LDS tile
+// of row pitch `pitch`, via two transposing reads.
+template <class M>
+__device__ __forceinline__ bf16x8 frag_t(const __bf16 *tile, int pitch, int u, int col0, int trr,
+                                         int trc) {
+  const __bf16 *base = tile + (M::K * u + trr) * pitch + col0 + trc;
+  const v4i16 lo = ds_read_tr16(base), hi = ds_read_tr16(base + 4 * pitch);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// TB = false: B tile row-major [BN][BK] (K-contiguous); true: K-major like A.
+template <class C, bool TB>
 __device__ __forceinline__ void mma_stage_t(const __bf16 *At, const __bf16 *Bs, int arow0,
                                             const int (&brow)[C::NJ], int lane,
                                             typename C::acc_t (&acc)[C::MI][C::NJ]) {
@@ -222,13 +246,10 @@ __device__ __forceinline__ void mma_stage_t(const __bf16 *At, const __bf16 *Bs, 
     bf16x8 a[C::MI], b[C::NJ];
 #pragma unroll
     for (int j = 0; j < C::NJ; ++j)
-      b[j] = *(const bf16x8 *)(Bs + (brow[j] + r) * C::PITCH + M::K * u + kq);
+      b[j] = TB ? frag_t<M>(Bs, C::PITCH_TB, u, brow[j], trr, trc)
+                : *(const bf16x8 *)(Bs + (brow[j] + r) * C::PITCH + M::K * u + kq);
 #pragma unroll
-    for (int i = 0; i < C::MI; ++i) {
-      const __bf16 *base = At + (M::K * u + trr) * C::PITCH_T + arow0 + C::FM * i + trc;
-      const v4i16 lo = ds_read_tr16(base), hi = ds_read_tr16(base + 4 * C::PITCH_T);
-      a[i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    }
+    for (int i = 0; i < C::MI; ++i) a[i] = frag_t<M>(At, C::PITCH_T, u, arow0 + C::FM * i, trr, trc);
 #pragma unroll
     for (int i = 0; i < C::MI; ++i)
 #pragma unroll
@@ -267,8 +288,9 @@ __device__ __forceinline__ void kloop(__bf16 *smem, Loader<C, C::A_PIECES> &la,
 }
 
 template <class C>
-__device__ __forceinline__ void kloop_t(__bf16 *smem, LoaderT<C> &la, Loader<C, C::B_PIECES> &lb,
-                                        int nk, int tid, int arow0, const int (&brow)[C::NJ],
+__device__ __forceinline__ void kloop_t(__bf16 *smem, LoaderT<C, C::BM> &la,
+                                        Loader<C, C::B_PIECES> &lb, int nk, int tid, int arow0,
+                                        const int (&brow)[C::NJ],
                                         typename C::acc_t (&acc)[C::MI][C::NJ]) {
   __bf16 *const Bbase = smem + 2 * C::AT_STAGE;
   const int lane = tid & 63, r0 = tid / C::KP, q = tid % C::KP;
@@ -283,10 +305,40 @@ __device__ __forceinline__ void kloop_t(__bf16 *smem, LoaderT<C> &la, Loader<C, 
       la.fetch((s + 1) * C::BK);
       lb.fetch((s + 1) * C::BK, q);
     }
-    mma_stage_t<C>(smem + cur * C::AT_STAGE, Bbase + cur * C::B_STAGE, arow0, brow, lane, acc);
+    mma_stage_t<C, false>(smem + cur * C::AT_STAGE, Bbase + cur * C::B_STAGE, arow0, brow, lane,
+                          acc);
     if (s + 1 < nk) {
       la.stash(smem + (cur ^ 1) * C::AT_STAGE, tid);
       lb.stash(Bbase + (cur ^ 1) * C::B_STAGE, r0, q);
+    }
+    __syncthreads();
+  }
+}
+
+// Both operands K-major in memory (the Gram product of Zt with itself).
+template <class C>
+__device__ __forceinline__ void kloop_tt(__bf16 *smem, LoaderT<C, C::BM> &la,
+                                         LoaderT<C, C::BN> &lb, int nk, int tid, int arow0,
+                                         const int (&brow)[C::NJ],
+                                         typename C::acc_t (&acc)[C::MI][C::NJ]) {
+  __bf16 *const Bbase = smem + 2 * C::AT_STAGE;
+  const int lane = tid & 63;
+  la.fetch(0);
+  lb.fetch(0);
+  la.stash(smem, tid);
+  lb.stash(Bbase, tid);
+  __syncthreads();
+  for (int s = 0; s < nk; ++s) {
+    const int cur = s & 1;
+    if (s + 1 < nk) {
+      la.fetch((s + 1) * C::BK);
+      lb.fetch((s + 1) * C::BK);
+    }
+    mma_stage_t<C, true>(smem + cur * C::AT_STAGE, Bbase + cur * C::BT_STAGE, arow0, brow, lane,
+                         acc);
+    if (s + 1 < nk) {
+      la.stash(smem + (cur ^ 1) * C::AT_STAGE, tid);
+      lb.stash(Bbase + (cur ^ 1) * C::BT_STAGE, tid);
     }
     __syncthreads();
   }
@@ -440,41 +492,49 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
 }
 
 // ---------------------------------------------------------------------------
-// O rows of chunks [j0, j0 + nj) of every sequence: O_j = Z_j S_j (S_j stored
-// output-major, d rows of d_ff).
+// O rows of chunk groups [q0, q0 + nq) of every sequence (G = 1: one chunk per
+// group): O = Z S_q over the group's rows (S_q stored output-major, d rows of
+// d_ff), plus, when pt is given, the updates of the group's earlier chunks as
+// P (eta V), P^T read from the Gram buffer. The MSE rule (G = 1) also writes
+// Rt = eta (V - O)^T.
 template <class C>
 __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC))) void k_apply(
-    Slab s, int j0, int nj, const __bf16 *__restrict__ zt, const __bf16 *__restrict__ snap,
-    int64_t snap_seq_stride, int64_t snap_chunk_stride, float *__restrict__ o,
-    const __bf16 *__restrict__ vt, __bf16 *__restrict__ rt) {
+    Slab s, int q0, int nq, const __bf16 *__restrict__ zt, const __bf16 *__restrict__ snap,
+    int64_t snap_seq_stride, int64_t snap_group_stride, const __bf16 *__restrict__ pt,
+    int64_t pt_seq_stride, float *__restrict__ o, const __bf16 *__restrict__ vt,
+    __bf16 *__restrict__ rt) {
   static_assert(C::SMEM_T_ELEMS * 2 <= 160 * 1024, "LDS overflow");
+  static_assert(kChunkAlign % C::BK == 0, "chunk starts must be whole K steps");
   __shared__ __bf16 smem[C::SMEM_T_ELEMS];
   using M = typename C::M;
-  const int nm = (s.Bp + C::BM - 1) / C::BM, nn = (s.d + C::BN - 1) / C::BN;
-  const int per_chunk = nm * nn;
+  using LA = LoaderT<C, C::BM>;
+  const int RG = s.G * s.Bp;  // rows of a full group
+  const int nm = (RG + C::BM - 1) / C::BM, nn = (s.d + C::BN - 1) / C::BN;
+  const int per_group = nm * nn;
   const int id = xcd_remap(blockIdx.x, gridDim.x);
-  const int bz = id / per_chunk;
-  const int n_seq = bz / nj, jl = bz % nj, j = j0 + jl;
+  const int bz = id / per_group;
+  const int n_seq = bz / nq, ql = bz % nq, q = q0 + ql;
   int tm, tn;
-  tile_of<C::GM>(id % per_chunk, nm, nn, tm, tn);
+  tile_of<C::GM>(id % per_group, nm, nn, tm, tn);
   const int m0 = tm * C::BM, n0 = tn * C::BN;
+  const int j_first = q * s.G;                    // the group's first chunk in the slab
+  const int R = min(s.G, s.nc - j_first) * s.Bp;  // its rows (the slab's last group may be short)
+  if (m0 >= R) return;
+  const int64_t row0 = (int64_t)j_first * s.Bp;  // its first slab row
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WN, wn = wave % C::WN;
-  // A = Z_j read from Zt (token-contiguous rows of d_ff): K row f, M columns
-  // = the chunk's slab rows j Bp + m. Columns past the slab's rows (a chunk
-  // shorter than the tile) are clamped in bounds; their outputs are dropped.
-  LoaderT<C> la;
+  const int r0 = tid / C::KP;
+  // A = Z read from Zt (token-contiguous rows of d_ff): K row f, M columns =
+  // the group's slab rows. Columns past the workspace rows are clamped in
+  // bounds; the rows they feed are past the group and are dropped.
+  LA la;
   Loader<C, C::B_PIECES> lb;
   const __bf16 *zts = zt + (int64_t)n_seq * s.F * s.Lp;
-  const __bf16 *ss = snap + n_seq * snap_seq_stride + jl * snap_chunk_stride;
+  const __bf16 *ss = snap + n_seq * snap_seq_stride + ql * snap_group_stride;
   la.ld = s.Lp;
 #pragma unroll
-  for (int i = 0; i < C::AT_PIECES; ++i) {
-    const int id2 = tid + i * C::NTHR;
-    const int64_t col = min((int64_t)j * s.Bp + m0 + 8 * (id2 % (C::BM / 8)), s.Lp - 8);
-    la.ptr[i] = zts + (int64_t)(id2 / (C::BM / 8)) * s.Lp + col;
-  }
-  const int r0 = tid / C::KP;
+  for (int i = 0; i < LA::NP; ++i)
+    la.ptr[i] = zts + (int64_t)LA::krow(tid, i) * s.Lp + min(row0 + m0 + LA::col(tid, i), s.Lp - 8);
 #pragma unroll
   for (int i = 0; i < C::B_PIECES; ++i) {
     const int n = n0 + r0 + C::RPP * i;
@@ -487,7 +547,27 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
   zero_acc<C>(acc);
   kloop_t<C>(smem, la, lb, s.F / C::BK, tid, wm * C::WTM, brow, acc);
 
-  const int64_t chunk_tok0 = s.tok0 + (int64_t)j * s.B;
+  const __bf16 *vts = vt + (int64_t)n_seq * s.d * s.Lp;
+  if (pt) {
+    // rows of the tile see the group's tokens before their own chunk; the
+    // tile's last chunk starts at cs_last, so K runs over group rows
+    // [0, cs_last) and P is zero where a row's chunk is not yet complete.
+    const int cs_last = (min(m0 + C::BM, R) - 1) / s.Bp * s.Bp;
+    if (cs_last > 0) {
+      const __bf16 *pts = pt + n_seq * pt_seq_stride + (int64_t)q * RG * RG;
+      la.ld = RG;
+#pragma unroll
+      for (int i = 0; i < LA::NP; ++i)
+        la.ptr[i] = pts + (int64_t)LA::krow(tid, i) * RG + min(m0 + LA::col(tid, i), RG - 8);
+#pragma unroll
+      for (int i = 0; i < C::B_PIECES; ++i) {
+        const int n = n0 + r0 + C::RPP * i;
+        lb.ptr[i] = vts + (int64_t)(n < s.d ? n : 0) * s.Lp + row0;
+      }
+      kloop_t<C>(smem, la, lb, cs_last / C::BK, tid, wm * C::WTM, brow, acc);
+    }
+  }
+
   float *os = o ? o + n_seq * s.x_seq_stride : nullptr;  // nullptr: residual only
 #pragma unroll
   for (int i = 0; i < C::MI; ++i)
@@ -497,21 +577,20 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
       for (int g = 0; g < M::NG; ++g) {
         const int m = m0 + wm * C::WTM + C::FM * i + M::rrow(lane, g);
         const int n = n0 + wn * C::WTN + C::FM * jj + M::rcol(lane);
-        if (n >= s.d || m >= s.Bp) continue;
+        if (n >= s.d || m >= R) continue;
+        // rows m .. m + 3 share one chunk (Bp is a multiple of 4)
+        const int ic = m % s.Bp;
+        const int64_t t0 = s.tok0 + (int64_t)(j_first + m / s.Bp) * s.B + ic;
         const f32x4 a4 = get4(acc[i][jj], g);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int64_t t = chunk_tok0 + m + r;
-          if (os && m + r < s.B && t < s.L) os[t * s.d + n] = a4[r];
-        }
+        for (int r = 0; r < 4; ++r)
+          if (os && ic + r < s.B && t0 + r < s.L) os[(t0 + r) * s.d + n] = a4[r];
         if (rt) {
-          const bf16x4 v = *(const bf16x4 *)(vt + (int64_t)n_seq * s.d * s.Lp + (int64_t)n * s.Lp +
-                                             (int64_t)j * s.Bp + m);
+          const bf16x4 v = *(const bf16x4 *)(vts + (int64_t)n * s.Lp + row0 + m);
           bf16x4 rv;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int64_t t = chunk_tok0 + m + r;
-            const bool valid = m + r < s.B && t < s.L;
+            const bool valid = ic + r < s.B && t0 + r < s.L;
             rv[r] = (__bf16)(valid ? s.eta * ((float)v[r] - a4[r]) : 0.f);
           }
           *(bf16x4 *)(rt + (int64_t)n_seq * s.d * s.Bp + (int64_t)n * s.Bp + m) = rv;
@@ -520,17 +599,86 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
 }
 
 // ---------------------------------------------------------------------------
+// Block-causal Gram of chunk groups [0, ng) of the slab: P^T[s][m] = z_m . z_s
+// (a sum over d_ff) when group row s lies in an earlier chunk than group row
+// m, else 0. A = Zt columns m, B = Zt columns s, both K-major (rows of d_ff)
+// in memory and read through transposing LDS reads. Only the tiles the apply
+// reads are computed: s below the first row of the m tile's last chunk.
+template <class C>
+__global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC))) void k_gram(
+    Slab s, int ng, const __bf16 *__restrict__ zt, __bf16 *__restrict__ pt,
+    int64_t pt_seq_stride) {
+  static_assert(C::SMEM_TT_ELEMS * 2 <= 160 * 1024, "LDS overflow");
+  __shared__ __bf16 smem[C::SMEM_TT_ELEMS];
+  using M = typename C::M;
+  using LA = LoaderT<C, C::BM>;
+  using LB = LoaderT<C, C::BN>;
+  const int RG = s.G * s.Bp;
+  const int nm = (RG + C::BM - 1) / C::BM, nn = (RG + C::BN - 1) / C::BN;
+  const int per_group = nm * nn;
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  const int bz = id / per_group;
+  const int n_seq = bz / ng, q = bz % ng;
+  const int tm = (id % per_group) / nn, tn = (id % per_group) % nn;
+  const int m0 = tm * C::BM, s0 = tn * C::BN;
+  const int j_first = q * s.G;
+  const int R = min(s.G, s.nc - j_first) * s.Bp;
+  if (m0 >= R) return;
+  const int cs_last = (min(m0 + C::BM, R) - 1) / s.Bp * s.Bp;
+  if (s0 >= cs_last) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int64_t row0 = (int64_t)j_first * s.Bp;
+  const __bf16 *zts = zt + (int64_t)n_seq * s.F * s.Lp;
+  LA la;
+  LB lb;
+  la.ld = lb.ld = s.Lp;
+#pragma unroll
+  for (int i = 0; i < LA::NP; ++i)
+    la.ptr[i] = zts + (int64_t)LA::krow(tid, i) * s.Lp + min(row0 + m0 + LA::col(tid, i), s.Lp - 8);
+#pragma unroll
+  for (int i = 0; i < LB::NP; ++i)
+    lb.ptr[i] = zts + (int64_t)LB::krow(tid, i) * s.Lp + min(row0 + s0 + LB::col(tid, i), s.Lp - 8);
+  int brow[C::NJ];
+#pragma unroll
+  for (int jj = 0; jj < C::NJ; ++jj) brow[jj] = wn * C::WTN + C::FM * jj;
+  typename C::acc_t acc[C::MI][C::NJ];
+  zero_acc<C>(acc);
+  kloop_tt<C>(smem, la, lb, s.F / C::BK, tid, wm * C::WTM, brow, acc);
+
+  __bf16 *pts = pt + n_seq * pt_seq_stride + (int64_t)q * RG * RG;
+#pragma unroll
+  for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+    for (int jj = 0; jj < C::NJ; ++jj)
+#pragma unroll
+      for (int g = 0; g < M::NG; ++g) {
+        const int m = m0 + wm * C::WTM + C::FM * i + M::rrow(lane, g);
+        const int sc = s0 + wn * C::WTN + C::FM * jj + M::rcol(lane);
+        if (m < RG && sc < RG) {
+          const f32x4 a4 = get4(acc[i][jj], g);
+          const bool earlier = sc / s.Bp < m / s.Bp;  // rows m .. m + 3 share a chunk
+          bf16x4 v;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = (__bf16)(earlier ? a4[r] : 0.f);
+          *(bf16x4 *)(pts + (int64_t)sc * RG + m) = v;
+        }
+      }
+}
+
+// ---------------------------------------------------------------------------
 // W^T tile update: rows f (d_ff), columns c (d), K = tokens. The fp32 tile
-// lives in the accumulators for chunks [j_first, j_first + n_chunks).
+// lives in the accumulators for chunks [j_first, j_first + n_chunks), taken G
+// at a time (one K loop per group of G chunks, whose rows are contiguous).
 // A operand = Zt (rows f, token-contiguous); B operand = Vt or Rt (rows c).
-// snap_each_chunk: write S[j] = bf16(W) before chunk j's accumulation;
+// snap_each_group: write S[g] = bf16(W) before group g's accumulation;
 // snap_after: write S = bf16(W) after the last chunk.
 template <class C>
 __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC))) void k_update(
-    Slab s, int j_first, int n_chunks, const __bf16 *__restrict__ zt,
+    Slab s, int j_first, int n_chunks, int G, const __bf16 *__restrict__ zt,
     const __bf16 *__restrict__ bsrc, int64_t b_ld, int64_t b_seq_stride, int64_t b_chunk_stride,
     float *__restrict__ w, __bf16 *__restrict__ snap, int64_t snap_seq_stride,
-    int64_t snap_chunk_stride, int snap_each_chunk, int snap_after) {
+    int64_t snap_group_stride, int snap_each_group, int snap_after) {
   static_assert(C::SMEM_ELEMS * 2 <= 160 * 1024, "LDS overflow");
   __shared__ __bf16 smem[C::SMEM_ELEMS];
   using M = typename C::M;
@@ -588,9 +736,11 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
   const int steps = s.Bp / C::BK;
   const __bf16 *zts = zt + (int64_t)n_seq * s.F * s.Lp;
   const __bf16 *bs = bsrc + n_seq * b_seq_stride;
-  for (int jc = 0; jc < n_chunks; ++jc) {
+  for (int jc = 0; jc < n_chunks; jc += G) {
     const int j = j_first + jc;
-    if (snap_each_chunk) write_snap(snap + n_seq * snap_seq_stride + jc * snap_chunk_stride);
+    const int nch = min(G, n_chunks - jc);
+    if (snap_each_group)
+      write_snap(snap + n_seq * snap_seq_stride + (int64_t)(jc / G) * snap_group_stride);
 #pragma unroll
     for (int i = 0; i < C::A_PIECES; ++i) {
       const int f = f0 + r0 + C::RPP * i;
@@ -601,7 +751,7 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
       const int c = c0 + r0 + C::RPP * i;
       lb.ptr[i] = bs + (int64_t)(c < s.d ? c : 0) * b_ld + jc * b_chunk_stride;
     }
-    kloop<C>(smem, la, lb, steps, tid, wm * C::WTM, brow, acc);
+    kloop<C>(smem, la, lb, nch * steps, tid, wm * C::WTM, brow, acc);
   }
   if (snap_after) write_snap(snap + n_seq * snap_seq_stride);
 #pragma unroll
@@ -690,18 +840,32 @@ hipError_t launch_proj(const Slab &s, const Weights &w, const WsPtrs &ws, hipStr
   return hipGetLastError();
 }
 
+// Groups of the slab: ceil(nc / G).
+inline int slab_groups(const Slab &s) { return (s.nc + s.G - 1) / s.G; }
+
 template <class C>
-hipError_t launch_apply(const Slab &s, int j0, int nj, const WsPtrs &ws, float *o,
+hipError_t launch_apply(const Slab &s, int q0, int nq, const WsPtrs &ws, float *o,
                         hipStream_t st) {
   const int64_t dF = (int64_t)s.d * s.F;
-  const int64_t snap_seq = s.mse ? dF : (int64_t)s.nc_cap * dF;
-  const int64_t snap_chunk = s.mse ? 0 : dF;
-  const __bf16 *snap = (const __bf16 *)ws.s + (s.mse ? 0 : (int64_t)j0 * dF);
-  const int64_t nb =
-      ((s.Bp + C::BM - 1) / C::BM) * ((s.d + C::BN - 1) / C::BN) * (int64_t)nj * s.n_seq;
-  hipLaunchKernelGGL(k_apply<C>, dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, j0, nj,
-                     (const __bf16 *)ws.zt, snap, snap_seq, snap_chunk, o, (const __bf16 *)ws.vt,
-                     s.mse ? (__bf16 *)ws.rt : nullptr);
+  const int64_t RG = (int64_t)s.G * s.Bp;
+  const int64_t snap_seq = s.mse ? dF : (int64_t)s.ng_cap * dF;
+  const int64_t snap_group = s.mse ? 0 : dF;
+  const __bf16 *snap = (const __bf16 *)ws.s + (s.mse ? 0 : (int64_t)q0 * dF);
+  const int64_t nb = ((RG + C::BM - 1) / C::BM) * ((s.d + C::BN - 1) / C::BN) * nq * s.n_seq;
+  hipLaunchKernelGGL(k_apply<C>, dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, q0, nq,
+                     (const __bf16 *)ws.zt, snap, snap_seq, snap_group,
+                     s.G > 1 ? (const __bf16 *)ws.p : nullptr, (int64_t)s.ng_cap * RG * RG, o,
+                     (const __bf16 *)ws.vt, s.mse ? (__bf16 *)ws.rt : nullptr);
+  return hipGetLastError();
+}
+
+template <class C>
+hipError_t launch_gram(const Slab &s, const WsPtrs &ws, hipStream_t st) {
+  const int64_t RG = (int64_t)s.G * s.Bp;
+  const int ng = slab_groups(s);
+  const int64_t nb = ((RG + C::BM - 1) / C::BM) * ((RG + C::BN - 1) / C::BN) * ng * s.n_seq;
+  hipLaunchKernelGGL(k_gram<C>, dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, ng,
+                     (const __bf16 *)ws.zt, (__bf16 *)ws.p, (int64_t)s.ng_cap * RG * RG);
   return hipGetLastError();
 }
 
@@ -710,9 +874,9 @@ hipError_t launch_update_scan(const Slab &s, const WsPtrs &ws, float *w_state, h
   const int64_t dF = (int64_t)s.d * s.F;
   const int64_t nb = ((s.F + C::BM - 1) / C::BM) * ((s.d + C::BN - 1) / C::BN) * s.n_seq;
   // B operand: Vt rows c; chunk jc starts jc * Bp tokens along the row
-  hipLaunchKernelGGL(k_update<C>, dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, 0, s.nc,
+  hipLaunchKernelGGL(k_update<C>, dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, 0, s.nc, s.G,
                      (const __bf16 *)ws.zt, (const __bf16 *)ws.vt, s.Lp, (int64_t)s.d * s.Lp,
-                     (int64_t)s.Bp, w_state, (__bf16 *)ws.s, (int64_t)s.nc_cap * dF, dF, 1, 0);
+                     (int64_t)s.Bp, w_state, (__bf16 *)ws.s, (int64_t)s.ng_cap * dF, dF, 1, 0);
   return hipGetLastError();
 }
 
@@ -722,7 +886,7 @@ hipError_t launch_update_one(const Slab &s, int j, const WsPtrs &ws, float *w_st
   const int64_t dF = (int64_t)s.d * s.F;
   const int64_t nb = ((s.F + C::BM - 1) / C::BM) * ((s.d + C::BN - 1) / C::BN) * s.n_seq;
   // B operand: Rt [n][d][Bp] of chunk j
-  hipLaunchKernelGGL(k_update<C>, dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, j, 1,
+  hipLaunchKernelGGL(k_update<C>, dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, j, 1, 1,
                      (const __bf16 *)ws.zt, (const __bf16 *)ws.rt, (int64_t)s.Bp,
                      (int64_t)s.d * s.Bp, (int64_t)0, w_state, (__bf16 *)ws.s, dF, (int64_t)0, 0,
                      1);
@@ -746,7 +910,12 @@ using ProjCfg = Cfg<2, 4, 32, 16, 16, 8>;
 using ApplyCfg = Cfg<2, 4, 64, 16, 16, 8>;
 using ApplySmallCfg = Cfg<1, 2, 64, 16, 16, 8>;  // when ApplyCfg would leave most CUs idle
 using UpdateCfg = Cfg<1, 2, 64, 16, 16, 8, 1, 16>;
+using GramCfg = Cfg<2, 4, 64, 16, 16, 8>;
 static_assert(kChunkAlign % UpdateCfg::BK == 0, "chunk pitch must be whole update K steps");
+// The Gram computes, per m tile, the columns the apply's m tiles read: its m
+// tiles must be unions of whole apply m tiles.
+static_assert(GramCfg::BM % ApplyCfg::BM == 0 && GramCfg::BM % ApplySmallCfg::BM == 0,
+              "Gram and apply row tiles must nest");
 
 }  // namespace mfma
 
@@ -773,12 +942,15 @@ hipError_t mf_gateup(const Slab &s, const __bf16 *x, const Weights &w, const WsP
 hipError_t mf_proj(const Slab &s, const Weights &w, const WsPtrs &ws, hipStream_t st) {
   return mfma::launch_proj<mfma::ProjCfg>(s, w, ws, st);
 }
-hipError_t mf_apply(const Slab &s, int j0, int nj, const WsPtrs &ws, float *o, hipStream_t st) {
+hipError_t mf_apply(const Slab &s, int q0, int nq, const WsPtrs &ws, float *o, hipStream_t st) {
   using C = mfma::ApplyCfg;
-  const int64_t big_blocks =
-      ((s.Bp + C::BM - 1) / C::BM) * ((s.d + C::BN - 1) / C::BN) * (int64_t)nj * s.n_seq;
-  if (big_blocks < 512) return mfma::launch_apply<mfma::ApplySmallCfg>(s, j0, nj, ws, o, st);
-  return mfma::launch_apply<C>(s, j0, nj, ws, o, st);
+  const int64_t big_blocks = (((int64_t)s.G * s.Bp + C::BM - 1) / C::BM) *
+                             ((s.d + C::BN - 1) / C::BN) * (int64_t)nq * s.n_seq;
+  if (big_blocks < 512) return mfma::launch_apply<mfma::ApplySmallCfg>(s, q0, nq, ws, o, st);
+  return mfma::launch_apply<C>(s, q0, nq, ws, o, st);
+}
+hipError_t mf_gram(const Slab &s, const WsPtrs &ws, hipStream_t st) {
+  return mfma::launch_gram<mfma::GramCfg>(s, ws, st);
 }
 hipError_t mf_update_scan(const Slab &s, const WsPtrs &ws, float *w_state, hipStream_t st) {
   return mfma::launch_update_scan<mfma::UpdateCfg>(s, ws, w_state, st);

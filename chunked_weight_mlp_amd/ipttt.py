@@ -34,7 +34,7 @@ EXPORTS = (
     "ipttt_status_str", "ipttt_last_error",
 )
 
-KERNELS = ("gateup", "conv", "proj", "update", "apply", "snapshot")  # ipttt_kernel order
+KERNELS = ("gateup", "conv", "proj", "update", "apply", "snapshot", "gram")  # ipttt_kernel order
 
 
 class LayerDesc(ctypes.Structure):
@@ -48,6 +48,7 @@ class LayerDesc(ctypes.Structure):
         ("update", ctypes.c_int),
         ("in_dtype", ctypes.c_int),
         ("flags", ctypes.c_uint32),
+        ("group_chunks", ctypes.c_int32),
         ("w_gate", ctypes.c_void_p),
         ("w_up", ctypes.c_void_p),
         ("proj", ctypes.c_void_p),
@@ -197,7 +198,7 @@ class Layer:
     def __init__(self, *, w_gate, w_up, proj, conv_w, w0, chunk: int, eta: float,
                  update: str = "linear", max_batch: int = 1, workspace_bytes: int | None = None,
                  slab_chunks: int | None = None, max_seq_len: int | None = None,
-                 flags: int = 0):
+                 flags: int = 0, group_chunks: int = 0):
         d_ff, d = w_gate.shape
         dtype = w_gate.dtype
         if dtype not in _DT:
@@ -207,7 +208,7 @@ class Layer:
         self.w_state = torch.empty((max_batch, d, d_ff), dtype=torch.float32, device=dev)
         desc = LayerDesc(d=d, d_ff=d_ff, conv_k=conv_w.shape[1], chunk=chunk, max_batch=max_batch,
                          eta=eta, update=IPTTT_UPDATE_MSE if update == "mse" else IPTTT_UPDATE_LINEAR,
-                         in_dtype=_DT[dtype], flags=flags)
+                         in_dtype=_DT[dtype], flags=flags, group_chunks=group_chunks)
         if workspace_bytes is None:
             if slab_chunks is None:
                 slab_chunks = 1 if max_seq_len is None else -(-max_seq_len // chunk)

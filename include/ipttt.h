@@ -82,6 +82,18 @@ typedef enum { IPTTT_UPDATE_LINEAR = 0, IPTTT_UPDATE_MSE = 1 } ipttt_update;
  * order); fp32 layers always use them. */
 #define IPTTT_FLAG_GENERIC_KERNELS 1u
 
+/* Chunk-parallel linear scan (bf16 MFMA path, linear rule). The linear update
+ * is associative, a plain sum of per-chunk terms (explainer page §2.3), so a
+ * group of G consecutive chunks can share one copy of W: with W_q the fast
+ * weight at the group's first chunk,
+ *   O_t = z_t W_q + sum over earlier-chunk tokens s of the group of
+ *         (z_t . z_s) eta v_s,
+ * which is O_k = Z_k W_k for every chunk k of the group. The scan then keeps
+ * one bf16 copy of W per group instead of per chunk, and the apply adds the
+ * block-causal Gram term. group_chunks sets G (1 gives the plain chunk scan;
+ * G * round_up(chunk, 64) must not exceed 4096); 0 lets the library choose,
+ * about 1024 chunk-padded rows per group. Results agree with the plain scan
+ * up to bf16 rounding. Other paths ignore the field. */
 typedef struct {
   int32_t d;           /* model width (columns of X, E, O)                       */
   int32_t d_ff;        /* MLP width F (rows of the fast weight's input side)     */
@@ -92,6 +104,8 @@ typedef struct {
   ipttt_update update; /* linear or MSE rule                                     */
   ipttt_dtype in_dtype;/* dtype of x, e, w_gate, w_up, proj, conv_w              */
   uint32_t flags;      /* IPTTT_FLAG_*                                           */
+  int32_t group_chunks;/* chunks per group of the chunk-parallel linear scan, see
+                          below; 0 = library choice, 1 = plain chunk scan       */
   const void *w_gate;  /* [d_ff][d]                                              */
   const void *w_up;    /* [d_ff][d]                                              */
   const void *proj;    /* [d][d]                                                 */
@@ -167,7 +181,8 @@ typedef enum {
   IPTTT_K_UPDATE = 3,   /* W += eta Z^T V (scan) or the MSE update   */
   IPTTT_K_APPLY = 4,    /* O = Z W_k                                 */
   IPTTT_K_SNAPSHOT = 5, /* bf16 / fp32 copy of W read by the apply   */
-  IPTTT_K_COUNT = 6
+  IPTTT_K_GRAM = 6,     /* block-causal Z Z^T of a chunk group       */
+  IPTTT_K_COUNT = 7
 } ipttt_kernel;
 
 ipttt_status ipttt_profile_begin(ipttt_layer *h);

@@ -114,6 +114,29 @@ def test_workspace_bytes(lib):
     assert B.ipttt_workspace_bytes(mse, 1, 4) > 0
 
 
+def test_workspace_bytes_of_chunk_groups(lib):
+    """Groups of G chunks share one W snapshot and add a (G Bp)^2 Gram buffer."""
+    mem = FakeMem()
+    d, F, Bc = 64, 256, 64
+    el = 2
+    snap = d * F * el
+    plain = B.ipttt_workspace_bytes(make_desc(mem, chunk=Bc, group_chunks=1), 1, 8)
+    grouped = B.ipttt_workspace_bytes(make_desc(mem, chunk=Bc, group_chunks=4), 1, 8)
+    # 8 snapshots -> 2, plus 2 groups of (4 * 64)^2 Gram entries
+    assert grouped - plain == -6 * snap + 2 * (4 * Bc) ** 2 * el
+    # a slab shorter than a group uses groups of the slab's length
+    one = B.ipttt_workspace_bytes(make_desc(mem, chunk=Bc, group_chunks=4), 1, 1)
+    assert one == B.ipttt_workspace_bytes(make_desc(mem, chunk=Bc, group_chunks=1), 1, 1)
+    # default: about 1024 padded rows per group (16 chunks of 64)
+    auto = B.ipttt_workspace_bytes(make_desc(mem, chunk=Bc, group_chunks=0), 1, 32)
+    g16 = B.ipttt_workspace_bytes(make_desc(mem, chunk=Bc, group_chunks=16), 1, 32)
+    assert auto == g16
+    # the rule, the generic kernels and fp32 layers keep one snapshot per chunk
+    for kw in (dict(update=1), dict(flags=B.IPTTT_FLAG_GENERIC_KERNELS), dict(in_dtype=0)):
+        assert (B.ipttt_workspace_bytes(make_desc(mem, chunk=Bc, group_chunks=4, **kw), 1, 8) ==
+                B.ipttt_workspace_bytes(make_desc(mem, chunk=Bc, group_chunks=1, **kw), 1, 8))
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(d=0), B.IPTTT_E_INVALID),
     (dict(d_ff=-3), B.IPTTT_E_INVALID),
@@ -126,6 +149,8 @@ def test_workspace_bytes(lib):
     (dict(flags=0x80), B.IPTTT_E_INVALID),
     (dict(eta=float("nan")), B.IPTTT_E_INVALID),
     (dict(eta=float("inf")), B.IPTTT_E_INVALID),
+    (dict(group_chunks=-1), B.IPTTT_E_INVALID),
+    (dict(group_chunks=33), B.IPTTT_E_UNSUPPORTED),   # 33 x 128 padded rows > 4096
 ])
 def test_init_rejects_bad_sizes(lib, kw, status):
     mem = FakeMem()

@@ -3,8 +3,9 @@ benchmark times (the whole sequence in one pass of the update scan).
 
 The oracle cannot scan 128k tokens of a 4B-shaped layer in seconds, so it
 checks what it can compute one by one:
-  - O on the first two chunks (the oracle scans just those chunks; the HIP
-    path's later chunks cannot change them, by causality);
+  - O on the first chunks, two or, at small chunk sizes, one chunk group
+    and two more (the oracle scans just those chunks; the HIP path's later
+    chunks cannot change them, by causality);
   - sampled entries of the final fast weight (linear rule): by associativity
     W_final[f, c] = W_0[f, c] + eta sum_t Z[t, f] V[t, c] needs one column of
     Z and one of V, O(L d) each;
@@ -70,8 +71,10 @@ def test_full_size(name):
     assert torch.isfinite(o).all()
     ow = wl.to_oracle(weights)
 
-    # first two chunks of every sequence
-    t2 = 2 * w.chunk
+    # first chunks of every sequence: two, plus one default chunk group
+    # (about 1024 padded rows) for the linear rule
+    group = max(1, 1024 // (-(-w.chunk // 64) * 64)) if w.update == "linear" else 0
+    t2 = min(w.seq_len, (group + 2) * w.chunk)
     say(f"[full] {name}: oracle on the first {t2} tokens of {w.n_seq} sequence(s)")
     O2, _ = oracle.prefill(x[:, :t2].double().numpy(), e[:, :t2].double().numpy(), ow["W_g"], ow["W_u"],
                            ow["conv_w"], ow["Proj"], ow["W_0"], w.eta, w.chunk, update=w.update)
@@ -104,8 +107,9 @@ def test_full_size(name):
 
 @pytest.mark.parametrize("Bc", [64, 256, 512, 1024, 4096])
 def test_chunk_sweep_full_size(Bc):
-    """4B-shaped layer at L = 65536 and each chunk size: first chunks and sampled
-    final-weight entries against the oracle (the prefix-sum form's W_final)."""
+    """4B-shaped layer at L = 65536 and each chunk size: the first chunks (past
+    the first chunk group) and sampled final-weight entries against the oracle
+    (the prefix-sum form)."""
     w = wl.WORKLOADS[f"qwen3_4b_L64k_B{Bc}"]
     weights = wl.make_weights(w)
     x, e = wl.make_inputs(w)
@@ -113,7 +117,10 @@ def test_chunk_sweep_full_size(Bc):
     say(f"[sweep-full] B={Bc}: GPU run, {slab} chunks per pass")
     o, ws = run_full(w, weights, x, e, slab)
     ow = wl.to_oracle(weights)
-    t2 = min(w.seq_len, 2 * Bc)
+    # the default chunk group (about 1024 padded rows) plus two chunks: covers
+    # the Gram term inside the first group and the second group's snapshot
+    group = max(1, 1024 // (-(-Bc // 64) * 64))
+    t2 = min(w.seq_len, (group + 2) * Bc)
     Op, _ = oracle.prefill_prefix_form(x[:, :t2].double().numpy(), e[:, :t2].double().numpy(),
                                        ow["W_g"], ow["W_u"], ow["conv_w"], ow["Proj"], ow["W_0"],
                                        w.eta, Bc)

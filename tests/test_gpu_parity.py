@@ -40,11 +40,12 @@ def need_gpu():
 
 
 def make_layer(w: wl.Workload, weights, flags=0, max_batch=None, slab_chunks=None,
-               workspace_bytes=None):
+               workspace_bytes=None, group_chunks=0):
     dev = {k: v.to(DEV) for k, v in weights.items()}
     return B.Layer(**dev, chunk=w.chunk, eta=w.eta, update=w.update,
                    max_batch=max_batch or w.n_seq, slab_chunks=slab_chunks,
-                   max_seq_len=w.seq_len, workspace_bytes=workspace_bytes, flags=flags)
+                   max_seq_len=w.seq_len, workspace_bytes=workspace_bytes, flags=flags,
+                   group_chunks=group_chunks)
 
 
 def gpu_run(layer, x, e, reset=True):
@@ -68,13 +69,15 @@ def oracle_run(w, x, e, weights, W_start=None):
                           ow["W_0"] if W_start is None else W_start, w.eta, w.chunk, update=w.update)
 
 
-def check_against_oracle(w, flags=0, n_seq=None, seq_len=None, slab_chunks=None, seed=0):
+def check_against_oracle(w, flags=0, n_seq=None, seq_len=None, slab_chunks=None, seed=0,
+                         group_chunks=0):
     weights = wl.make_weights(w, seed_offset=seed)
     x, e = wl.make_inputs(w, seq_len=seq_len, n_seq=n_seq, seed_offset=seed)
     N, L = x.shape[0], x.shape[1]
     say(f"[parity] {w.name} N={N} L={L} B={w.chunk} d={w.d} F={w.d_ff} {w.dtype} {w.update} "
-        f"flags={flags} slab={slab_chunks}")
-    layer = make_layer(w.replace(n_seq=N, seq_len=L), weights, flags=flags, slab_chunks=slab_chunks)
+        f"flags={flags} slab={slab_chunks} group={group_chunks}")
+    layer = make_layer(w.replace(n_seq=N, seq_len=L), weights, flags=flags, slab_chunks=slab_chunks,
+                       group_chunks=group_chunks)
     o = gpu_run(layer, x, e).to("cpu", torch.float64).numpy()
     Wg = w_pages(layer, N)
     O_ref, W_ref = oracle_run(w, x, e, weights)
@@ -123,6 +126,43 @@ def test_bf16_small_shapes(flags, update, L, Bc):
 def test_bf16_multi_slab():
     """A workspace for 3 chunks forces several passes over a 9-chunk sequence."""
     check_against_oracle(BF16_SMALL.replace(chunk=64), seq_len=9 * 64 - 5, slab_chunks=3)
+
+
+@pytest.mark.parametrize("Bc,G,L,N", [
+    (64, 0, 2000, 2),     # default group (16 chunks), ragged last chunk, two groups
+    (96, 3, 1000, 1),     # 384 group rows: not a multiple of the apply's row tile
+    (128, 5, 3000, 2),    # a short last group (4 of 5 chunks)
+    (200, 2, 1500, 1),    # padding rows inside every chunk
+    (64, 64, 4096 + 37, 1),  # the largest group (4096 rows) and a one-chunk last group
+    (64, 4, 100, 1),      # fewer chunks than a group
+])
+def test_bf16_chunk_groups(Bc, G, L, N):
+    """Chunk-parallel form: one W snapshot per group of G chunks, the group's
+    earlier chunks added through the block-causal Gram product."""
+    check_against_oracle(BF16_SMALL.replace(chunk=Bc), n_seq=N, seq_len=L, group_chunks=G)
+
+
+def test_bf16_chunk_groups_multi_slab():
+    """A workspace for 7 chunks with groups of 3: slabs of 6 chunks (whole groups)."""
+    check_against_oracle(BF16_SMALL.replace(chunk=64), seq_len=20 * 64 - 9, slab_chunks=7,
+                         group_chunks=3)
+
+
+def test_chunk_groups_match_plain_scan():
+    """Grouped and plain scans differ only by rounding: O agrees to bf16 level
+    and the final weight, a sum of the same products, very closely."""
+    w = BF16_SMALL.replace(chunk=64, n_seq=1, seq_len=1500)
+    weights = wl.make_weights(w)
+    x, e = wl.make_inputs(w)
+    outs = []
+    for g in (1, 8):
+        layer = make_layer(w, weights, group_chunks=g)
+        outs.append((gpu_run(layer, x, e).double().cpu().numpy(), w_pages(layer, 1)))
+        layer.close()
+    eo = rel_fro(outs[1][0], outs[0][0])
+    ew = rel_fro(outs[1][1], outs[0][1])
+    say(f"[groups] grouped vs plain: rel O={eo:.3e} W={ew:.3e}")
+    assert eo <= 1e-2 and ew <= 1e-5
 
 
 def test_qwen3_4b_shape_two_chunks_and_tail():
@@ -190,12 +230,14 @@ def test_causality_bitwise():
         assert not torch.equal(o3[:, (k + 1) * 128:], o[:, (k + 1) * 128:])
 
 
-@pytest.mark.parametrize("update", ["linear", "mse"])
-def test_continuation_bitwise(update):
+@pytest.mark.parametrize("update,group", [("linear", 1), ("linear", 2), ("mse", 0)])
+def test_continuation_bitwise(update, group):
+    """The first call ends on a chunk boundary (and, grouped, on a group
+    boundary), so two calls run the same arithmetic as one."""
     w = BF16_SMALL.replace(n_seq=2, seq_len=5 * 128 + 50, update=update, eta=2e-3)
     weights = wl.make_weights(w)
     x, e = wl.make_inputs(w)
-    layer = make_layer(w, weights)
+    layer = make_layer(w, weights, group_chunks=group)
     o = gpu_run(layer, x, e).clone()
     wf = layer.w_state.clone()
     layer.reset()
