@@ -316,7 +316,8 @@ ipttt_status run_scan(ipttt_layer *h, const T *x, const T *e, float *o, int slot
     return ws_layout(elem, n_seq, d.d, d.d_ff, Bp, (int)n, (int)std::min<int64_t>(G_max, n), mse,
                      !h->mfma);
   };
-  int64_t lo = 1, hi = K;
+  // slab rows are indexed in 32 bits on the device
+  int64_t lo = 1, hi = std::min<int64_t>(K, ((int64_t)1 << 30) / Bp);
   if (layout(1).total > d.workspace_bytes)
     return fail(IPTTT_E_WORKSPACE, "workspace_bytes=%zu cannot hold one chunk of %d sequences (%zu)",
                 d.workspace_bytes, n_seq, layout(1).total);

@@ -1,15 +1,16 @@
 // bf16 MFMA kernels of the fast-weight prefill for gfx950 (CDNA4).
 //
-// All four dense contractions share one block structure, templated on the
-// wave grid, the K step and the MFMA shape (Cfg): WM x WN waves, each computing
-// a 128 x 64 output tile from FM x FM MFMA tiles (v_mfma_f32_32x32x16_bf16 or
-// v_mfma_f32_16x16x32_bf16), so a block covers (128 WM) x (64 WN). K is staged
-// through LDS BK at a time in two buffers; the global loads of step s+1 are in
-// flight while step s runs on MFMA. Both operands are K-contiguous in memory
-// ("NT"): a lane's MFMA operand is 8 consecutive K values (one 16-byte LDS
-// read). LDS rows are padded (PAD elements) so that the fragment reads of
-// consecutive lanes, which walk down consecutive rows, spread over the banks;
-// shapes and paddings were picked by timing on MI355X.
+// All the dense contractions share one block structure, templated on the
+// wave grid, the K step, the MFMA shape and the wave tile (Cfg): WM x WN
+// waves, each computing a 128 x WTN output tile from FM x FM MFMA tiles
+// (v_mfma_f32_32x32x16_bf16 or v_mfma_f32_16x16x32_bf16), so a block covers
+// (128 WM) x (WTN WN). K is staged through LDS BK at a time in two buffers;
+// the global loads of step s+1 are in flight while step s runs on MFMA. Both
+// operands are K-contiguous in memory ("NT"): a lane's MFMA operand is 8
+// consecutive K values (one 16-byte LDS read). LDS rows are padded (PAD
+// elements) so that the fragment reads of consecutive lanes, which walk down
+// consecutive rows, spread over the banks; shapes and paddings were picked by
+// timing on MI355X.
 //
 // Kernels:
 //   k_gateup   Z = SiLU(X W_g) * (X W_u)   M = slab rows, N = d_ff (half the
@@ -89,14 +90,14 @@ __device__ __forceinline__ void set4(f32x16 &a, int g, f32x4 v) {
 }
 
 template <int WM_, int WN_, int BK_, int FM_ = 32, int PAD_ = 16, int PADT_ = 8, int OCC_ = 1,
-          int GM_ = 8>
+          int GM_ = 8, int WTN_ = 64>
 struct Cfg {
   static constexpr int WM = WM_, WN = WN_, BK = BK_, FM = FM_;
   static constexpr int GM = GM_;  // row tiles per group in the tile order (tile_of)
   static constexpr int OCC = OCC_;  // waves per SIMD the register allocation must allow
   using M = Mfma<FM>;
   using acc_t = typename M::acc_t;
-  static constexpr int WTM = 128, WTN = 64;  // wave tile
+  static constexpr int WTM = 128, WTN = WTN_;  // wave tile
   static constexpr int MI = WTM / FM, NJ = WTN / FM;
   static constexpr int BM = WTM * WM, BN = WTN * WN;
   static constexpr int NTHR = 64 * WM * WN;
@@ -352,10 +353,11 @@ __device__ __forceinline__ void zero_acc(typename C::acc_t (&acc)[C::MI][C::NJ])
     for (int j = 0; j < C::NJ; ++j) acc[i][j] = typename C::acc_t{};
 }
 
-__device__ __forceinline__ int64_t slab_row_token(const Slab &s, int64_t p) {
-  const int64_t j = p / s.Bp, i = p % s.Bp;
+// Token of slab row p (slab rows fit in 32 bits), or -1 for a padding row.
+__device__ __forceinline__ int64_t slab_row_token(const Slab &s, int p) {
+  const int j = p / s.Bp, i = p - j * s.Bp;
   if (i >= s.B || j >= s.nc) return -1;
-  const int64_t t = s.tok0 + j * s.B + i;
+  const int64_t t = s.tok0 + (int64_t)j * s.B + i;
   return t < s.L ? t : -1;
 }
 
@@ -414,23 +416,29 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
 #pragma unroll
   for (int i = 0; i < C::MI; ++i)
 #pragma unroll
-    for (int j = 0; j < HJ; ++j)
+    for (int g = 0; g < M::NG; ++g) {
+      // rows p .. p + 3 lie in one chunk (Bp is a multiple of 4); chunk-padding
+      // rows and tokens past the sequence end are written as exact zeros
+      const int p = m0 + wm * C::WTM + C::FM * i + M::rrow(lane, g);
+      const int jc = p / s.Bp, ic = p - jc * s.Bp;
+      const int64_t t0 = s.tok0 + (int64_t)jc * s.B + ic;
+      bool real[4];
 #pragma unroll
-      for (int g = 0; g < M::NG; ++g) {
-        const int p = m0 + wm * C::WTM + C::FM * i + M::rrow(lane, g);
+      for (int r = 0; r < 4; ++r) real[r] = jc < s.nc && ic + r < s.B && t0 + r < s.L;
+      if (p >= P) continue;
+#pragma unroll
+      for (int j = 0; j < HJ; ++j) {
         const int f = f0 + wn * WF + C::FM * j + M::rcol(lane);
-        if (p < P && f < s.F) {
+        if (f < s.F) {
           const f32x4 gv = get4(acc[i][j], g), uv = get4(acc[i][j + HJ], g);
           bf16x4 v;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            // chunk-padding rows (and tokens past the sequence end) are exact zeros
-            const bool real = slab_row_token(s, p + r) >= 0;
-            v[r] = (__bf16)(real ? gv[r] / (1.f + __expf(-gv[r])) * uv[r] : 0.f);
-          }
+          for (int r = 0; r < 4; ++r)  // SiLU(a) = a / (1 + e^-a), fast reciprocal
+            v[r] = (__bf16)(real[r] ? gv[r] * __frcp_rn(1.f + __expf(-gv[r])) * uv[r] : 0.f);
           *(bf16x4 *)(zts + (int64_t)f * s.Lp + p) = v;
         }
       }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -572,30 +580,32 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
 #pragma unroll
   for (int i = 0; i < C::MI; ++i)
 #pragma unroll
-    for (int jj = 0; jj < C::NJ; ++jj)
+    for (int g = 0; g < M::NG; ++g) {
+      // rows m .. m + 3 share one chunk (Bp is a multiple of 4)
+      const int m = m0 + wm * C::WTM + C::FM * i + M::rrow(lane, g);
+      const int jc = m / s.Bp, ic = m - jc * s.Bp;
+      const int64_t t0 = s.tok0 + (int64_t)(j_first + jc) * s.B + ic;
+      bool valid[4];
 #pragma unroll
-      for (int g = 0; g < M::NG; ++g) {
-        const int m = m0 + wm * C::WTM + C::FM * i + M::rrow(lane, g);
+      for (int r = 0; r < 4; ++r) valid[r] = ic + r < s.B && t0 + r < s.L;
+      if (m >= R) continue;
+#pragma unroll
+      for (int jj = 0; jj < C::NJ; ++jj) {
         const int n = n0 + wn * C::WTN + C::FM * jj + M::rcol(lane);
-        if (n >= s.d || m >= R) continue;
-        // rows m .. m + 3 share one chunk (Bp is a multiple of 4)
-        const int ic = m % s.Bp;
-        const int64_t t0 = s.tok0 + (int64_t)(j_first + m / s.Bp) * s.B + ic;
+        if (n >= s.d) continue;
         const f32x4 a4 = get4(acc[i][jj], g);
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          if (os && ic + r < s.B && t0 + r < s.L) os[(t0 + r) * s.d + n] = a4[r];
+          if (os && valid[r]) os[(t0 + r) * s.d + n] = a4[r];
         if (rt) {
           const bf16x4 v = *(const bf16x4 *)(vts + (int64_t)n * s.Lp + row0 + m);
           bf16x4 rv;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const bool valid = ic + r < s.B && t0 + r < s.L;
-            rv[r] = (__bf16)(valid ? s.eta * ((float)v[r] - a4[r]) : 0.f);
-          }
+          for (int r = 0; r < 4; ++r) rv[r] = (__bf16)(valid[r] ? s.eta * ((float)v[r] - a4[r]) : 0.f);
           *(bf16x4 *)(rt + (int64_t)n_seq * s.d * s.Bp + (int64_t)n * s.Bp + m) = rv;
         }
       }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -905,7 +915,7 @@ static_assert(kChunkAlign % CONV_RUN == 0, "conv runs must not cross a chunk");
 
 // Block shapes, MFMA shapes and LDS row paddings chosen by timing on MI355X at
 // the 4B layer shape (d 2560, d_ff 9728, 16 chunks of 1024).
-using GateUpCfg = Cfg<2, 4, 64, 16, 16, 8>;
+using GateUpCfg = Cfg<2, 4, 64, 16, 16, 8, 1, 16>;
 using ProjCfg = Cfg<2, 4, 32, 16, 16, 8>;
 using ApplyCfg = Cfg<2, 4, 64, 16, 16, 8>;
 using ApplySmallCfg = Cfg<1, 2, 64, 16, 16, 8>;  // when ApplyCfg would leave most CUs idle
