@@ -4,8 +4,10 @@ Only the test suite, the package smoke check and the benchmark's CPU-baseline le
 may import this package; the HIP library and its binding never do.
 """
 from .ipttt_oracle import (  # noqa: F401
+    backward,
     chunk_ranges,
     conv_chunk,
+    conv_chunk_backward,
     decode_steps,
     final_weight_entries,
     gate_up,
@@ -13,5 +15,6 @@ from .ipttt_oracle import (  # noqa: F401
     prefill_prefix_form,
     prefill_with_resets,
     silu,
+    silu_grad,
     target_chunk,
 )

@@ -52,6 +52,12 @@ with its justification, in the design notes of the repository):
   R9  State persists across calls; each call starts a new chunk at its first
       token. Reset puts the pretrained W_0 back ([explainer] §3.2 boundary
       reset).
+  RB1 Training through the layer ([explainer] §4.1 continued training of a
+      pretrained model, §4.2 pretraining from scratch) differentiates the scan
+      as written, through every update (no stop-gradient). The trainable
+      inputs are X, E, W_g, W_u, the projection (trainable by [explainer]
+      §2.3), the conv weights and the fast weight's start value W_0 (the
+      pretrained down projection); eta is a fixed hyper-parameter.
 
 Parity: every function here is pinned by the not-gpu tests in
 tests/test_oracle.py against closed forms, library routines (torch silu,
@@ -74,6 +80,9 @@ __all__ = [
     "prefill_with_resets",
     "final_weight_entries",
     "decode_steps",
+    "silu_grad",
+    "conv_chunk_backward",
+    "backward",
 ]
 
 
@@ -276,3 +285,103 @@ def decode_steps(X, E, W_g, W_u, conv_w, Proj, W, eta, B, buffered=0, update="li
         _, W_after = prefill(X[None, :full], E[None, :full], W_g, W_u, conv_w, Proj, W, eta, B,
                              update=update)
     return O[0], W_after[0]
+
+
+def silu_grad(a: np.ndarray) -> np.ndarray:
+    """Derivative of SiLU: d/da [a sigmoid(a)] = sigmoid(a) (1 + a (1 - sigmoid(a)))."""
+    s = 1.0 / (1.0 + np.exp(-a))
+    return s * (1.0 + a * (1.0 - s))
+
+
+def conv_chunk_backward(dC_chunk, E_chunk, conv_w):
+    """Adjoint of conv_chunk for one chunk: given dL/dC, returns (dL/dE, dL/dconv_w).
+
+    C[t, c] += conv_w[c, j] E[t + j, c] for t + j inside the chunk, so each tap
+    sends dC[t] back to E[t + j] and collects dC[t] * E[t + j] for its weight.
+    """
+    dC_chunk, E_chunk, conv_w = _f64(dC_chunk), _f64(E_chunk), _f64(conv_w)
+    T, d = E_chunk.shape
+    dE = np.zeros((T, d), dtype=np.float64)
+    dw = np.zeros(conv_w.shape, dtype=np.float64)
+    for j in range(conv_w.shape[1]):
+        if j >= T:
+            break
+        dE[j:] += conv_w[:, j][None, :] * dC_chunk[: T - j]
+        dw[:, j] += (dC_chunk[: T - j] * E_chunk[j:]).sum(axis=0)
+    return dE, dw
+
+
+def backward(X, E, W_g, W_u, conv_w, Proj, W_start, eta, B, dO, dW_final=None, update="linear"):
+    """Gradients through the scan of prefill() (RB1), for the scalar loss whose
+    gradient with respect to O is dO and with respect to W_final is dW_final
+    (None: zero).
+
+    X, E, dO: [N, L, d]; W_start: [F, d] shared by the sequences or [N, F, d];
+    dW_final: [N, F, d] or None. Returns a dict with dX, dE [N, L, d], dW_g,
+    dW_u [d, F], dProj [d, d], dconv_w [d, Kc] (summed over sequences) and
+    dW_start (shape of W_start; summed over sequences when shared).
+
+    The forward is rerun chunk by chunk, keeping each chunk's W_k, then the
+    chain rule runs over the chunks in reverse with G = dL/dW_{k+1}:
+      linear  W_{k+1} = W_k + eta Z^T V:
+        dZ_k = dO_k W_k^T + eta V_k G^T     dV_k = eta Z_k G     G <- G + Z_k^T dO_k
+      mse     W_{k+1} = W_k - eta Z^T R,  R_k = Z_k W_k - V_k:
+        dY_k = dO_k - eta Z_k G             (gradient reaching Z_k W_k)
+        dZ_k = dY_k W_k^T - eta R_k G^T     dV_k = eta Z_k G     G <- G + Z_k^T dY_k
+    and on to the slow weights: with A = X W_g, U = X W_u, Z = SiLU(A) U,
+      dA = dZ U SiLU'(A), dU = dZ SiLU(A), dX = dA W_g^T + dU W_u^T,
+      dW_g = X^T dA, dW_u = X^T dU, dC = dV Proj^T, dProj = C^T dV, and the
+      conv's adjoint inside the chunk (conv_chunk_backward).
+    After the first chunk G is dL/dW_0.
+    """
+    _check_update(update)
+    X, E, dO = _f64(X), _f64(E), _f64(dO)
+    W_g, W_u, conv_w, Proj = _f64(W_g), _f64(W_u), _f64(conv_w), _f64(Proj)
+    W_start = _f64(W_start)
+    N, L, d = X.shape
+    F = W_start.shape[-2]
+    out = dict(dX=np.zeros_like(X), dE=np.zeros_like(E), dW_g=np.zeros_like(W_g),
+               dW_u=np.zeros_like(W_u), dProj=np.zeros_like(Proj), dconv_w=np.zeros_like(conv_w),
+               dW_start=np.zeros_like(W_start))
+    for n in range(N):
+        W = (W_start[n] if W_start.ndim == 3 else W_start).copy()
+        saved = []
+        for s, e in chunk_ranges(L, B):
+            A = X[n, s:e] @ W_g
+            U = X[n, s:e] @ W_u
+            Z = silu(A) * U
+            C = conv_chunk(E[n, s:e], conv_w)
+            V = C @ Proj
+            saved.append((s, e, A, U, Z, C, V, W))
+            if update == "linear":
+                W = W + eta * (Z.T @ V)
+            else:
+                W = W - eta * (Z.T @ (Z @ W - V))
+        G = np.zeros((F, d)) if dW_final is None else _f64(dW_final)[n].copy()
+        for s, e, A, U, Z, C, V, Wk in reversed(saved):
+            dOk = dO[n, s:e]
+            if update == "linear":
+                dZ = dOk @ Wk.T + eta * (V @ G.T)
+                dV = eta * (Z @ G)
+                G = G + Z.T @ dOk
+            else:
+                R = Z @ Wk - V
+                dY = dOk - eta * (Z @ G)
+                dZ = dY @ Wk.T - eta * (R @ G.T)
+                dV = eta * (Z @ G)
+                G = G + Z.T @ dY
+            dA = dZ * U * silu_grad(A)
+            dU = dZ * silu(A)
+            out["dX"][n, s:e] = dA @ W_g.T + dU @ W_u.T
+            out["dW_g"] += X[n, s:e].T @ dA
+            out["dW_u"] += X[n, s:e].T @ dU
+            dC = dV @ Proj.T
+            out["dProj"] += C.T @ dV
+            dEk, dwk = conv_chunk_backward(dC, E[n, s:e], conv_w)
+            out["dE"][n, s:e] = dEk
+            out["dconv_w"] += dwk
+        if W_start.ndim == 3:
+            out["dW_start"][n] = G
+        else:
+            out["dW_start"] += G
+    return out

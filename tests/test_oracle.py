@@ -351,11 +351,136 @@ def pin_decode_steps(orc):
     np.testing.assert_array_equal(Wd, W16[0])
 
 
+# ---- backward through the scan ------------------------------------------------
+
+GRAD_KEYS = ("dX", "dE", "dW_g", "dW_u", "dProj", "dconv_w", "dW_start")
+
+
+def lib_scan_graph(p, eta, B, update):
+    """The library model's scan kept on torch's autograd graph: the update step
+    is derived by autograd from its loss with create_graph, so the gradient of
+    anything downstream flows through every update."""
+    X, E = p["X"], p["E"]
+    N, L, _ = X.shape
+    Os, Wf = [], []
+    for n in range(N):
+        W = p["W_0"]
+        rows = []
+        for s in range(0, L, B):
+            e_ = min(s + B, L)
+            x = X[n, s:e_]
+            Z = Fn.silu(Fn.linear(x, p["W_g"].T)) * Fn.linear(x, p["W_u"].T)
+            Kc = p["conv_w"].shape[1]
+            inp = Fn.pad(E[n, s:e_].T[None], (0, Kc - 1))
+            C = Fn.conv1d(inp, p["conv_w"][:, None, :], groups=p["conv_w"].shape[0])[0].T
+            V = Fn.linear(C, p["Proj"].T)
+            rows.append(Z @ W)
+            loss = -((Z @ W) * V).sum() if update == "linear" else 0.5 * ((Z @ W - V) ** 2).sum()
+            (g,) = torch.autograd.grad(loss, W, create_graph=True)
+            W = W - eta * g
+        Os.append(torch.cat(rows))
+        Wf.append(W)
+    return torch.stack(Os), torch.stack(Wf)
+
+
+def grads_by_autograd(c, dO, dWf, eta, B, update):
+    p = {k: T(v).requires_grad_(True) for k, v in c.items()}
+    O, Wf = lib_scan_graph(p, eta, B, update)
+    loss = (O * T(dO)).sum() + (Wf * T(dWf)).sum()
+    names = ("X", "E", "W_g", "W_u", "Proj", "conv_w", "W_0")
+    gs = torch.autograd.grad(loss, [p[k] for k in names])
+    return {("d" + k if k != "W_0" else "dW_start"): g.numpy() for k, g in zip(names, gs)}
+
+
+def orc_grads(orc, c, dO, dWf, eta, B, update):
+    return orc.backward(c["X"], c["E"], c["W_g"], c["W_u"], c["conv_w"], c["Proj"], c["W_0"], eta,
+                        B, dO, dW_final=dWf, update=update)
+
+
+def pin_backward_autograd(orc):
+    """Every gradient against torch.autograd through the library model (both
+    rules, two sequences, a short last chunk, an upstream gradient on W_final)."""
+    for update, eta in (("linear", 0.05), ("mse", 0.02)):
+        c = case(31, N=2, L=23, d=5, F=7)
+        r = np.random.default_rng(32)
+        dO = r.standard_normal((2, 23, 5))
+        dWf = r.standard_normal((2, 7, 5))
+        got = orc_grads(orc, c, dO, dWf, eta, 5, update)
+        ref = grads_by_autograd(c, dO, dWf, eta, 5, update)
+        for k in GRAD_KEYS:
+            np.testing.assert_allclose(got[k], ref[k], rtol=1e-9, atol=1e-11, err_msg=f"{update} {k}")
+
+
+def pin_backward_finite_differences(orc):
+    """Directional derivatives of the (separately pinned) forward by central
+    differences: <grad, Delta> = (L(p + h Delta) - L(p - h Delta)) / 2h."""
+    for update, eta in (("linear", 0.1), ("mse", 0.05)):
+        c = case(41, N=1, L=11, d=4, F=6)
+        r = np.random.default_rng(42)
+        dO = r.standard_normal((1, 11, 4))
+        dWf = r.standard_normal((1, 6, 4))
+        g = orc_grads(orc, c, dO, dWf, eta, 3, update)
+
+        def loss(cc):
+            O, Wf = run(orc, cc, eta, 3, update)
+            return float((O * dO).sum() + (Wf * dWf).sum())
+
+        names = ("X", "E", "W_g", "W_u", "Proj", "conv_w", "W_0")
+        for trial in range(3):
+            delta = {k: r.standard_normal(c[k].shape) for k in names}
+            h = 1e-5
+            plus = {k: c[k] + h * delta[k] for k in names}
+            minus = {k: c[k] - h * delta[k] for k in names}
+            fd = (loss(plus) - loss(minus)) / (2 * h)
+            an = sum(float((g["d" + k if k != "W_0" else "dW_start"] * delta[k]).sum()) for k in names)
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (update, trial, fd, an)
+
+
+def pin_backward_eta0(orc):
+    """eta = 0: the textbook gated-MLP backward with the fixed weight W_0:
+    dW_0 = sum Z^T dO + dW_final, dX from dZ = dO W_0^T, and no gradient reaches
+    the target (E, Proj, conv)."""
+    c = case(51, N=2, L=9, d=4, F=6)
+    r = np.random.default_rng(52)
+    dO = r.standard_normal((2, 9, 4))
+    dWf = r.standard_normal((2, 6, 4))
+    g = orc_grads(orc, c, dO, dWf, 0.0, 4, "linear")
+    x = T(c["X"]).requires_grad_(True)
+    wg, wu = T(c["W_g"]).requires_grad_(True), T(c["W_u"]).requires_grad_(True)
+    Z = Fn.silu(x @ wg) * (x @ wu)
+    dx, dwg, dwu = torch.autograd.grad((Z @ T(c["W_0"]) * T(dO)).sum(), [x, wg, wu])
+    Zn = Z.detach().numpy()
+    np.testing.assert_allclose(g["dW_start"], np.einsum("ntf,ntc->fc", Zn, dO) + dWf.sum(0), rtol=1e-11)
+    np.testing.assert_allclose(g["dX"], dx.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(g["dW_g"], dwg.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(g["dW_u"], dwu.numpy(), rtol=1e-10, atol=1e-12)
+    for k in ("dE", "dProj", "dconv_w"):
+        assert np.abs(g[k]).max() == 0.0, k
+
+
+def pin_backward_linear_in_upstream(orc):
+    """The gradients are linear in the upstream gradients (dO, dW_final), and the
+    per-sequence start weight gets each sequence's own dW_0."""
+    c = case(61, N=2, L=10, d=4, F=6)
+    r = np.random.default_rng(62)
+    a = (r.standard_normal((2, 10, 4)), r.standard_normal((2, 6, 4)))
+    b = (r.standard_normal((2, 10, 4)), r.standard_normal((2, 6, 4)))
+    ga = orc_grads(orc, c, *a, 0.1, 3, "mse")
+    gb = orc_grads(orc, c, *b, 0.1, 3, "mse")
+    gs = orc_grads(orc, c, a[0] + 2 * b[0], a[1] + 2 * b[1], 0.1, 3, "mse")
+    for k in GRAD_KEYS:
+        np.testing.assert_allclose(gs[k], ga[k] + 2 * gb[k], rtol=1e-9, atol=1e-11)
+    c3 = dict(c, W_0=np.stack([c["W_0"], c["W_0"]]))
+    g3 = orc_grads(orc, c3, *a, 0.1, 3, "mse")
+    np.testing.assert_allclose(g3["dW_start"].sum(0), ga["dW_start"], rtol=1e-12)
+
+
 PINS = [
     pin_gate_up_library, pin_conv_library, pin_next_token_target, pin_eta0_textbook,
     pin_single_chunk, pin_library_model, pin_prefix_form, pin_dual_form, pin_final_state,
     pin_causality, pin_brute_force, pin_continuation, pin_batch_independence,
-    pin_update_direction, pin_resets, pin_decode_steps,
+    pin_update_direction, pin_resets, pin_decode_steps, pin_backward_autograd,
+    pin_backward_finite_differences, pin_backward_eta0, pin_backward_linear_in_upstream,
 ]
 
 
@@ -390,6 +515,19 @@ MUTANTS = {
     "prefix form inclusive": ("O[n, s:e] = Zs[k] @ (W0 + eta * prefix)\n            prefix = prefix + S[k]",
                               "prefix = prefix + S[k]\n            O[n, s:e] = Zs[k] @ (W0 + eta * prefix)"),
     "reset keeps state": ("            W = _f64(W_0).copy()\n", "            pass\n"),
+    # backward
+    "backward drops the update path of dZ": ("dZ = dOk @ Wk.T + eta * (V @ G.T)", "dZ = dOk @ Wk.T"),
+    "backward uses G_k not G_k+1": (
+        "dZ = dOk @ Wk.T + eta * (V @ G.T)\n                dV = eta * (Z @ G)\n                G = G + Z.T @ dOk",
+        "G = G + Z.T @ dOk\n                dZ = dOk @ Wk.T + eta * (V @ G.T)\n                dV = eta * (Z @ G)"),
+    "backward dV drops eta": ("dV = eta * (Z @ G)\n                G = G + Z.T @ dOk",
+                              "dV = Z @ G\n                G = G + Z.T @ dOk"),
+    "silu derivative drops a term": ("return s * (1.0 + a * (1.0 - s))", "return s"),
+    "conv adjoint shifted the wrong way": ("dE[j:] += conv_w[:, j][None, :] * dC_chunk[: T - j]",
+                                           "dE[: T - j] += conv_w[:, j][None, :] * dC_chunk[j:]"),
+    "mse backward residual path sign": ("dY = dOk - eta * (Z @ G)", "dY = dOk + eta * (Z @ G)"),
+    "mse backward drops R G^T": ("dZ = dY @ Wk.T - eta * (R @ G.T)", "dZ = dY @ Wk.T"),
+    "dProj transposed": ('out["dProj"] += C.T @ dV', 'out["dProj"] += (C.T @ dV).T'),
 }
 
 
@@ -408,7 +546,7 @@ def test_pins_catch_planted_mistakes(name):
     for pin in PINS:
         try:
             pin(mod)
-        except (AssertionError, ValueError, IndexError):
+        except (AssertionError, ValueError, IndexError, RuntimeError):
             failed.append(pin.__name__)
     assert failed, f"planted mistake '{name}' passed every pin"
 
