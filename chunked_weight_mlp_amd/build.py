@@ -9,7 +9,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libipttt.so")
-SOURCES = ["ipttt.cpp", "kernels_generic.hip", "kernels_mfma.hip", "kernels_decode.hip"]
+SOURCES = ["ipttt.cpp", "kernels_generic.hip", "kernels_mfma.hip", "kernels_decode.hip",
+           "kernels_backward.hip"]
 ARCH = "gfx950"
 
 

@@ -116,4 +116,40 @@ hipError_t mf_update_one(const Slab &s, int j, const WsPtrs &ws, float *w_state,
 hipError_t mf_apply(const Slab &s, int q0, int nq, const WsPtrs &ws, float *o,
                     hipStream_t st);
 
+// Gate/up that also writes the pre-activations At = X W_g, Ut = X W_u
+// ([n][F][Lp] bf16, padding rows 0), for the backward.
+hipError_t mf_gateup_pre(const Slab &s, const __bf16 *x, const Weights &w, const WsPtrs &ws,
+                         __bf16 *at, __bf16 *ut, hipStream_t st);
+// Backward scan over all chunks of the slab, last to first: snap[n][j] =
+// bf16(G) (G_{j+1}), then G += Zt_j . Bt_j; g is fp32 [n][d][F].
+hipError_t mf_update_reverse(const Slab &s, const __bf16 *zt, const __bf16 *bt, float *g,
+                             __bf16 *snap, hipStream_t st);
+
+// ---- backward (bf16 MFMA path, one slab holding the whole sequence) -----------
+struct BwBufs {
+  const __bf16 *zt, *at, *ut;  // [n][F][Lp] Z, X W_g, X W_u (token-contiguous)
+  const __bf16 *c, *vt;        // [n][Lp][d] conv output; [n][d][Lp] eta V
+  const __bf16 *snap_w;        // [n][nc][d][F] W_j, the weight chunk j applied
+  const __bf16 *snap_g;        // [n][nc][d][F] G_{j+1} = dL/dW_{j+1}
+  const __bf16 *dot, *xt;      // [n][d][Lp] dO and X, transposed
+  __bf16 *dat, *dut;           // [n][F][Lp] dA, dU (dut directly follows dat)
+  __bf16 *dvt;                 // [n][d][Lp] dV
+  float *dc;                   // [n][Lp][d] dC
+  float *part;                 // [conv runs][d][Kc] partial conv-weight gradients
+};
+hipError_t bw_transpose_f32(const Slab &s, const float *in, __bf16 *out, hipStream_t st);
+hipError_t bw_transpose_bf16(const Slab &s, const __bf16 *in, __bf16 *out, hipStream_t st);
+hipError_t bw_dz(const Slab &s, const BwBufs &b, hipStream_t st);
+hipError_t bw_dv(const Slab &s, const BwBufs &b, hipStream_t st);
+hipError_t bw_dc(const Slab &s, const BwBufs &b, const void *proj, hipStream_t st);
+hipError_t bw_dx(const Slab &s, const BwBufs &b, const void *wg, const void *wu, float *dx,
+                 hipStream_t st);
+hipError_t bw_dw(const Slab &s, const BwBufs &b, float *dwg, float *dwu, hipStream_t st);
+hipError_t bw_dproj(const Slab &s, const BwBufs &b, float *dproj, hipStream_t st);
+int64_t bw_conv_runs(const Slab &s);
+hipError_t bw_conv(const Slab &s, const BwBufs &b, const __bf16 *e, const void *conv_w, float *de,
+                   float *dconv, hipStream_t st);
+hipError_t bw_sum_seq(const float *in, int n, int64_t len, float *out, hipStream_t st);
+hipError_t bw_fill(float *p, int64_t n, float v, hipStream_t st);
+
 }  // namespace ipttt

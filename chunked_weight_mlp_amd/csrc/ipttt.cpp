@@ -423,6 +423,47 @@ ipttt_status dispatch(ipttt_layer *h, const void *x, const void *e, float *o, in
   return run_scan<float>(h, (const float *)x, (const float *)e, o, slot0, n_seq, L, seq_stride, st);
 }
 
+// ---- backward ---------------------------------------------------------------
+
+bool bw_supported(const ipttt_layer_desc *d) {
+  return use_mfma(d) && d->update == IPTTT_UPDATE_LINEAR;
+}
+
+struct BwLayout {
+  size_t zt, at, ut, c, vt, wscr, gscr, snap_w, snap_g, dot, xt, dat, dut, dvt, dc, part, total;
+};
+
+// Workspace of the backward: the whole sequence in one slab of K chunks.
+BwLayout bw_layout(const ipttt_layer_desc &d, int n, int64_t L) {
+  BwLayout w{};
+  const size_t Bp = (size_t)chunk_pitch(d.chunk), K = (size_t)((L + d.chunk - 1) / d.chunk);
+  const size_t Lp = K * Bp, F = (size_t)d.d_ff, D = (size_t)d.d, N = (size_t)n;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += (size_t)ipttt::round_up((int64_t)bytes, 256);
+    return o;
+  };
+  w.zt = take(N * F * Lp * 2);
+  w.at = take(N * F * Lp * 2);
+  w.ut = take(N * F * Lp * 2);
+  w.c = take(N * Lp * D * 2);
+  w.vt = take(N * D * Lp * 2);
+  w.wscr = take(N * D * F * 4);
+  w.gscr = take(N * D * F * 4);
+  w.snap_w = take(N * K * D * F * 2);
+  w.snap_g = take(N * K * D * F * 2);
+  w.dot = take(N * D * Lp * 2);
+  w.xt = take(N * D * Lp * 2);
+  w.dat = take(N * F * Lp * 2);
+  w.dut = take(N * F * Lp * 2);
+  w.dvt = take(N * D * Lp * 2);
+  w.dc = take(N * Lp * D * 4);
+  w.part = take(N * K * (Bp / 16) * D * (size_t)d.conv_k * 4);
+  w.total = off;
+  return w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -483,6 +524,126 @@ ipttt_status ipttt_decode_step(ipttt_layer *h, const void *x, const void *e, int
   }
   if (pos + 1 == d.chunk)  // chunk complete: its update, as prefill would run it
     return dispatch(h, x, e, nullptr, 0, batch, d.chunk, seq_stride, st);
+  return IPTTT_OK;
+}
+
+size_t ipttt_backward_workspace_bytes(const ipttt_layer_desc *desc, int32_t batch,
+                                      int64_t seq_len) {
+  std::string saved = g_last_error;
+  ipttt_status s = check_sizes(desc);
+  g_last_error = saved;
+  if (s != IPTTT_OK || batch < 1 || seq_len < 1 || !bw_supported(desc)) return 0;
+  if ((seq_len + desc->chunk - 1) / desc->chunk * chunk_pitch(desc->chunk) > ((int64_t)1 << 30))
+    return 0;
+  return bw_layout(*desc, batch, seq_len).total;
+}
+
+ipttt_status ipttt_backward_layer(ipttt_layer *h, const void *x, const void *e, const float *d_o,
+                                  const float *d_wfinal, int32_t batch, int64_t seq_len,
+                                  const ipttt_grads *grads, void *workspace,
+                                  size_t workspace_bytes, void *hip_stream) {
+  using namespace ipttt;
+  if (!h) return fail(IPTTT_E_INVALID, "handle is NULL");
+  const ipttt_layer_desc &d = h->desc;
+  if (!bw_supported(&d))
+    return fail(IPTTT_E_UNSUPPORTED, "backward runs on bf16 MFMA layers with the linear rule");
+  if (batch < 1 || seq_len < 1)
+    return fail(IPTTT_E_INVALID, "batch=%d seq_len=%lld must be >= 1", batch, (long long)seq_len);
+  if (batch > d.max_batch)
+    return fail(IPTTT_E_INVALID, "batch=%d exceeds max_batch=%d", batch, d.max_batch);
+  ipttt_status s = check_call(h, x, e, d_o);
+  if (s != IPTTT_OK) return s;
+  if (!grads) return fail(IPTTT_E_INVALID, "grads is NULL");
+  float *outs[] = {grads->dx, grads->de, grads->dw_gate, grads->dw_up, grads->dproj,
+                   grads->dconv_w, grads->dw0};
+  const char *onames[] = {"dx", "de", "dw_gate", "dw_up", "dproj", "dconv_w", "dw0"};
+  for (int i = 0; i < 7; ++i)
+    if (!outs[i] || ((uintptr_t)outs[i] & 3u))
+      return fail(IPTTT_E_INVALID, "grads->%s is NULL or not 4-byte aligned", onames[i]);
+  if (d_wfinal && ((uintptr_t)d_wfinal & 3u))
+    return fail(IPTTT_E_INVALID, "d_wfinal is not 4-byte aligned");
+  const int B = d.chunk, Bp = chunk_pitch(B);
+  const int64_t K = (seq_len + B - 1) / B;
+  if (K * Bp > ((int64_t)1 << 30)) return fail(IPTTT_E_UNSUPPORTED, "seq_len too large");
+  if (!workspace || ((uintptr_t)workspace & 255u))
+    return fail(IPTTT_E_INVALID, "workspace is NULL or not 256-byte aligned");
+  const BwLayout lay = bw_layout(d, batch, seq_len);
+  if (workspace_bytes < lay.total)
+    return fail(IPTTT_E_WORKSPACE, "workspace_bytes=%zu below the %zu bytes this backward needs",
+                workspace_bytes, lay.total);
+
+  hipStream_t st = (hipStream_t)hip_stream;
+  char *base = (char *)workspace;
+  Slab sl{};
+  sl.n_seq = batch;
+  sl.d = d.d;
+  sl.F = d.d_ff;
+  sl.Kc = d.conv_k;
+  sl.B = B;
+  sl.Bp = Bp;
+  sl.nc = (int)K;
+  sl.nc_cap = (int)K;
+  sl.G = 1;
+  sl.ng_cap = (int)K;
+  sl.Lp = K * Bp;
+  sl.tok0 = 0;
+  sl.L = seq_len;
+  sl.x_seq_stride = seq_len * d.d;
+  sl.eta = d.eta;
+  sl.mse = 0;
+  WsPtrs ws{nullptr, base + lay.zt, base + lay.c, base + lay.vt, base + lay.snap_w, nullptr, nullptr};
+  Weights w{d.w_gate, d.w_up, d.proj, d.conv_w};
+  BwBufs bb{};
+  bb.zt = (const __bf16 *)(base + lay.zt);
+  bb.at = (const __bf16 *)(base + lay.at);
+  bb.ut = (const __bf16 *)(base + lay.ut);
+  bb.c = (const __bf16 *)(base + lay.c);
+  bb.vt = (const __bf16 *)(base + lay.vt);
+  bb.snap_w = (const __bf16 *)(base + lay.snap_w);
+  bb.snap_g = (const __bf16 *)(base + lay.snap_g);
+  bb.dot = (const __bf16 *)(base + lay.dot);
+  bb.xt = (const __bf16 *)(base + lay.xt);
+  bb.dat = (__bf16 *)(base + lay.dat);
+  bb.dut = (__bf16 *)(base + lay.dut);
+  bb.dvt = (__bf16 *)(base + lay.dvt);
+  bb.dc = (float *)(base + lay.dc);
+  bb.part = (float *)(base + lay.part);
+  float *wscr = (float *)(base + lay.wscr), *gscr = (float *)(base + lay.gscr);
+  const size_t dF = (size_t)d.d * d.d_ff;
+
+  // forward recompute from w0: Z with its pre-activations, eta V, W_j per chunk
+  for (int32_t i = 0; i < batch; ++i)
+    TRY_HIP(hipMemcpyAsync(wscr + i * dF, d.w0, dF * sizeof(float), hipMemcpyDeviceToDevice, st),
+            "w0 copy");
+  LAUNCH(IPTTT_K_GATEUP,
+         mf_gateup_pre(sl, (const __bf16 *)x, w, ws, (__bf16 *)(base + lay.at),
+                       (__bf16 *)(base + lay.ut), st),
+         "gate/up launch");
+  LAUNCH(IPTTT_K_CONV, mf_conv(sl, (const __bf16 *)e, w, ws, st), "conv launch");
+  LAUNCH(IPTTT_K_PROJ, mf_proj(sl, w, ws, st), "proj launch");
+  LAUNCH(IPTTT_K_UPDATE, mf_update_scan(sl, ws, wscr, st), "update scan launch");
+  // reverse scan: G_{j+1} per chunk, G_0 = dL/dW_0 per sequence
+  LAUNCH(IPTTT_K_BW_MISC, bw_transpose_f32(sl, d_o, (__bf16 *)bb.dot, st), "dO transpose launch");
+  LAUNCH(IPTTT_K_BW_MISC, bw_transpose_bf16(sl, (const __bf16 *)x, (__bf16 *)bb.xt, st),
+         "x transpose launch");
+  if (d_wfinal)
+    TRY_HIP(hipMemcpyAsync(gscr, d_wfinal, batch * dF * sizeof(float), hipMemcpyDeviceToDevice, st),
+            "d_wfinal copy");
+  else
+    LAUNCH(IPTTT_K_BW_MISC, bw_fill(gscr, (int64_t)(batch * dF), 0.f, st), "fill launch");
+  LAUNCH(IPTTT_K_BW_SCAN, mf_update_reverse(sl, bb.zt, bb.dot, gscr, (__bf16 *)bb.snap_g, st),
+         "reverse scan launch");
+  // per-chunk gradients, then the slow weights
+  LAUNCH(IPTTT_K_BW_DZ, bw_dz(sl, bb, st), "dZ launch");
+  LAUNCH(IPTTT_K_BW_DV, bw_dv(sl, bb, st), "dV launch");
+  LAUNCH(IPTTT_K_BW_SMALL, bw_dc(sl, bb, d.proj, st), "dC launch");
+  LAUNCH(IPTTT_K_BW_SMALL,
+         bw_conv(sl, bb, (const __bf16 *)e, d.conv_w, grads->de, grads->dconv_w, st),
+         "conv adjoint launch");
+  LAUNCH(IPTTT_K_BW_DX, bw_dx(sl, bb, d.w_gate, d.w_up, grads->dx, st), "dX launch");
+  LAUNCH(IPTTT_K_BW_DW, bw_dw(sl, bb, grads->dw_gate, grads->dw_up, st), "dW launch");
+  LAUNCH(IPTTT_K_BW_SMALL, bw_dproj(sl, bb, grads->dproj, st), "dProj launch");
+  LAUNCH(IPTTT_K_BW_SMALL, bw_sum_seq(gscr, batch, (int64_t)dF, grads->dw0, st), "dW0 launch");
   return IPTTT_OK;
 }
 

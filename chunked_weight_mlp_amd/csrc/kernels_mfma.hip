@@ -29,343 +29,18 @@
 //              chunks, optionally write the bf16 snapshot S_q, then
 //              accumulate Zt . Vt over the group's tokens.
 //   k_conv     depthwise conv of E, vector loads, sliding window.
-#include "internal.h"
+
+#include "mfma_common.h"
 
 namespace ipttt {
 namespace mfma {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-
-// MFMA tile shapes. Operand: lane l supplies row orow(l) of A (column of B) and
-// K values okoff(l) .. okoff(l) + 7 of one MFMA K step (K wide). Result: the
-// lane holds NG groups of 4 consecutive rows, group g starting at row
-// rrow(l, g), all in column rcol(l). Any consistent assignment of K values to
-// (lane, slot) gives the same sum; the row and column maps are the hardware's.
-template <int FM>
-struct Mfma;
-template <>
-struct Mfma<16> {
-  typedef f32x4 acc_t;
-  static constexpr int K = 32, NG = 1;
-  __device__ static __forceinline__ acc_t mma(bf16x8 a, bf16x8 b, acc_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-  }
-  __device__ static __forceinline__ int orow(int l) { return l & 15; }
-  __device__ static __forceinline__ int okoff(int l) { return 8 * (l >> 4); }
-  __device__ static __forceinline__ int rrow(int l, int) { return 4 * (l >> 4); }
-  __device__ static __forceinline__ int rcol(int l) { return l & 15; }
-  // transposed-A source address of lane l (see mma_stage_t)
-  __device__ static __forceinline__ int tr_row(int l) { return 8 * (l >> 4) + (l & 15) / 4; }
-  __device__ static __forceinline__ int tr_col(int l) { return 4 * (l & 3); }
-};
-template <>
-struct Mfma<32> {
-  typedef f32x16 acc_t;
-  static constexpr int K = 16, NG = 4;
-  __device__ static __forceinline__ acc_t mma(bf16x8 a, bf16x8 b, acc_t c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-  }
-  __device__ static __forceinline__ int orow(int l) { return l & 31; }
-  __device__ static __forceinline__ int okoff(int l) { return 8 * (l >> 5); }
-  __device__ static __forceinline__ int rrow(int l, int g) { return 8 * g + 4 * (l >> 5); }
-  __device__ static __forceinline__ int rcol(int l) { return l & 31; }
-  __device__ static __forceinline__ int tr_row(int l) { return 8 * (l >> 5) + (l & 15) / 4; }
-  __device__ static __forceinline__ int tr_col(int l) { return 16 * ((l >> 4) & 1) + 4 * (l & 3); }
-};
-
-__device__ __forceinline__ f32x4 get4(const f32x4 &a, int) { return a; }
-__device__ __forceinline__ f32x4 get4(const f32x16 &a, int g) {
-  return f32x4{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
-}
-__device__ __forceinline__ void set4(f32x4 &a, int, f32x4 v) { a = v; }
-__device__ __forceinline__ void set4(f32x16 &a, int g, f32x4 v) {
-  a[4 * g] = v[0];
-  a[4 * g + 1] = v[1];
-  a[4 * g + 2] = v[2];
-  a[4 * g + 3] = v[3];
-}
-
-template <int WM_, int WN_, int BK_, int FM_ = 32, int PAD_ = 16, int PADT_ = 8, int OCC_ = 1,
-          int GM_ = 8, int WTN_ = 64>
-struct Cfg {
-  static constexpr int WM = WM_, WN = WN_, BK = BK_, FM = FM_;
-  static constexpr int GM = GM_;  // row tiles per group in the tile order (tile_of)
-  static constexpr int OCC = OCC_;  // waves per SIMD the register allocation must allow
-  using M = Mfma<FM>;
-  using acc_t = typename M::acc_t;
-  static constexpr int WTM = 128, WTN = WTN_;  // wave tile
-  static constexpr int MI = WTM / FM, NJ = WTN / FM;
-  static constexpr int BM = WTM * WM, BN = WTN * WN;
-  static constexpr int NTHR = 64 * WM * WN;
-  static constexpr int PITCH = BK + PAD_;  // LDS row pitch in bf16
-  static constexpr int KP = BK / 8;        // 16-byte pieces per row per step
-  static constexpr int RPP = NTHR / KP;    // rows covered by one pass of all threads
-  static constexpr int A_PIECES = BM / RPP;
-  static constexpr int B_PIECES = BN / RPP;
-  static constexpr int A_STAGE = BM * PITCH, B_STAGE = BN * PITCH;
-  static constexpr int SMEM_ELEMS = 2 * (A_STAGE + B_STAGE);
-  // A held K-major in LDS ([BK rows of K][BM columns of M]) for an A operand
-  // stored M-contiguous in memory.
-  static constexpr int PITCH_T = BM + PADT_;
-  static constexpr int AT_PIECES = BK * (BM / 8) / NTHR;
-  static constexpr int AT_STAGE = BK * PITCH_T;
-  static constexpr int SMEM_T_ELEMS = 2 * (AT_STAGE + B_STAGE);
-  // both operands K-major ([BK rows of K][BM or BN columns])
-  static constexpr int PITCH_TB = BN + PADT_;
-  static constexpr int BT_STAGE = BK * PITCH_TB;
-  static constexpr int SMEM_TT_ELEMS = 2 * (AT_STAGE + BT_STAGE);
-  static_assert(BK % 32 == 0 && BM % RPP == 0 && BN % RPP == 0, "bad tile config");
-  static_assert(PAD_ % 8 == 0 && PADT_ % 4 == 0, "LDS rows must keep 16 / 8-byte alignment");
-  static_assert((BK * (BM / 8)) % NTHR == 0 && (BK * (BN / 8)) % NTHR == 0,
-                "bad transposed tile config");
-};
-
-__device__ __forceinline__ uint4 ld16(const __bf16 *p) { return *(const uint4 *)p; }
-
-// Logical block index: the hardware hands consecutive workgroups to the 8 XCDs
-// in turn; give each XCD a contiguous range of logical tiles so that tiles
-// that share operands also share that XCD's L2.
-__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
-  const int per = nblocks / 8, rem = nblocks % 8;
-  const int x = bid % 8, q = bid / 8;
-  return x * per + min(x, rem) + q;
-}
-
-// Tile order inside a grid of (nm x nn) tiles: groups of GM row tiles, column
-// tile slowest within a group, so neighbouring blocks share both operands.
-template <int GM>
-__device__ __forceinline__ void tile_of(int id, int nm, int nn, int &tm, int &tn) {
-  const int group = id / (GM * nn);
-  const int first = group * GM;
-  const int gm = min(GM, nm - first);
-  const int in = id % (GM * nn);
-  tm = first + in % gm;
-  tn = in / gm;
-}
-
-// Per-thread loader: the rows this thread copies into LDS (row (tid / KP) +
-// RPP i, 16-byte piece tid % KP). Rows outside the matrix point at a valid row
-// of it: every load is unconditional and nothing consumes the loaded value
-// before it is stored to LDS, so the loads of the next step stay in flight
-// behind the current step's MFMAs. The rows they feed are masked at the
-// epilogue (each output row or column depends only on its own operand row).
-template <class C, int NP>
-struct Loader {
-  const __bf16 *ptr[NP];
-  uint4 v[NP];
-  __device__ __forceinline__ void fetch(int k0, int q) {
-#pragma unroll
-    for (int i = 0; i < NP; ++i) v[i] = ld16(ptr[i] + k0 + 8 * q);
-  }
-  __device__ __forceinline__ void stash(__bf16 *stage, int r0, int q) const {
-#pragma unroll
-    for (int i = 0; i < NP; ++i) *(uint4 *)(stage + (r0 + C::RPP * i) * C::PITCH + 8 * q) = v[i];
-  }
-};
-
-template <class C>
-__device__ __forceinline__ void mma_stage(const __bf16 *As, const __bf16 *Bs, int arow0,
-                                          const int (&brow)[C::NJ], int lane,
-                                          typename C::acc_t (&acc)[C::MI][C::NJ]) {
-  using M = typename C::M;
-  const int r = M::orow(lane), kq = M::okoff(lane);
-#pragma unroll
-  for (int u = 0; u < C::BK / M::K; ++u) {
-    bf16x8 a[C::MI], b[C::NJ];
-#pragma unroll
-    for (int j = 0; j < C::NJ; ++j)
-      b[j] = *(const bf16x8 *)(Bs + (brow[j] + r) * C::PITCH + M::K * u + kq);
-#pragma unroll
-    for (int i = 0; i < C::MI; ++i)
-      a[i] = *(const bf16x8 *)(As + (arow0 + C::FM * i + r) * C::PITCH + M::K * u + kq);
-#pragma unroll
-    for (int i = 0; i < C::MI; ++i)
-#pragma unroll
-      for (int j = 0; j < C::NJ; ++j) acc[i][j] = M::mma(a[i], b[j], acc[i][j]);
-  }
-}
-
-// ---- A operand stored M-contiguous (K-major rows) ---------------------------
-// The tile is copied into LDS as BK rows of BM elements; each MFMA A fragment
-// (8 consecutive K values of one M row per lane) is assembled from two
-// ds_read_b64_tr_b16. That instruction works on groups of 16 lanes: lane i of
-// a group receives element (i % 4) of the 8-byte chunk read by lane 4 j + i / 4
-// of the group, for j = 0..3. Source lane p therefore points at K row (p / 4)
-// and M columns 4 (p % 4) .. + 3 of a 4 x 16 block, and lane i gets that
-// block's column i: 4 consecutive K values of M row i (tr_row / tr_col place
-// each 16-lane group on the rows and K values its MFMA operand needs).
-// COLS = BM for the A operand, BN for a B operand stored N-contiguous (its
-// fragments are read the same way, the MFMA B layout mirroring A's).
-template <class C, int COLS>
-struct LoaderT {
-  static constexpr int NP = C::BK * (COLS / 8) / C::NTHR;
-  static constexpr int PITCH = COLS + (C::PITCH_T - C::BM);
-  const __bf16 *ptr[NP];  // piece i's K row start, offset to its columns
-  int64_t ld;             // elements between K rows
-  uint4 v[NP];
-  // the K row and first column of piece i of thread tid within a step
-  __device__ static __forceinline__ int krow(int tid, int i) { return (tid + i * C::NTHR) / (COLS / 8); }
-  __device__ static __forceinline__ int col(int tid, int i) { return 8 * ((tid + i * C::NTHR) % (COLS / 8)); }
-  __device__ __forceinline__ void fetch(int k0) {
-#pragma unroll
-    for (int i = 0; i < NP; ++i) v[i] = ld16(ptr[i] + (int64_t)k0 * ld);
-  }
-  __device__ __forceinline__ void stash(__bf16 *stage, int tid) const {
-#pragma unroll
-    for (int i = 0; i < NP; ++i) *(uint4 *)(stage + krow(tid, i) * PITCH + col(tid, i)) = v[i];
-  }
-};
-
-__device__ __forceinline__ v4i16 ds_read_tr16(const __bf16 *p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)p);
-}
-
-// One MFMA operand fragment (8 K values of one row) from a K-major LDS tile
-// of row pitch `pitch`, via two transposing reads.
-template <class M>
-__device__ __forceinline__ bf16x8 frag_t(const __bf16 *tile, int pitch, int u, int col0, int trr,
-                                         int trc) {
-  const __bf16 *base = tile + (M::K * u + trr) * pitch + col0 + trc;
-  const v4i16 lo = ds_read_tr16(base), hi = ds_read_tr16(base + 4 * pitch);
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
-// TB = false: B tile row-major [BN][BK] (K-contiguous); true: K-major like A.
-template <class C, bool TB>
-__device__ __forceinline__ void mma_stage_t(const __bf16 *At, const __bf16 *Bs, int arow0,
-                                            const int (&brow)[C::NJ], int lane,
-                                            typename C::acc_t (&acc)[C::MI][C::NJ]) {
-  using M = typename C::M;
-  const int r = M::orow(lane), kq = M::okoff(lane);
-  const int trr = M::tr_row(lane), trc = M::tr_col(lane);
-#pragma unroll
-  for (int u = 0; u < C::BK / M::K; ++u) {
-    bf16x8 a[C::MI], b[C::NJ];
-#pragma unroll
-    for (int j = 0; j < C::NJ; ++j)
-      b[j] = TB ? frag_t<M>(Bs, C::PITCH_TB, u, brow[j], trr, trc)
-                : *(const bf16x8 *)(Bs + (brow[j] + r) * C::PITCH + M::K * u + kq);
-#pragma unroll
-    for (int i = 0; i < C::MI; ++i) a[i] = frag_t<M>(At, C::PITCH_T, u, arow0 + C::FM * i, trr, trc);
-#pragma unroll
-    for (int i = 0; i < C::MI; ++i)
-#pragma unroll
-      for (int j = 0; j < C::NJ; ++j) acc[i][j] = M::mma(a[i], b[j], acc[i][j]);
-  }
-}
-
-// Full K loop over nk steps of BK with double-buffered LDS. Stage addresses are
-// formed arithmetically from the __shared__ base so the compiler keeps them in
-// the LDS address space (ds_read / ds_write, not flat).
-template <class C>
-__device__ __forceinline__ void kloop(__bf16 *smem, Loader<C, C::A_PIECES> &la,
-                                      Loader<C, C::B_PIECES> &lb, int nk, int tid, int arow0,
-                                      const int (&brow)[C::NJ],
-                                      typename C::acc_t (&acc)[C::MI][C::NJ]) {
-  __bf16 *const Bbase = smem + 2 * C::A_STAGE;
-  const int lane = tid & 63, r0 = tid / C::KP, q = tid % C::KP;
-  la.fetch(0, q);
-  lb.fetch(0, q);
-  la.stash(smem, r0, q);
-  lb.stash(Bbase, r0, q);
-  __syncthreads();
-  for (int s = 0; s < nk; ++s) {
-    const int cur = s & 1;
-    if (s + 1 < nk) {
-      la.fetch((s + 1) * C::BK, q);
-      lb.fetch((s + 1) * C::BK, q);
-    }
-    mma_stage<C>(smem + cur * C::A_STAGE, Bbase + cur * C::B_STAGE, arow0, brow, lane, acc);
-    if (s + 1 < nk) {
-      la.stash(smem + (cur ^ 1) * C::A_STAGE, r0, q);
-      lb.stash(Bbase + (cur ^ 1) * C::B_STAGE, r0, q);
-    }
-    __syncthreads();
-  }
-}
-
-template <class C>
-__device__ __forceinline__ void kloop_t(__bf16 *smem, LoaderT<C, C::BM> &la,
-                                        Loader<C, C::B_PIECES> &lb, int nk, int tid, int arow0,
-                                        const int (&brow)[C::NJ],
-                                        typename C::acc_t (&acc)[C::MI][C::NJ]) {
-  __bf16 *const Bbase = smem + 2 * C::AT_STAGE;
-  const int lane = tid & 63, r0 = tid / C::KP, q = tid % C::KP;
-  la.fetch(0);
-  lb.fetch(0, q);
-  la.stash(smem, tid);
-  lb.stash(Bbase, r0, q);
-  __syncthreads();
-  for (int s = 0; s < nk; ++s) {
-    const int cur = s & 1;
-    if (s + 1 < nk) {
-      la.fetch((s + 1) * C::BK);
-      lb.fetch((s + 1) * C::BK, q);
-    }
-    mma_stage_t<C, false>(smem + cur * C::AT_STAGE, Bbase + cur * C::B_STAGE, arow0, brow, lane,
-                          acc);
-    if (s + 1 < nk) {
-      la.stash(smem + (cur ^ 1) * C::AT_STAGE, tid);
-      lb.stash(Bbase + (cur ^ 1) * C::B_STAGE, r0, q);
-    }
-    __syncthreads();
-  }
-}
-
-// Both operands K-major in memory (the Gram product of Zt with itself).
-template <class C>
-__device__ __forceinline__ void kloop_tt(__bf16 *smem, LoaderT<C, C::BM> &la,
-                                         LoaderT<C, C::BN> &lb, int nk, int tid, int arow0,
-                                         const int (&brow)[C::NJ],
-                                         typename C::acc_t (&acc)[C::MI][C::NJ]) {
-  __bf16 *const Bbase = smem + 2 * C::AT_STAGE;
-  const int lane = tid & 63;
-  la.fetch(0);
-  lb.fetch(0);
-  la.stash(smem, tid);
-  lb.stash(Bbase, tid);
-  __syncthreads();
-  for (int s = 0; s < nk; ++s) {
-    const int cur = s & 1;
-    if (s + 1 < nk) {
-      la.fetch((s + 1) * C::BK);
-      lb.fetch((s + 1) * C::BK);
-    }
-    mma_stage_t<C, true>(smem + cur * C::AT_STAGE, Bbase + cur * C::BT_STAGE, arow0, brow, lane,
-                         acc);
-    if (s + 1 < nk) {
-      la.stash(smem + (cur ^ 1) * C::AT_STAGE, tid);
-      lb.stash(Bbase + (cur ^ 1) * C::BT_STAGE, tid);
-    }
-    __syncthreads();
-  }
-}
-
-template <class C>
-__device__ __forceinline__ void zero_acc(typename C::acc_t (&acc)[C::MI][C::NJ]) {
-#pragma unroll
-  for (int i = 0; i < C::MI; ++i)
-#pragma unroll
-    for (int j = 0; j < C::NJ; ++j) acc[i][j] = typename C::acc_t{};
-}
-
-// Token of slab row p (slab rows fit in 32 bits), or -1 for a padding row.
-__device__ __forceinline__ int64_t slab_row_token(const Slab &s, int p) {
-  const int j = p / s.Bp, i = p - j * s.Bp;
-  if (i >= s.B || j >= s.nc) return -1;
-  const int64_t t = s.tok0 + (int64_t)j * s.B + i;
-  return t < s.L ? t : -1;
-}
 
 // ---------------------------------------------------------------------------
 template <class C>
 __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC))) void k_gateup(
     Slab s, const __bf16 *__restrict__ x, const __bf16 *__restrict__ wg,
-    const __bf16 *__restrict__ wu, __bf16 *__restrict__ zt) {
+    const __bf16 *__restrict__ wu, __bf16 *__restrict__ zt, __bf16 *__restrict__ at,
+    __bf16 *__restrict__ ut) {
   static_assert(C::SMEM_ELEMS * 2 <= 160 * 1024, "LDS overflow");
   __shared__ __bf16 smem[C::SMEM_ELEMS];
   using M = typename C::M;
@@ -436,6 +111,17 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
           for (int r = 0; r < 4; ++r)  // SiLU(a) = a / (1 + e^-a), fast reciprocal
             v[r] = (__bf16)(real[r] ? gv[r] * __frcp_rn(1.f + __expf(-gv[r])) * uv[r] : 0.f);
           *(bf16x4 *)(zts + (int64_t)f * s.Lp + p) = v;
+          if (at) {  // pre-activations, for the backward
+            bf16x4 va, vu;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              va[r] = (__bf16)(real[r] ? gv[r] : 0.f);
+              vu[r] = (__bf16)(real[r] ? uv[r] : 0.f);
+            }
+            const int64_t off = (int64_t)n_seq * s.F * s.Lp + (int64_t)f * s.Lp + p;
+            *(bf16x4 *)(at + off) = va;
+            *(bf16x4 *)(ut + off) = vu;
+          }
         }
       }
     }
@@ -682,13 +368,15 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
 // at a time (one K loop per group of G chunks, whose rows are contiguous).
 // A operand = Zt (rows f, token-contiguous); B operand = Vt or Rt (rows c).
 // snap_each_group: write S[g] = bf16(W) before group g's accumulation;
-// snap_after: write S = bf16(W) after the last chunk.
+// snap_after: write S = bf16(W) after the last chunk. reverse (G = 1): walk
+// the chunks last to first, snapshot S[j] before chunk j (the backward's
+// G_{j+1}).
 template <class C>
 __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC))) void k_update(
     Slab s, int j_first, int n_chunks, int G, const __bf16 *__restrict__ zt,
     const __bf16 *__restrict__ bsrc, int64_t b_ld, int64_t b_seq_stride, int64_t b_chunk_stride,
     float *__restrict__ w, __bf16 *__restrict__ snap, int64_t snap_seq_stride,
-    int64_t snap_group_stride, int snap_each_group, int snap_after) {
+    int64_t snap_group_stride, int snap_each_group, int snap_after, int reverse) {
   static_assert(C::SMEM_ELEMS * 2 <= 160 * 1024, "LDS overflow");
   __shared__ __bf16 smem[C::SMEM_ELEMS];
   using M = typename C::M;
@@ -746,7 +434,8 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
   const int steps = s.Bp / C::BK;
   const __bf16 *zts = zt + (int64_t)n_seq * s.F * s.Lp;
   const __bf16 *bs = bsrc + n_seq * b_seq_stride;
-  for (int jc = 0; jc < n_chunks; jc += G) {
+  for (int it = 0; it < n_chunks; it += G) {
+    const int jc = reverse ? n_chunks - 1 - it : it;
     const int j = j_first + jc;
     const int nch = min(G, n_chunks - jc);
     if (snap_each_group)
@@ -833,11 +522,11 @@ __global__ __launch_bounds__(256) void k_conv(Slab s, const __bf16 *__restrict__
 // ---- launchers (templated on the block configuration) ---------------------
 template <class C>
 hipError_t launch_gateup(const Slab &s, const __bf16 *x, const Weights &w, const WsPtrs &ws,
-                         hipStream_t st) {
+                         hipStream_t st, __bf16 *at = nullptr, __bf16 *ut = nullptr) {
   const int64_t P = (int64_t)s.nc * s.Bp;
   const int64_t nb = ((P + C::BM - 1) / C::BM) * ((s.F + C::BN / 2 - 1) / (C::BN / 2)) * s.n_seq;
   hipLaunchKernelGGL(k_gateup<C>, dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, x,
-                     (const __bf16 *)w.w_gate, (const __bf16 *)w.w_up, (__bf16 *)ws.zt);
+                     (const __bf16 *)w.w_gate, (const __bf16 *)w.w_up, (__bf16 *)ws.zt, at, ut);
   return hipGetLastError();
 }
 
@@ -886,7 +575,21 @@ hipError_t launch_update_scan(const Slab &s, const WsPtrs &ws, float *w_state, h
   // B operand: Vt rows c; chunk jc starts jc * Bp tokens along the row
   hipLaunchKernelGGL(k_update<C>, dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, 0, s.nc, s.G,
                      (const __bf16 *)ws.zt, (const __bf16 *)ws.vt, s.Lp, (int64_t)s.d * s.Lp,
-                     (int64_t)s.Bp, w_state, (__bf16 *)ws.s, (int64_t)s.ng_cap * dF, dF, 1, 0);
+                     (int64_t)s.Bp, w_state, (__bf16 *)ws.s, (int64_t)s.ng_cap * dF, dF, 1, 0, 0);
+  return hipGetLastError();
+}
+
+// Backward scan: G (fp32, [n][d][F] like W) += Zt_j . Bt_j over the chunks in
+// reverse, writing snap[n][j] = bf16(G) before chunk j. Bt rows c are
+// token-contiguous with the slab's row layout (pitch Lp).
+template <class C>
+hipError_t launch_update_reverse(const Slab &s, const __bf16 *zt, const __bf16 *bt, float *g,
+                                 __bf16 *snap, hipStream_t st) {
+  const int64_t dF = (int64_t)s.d * s.F;
+  const int64_t nb = ((s.F + C::BM - 1) / C::BM) * ((s.d + C::BN - 1) / C::BN) * s.n_seq;
+  hipLaunchKernelGGL(k_update<C>, dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, 0, s.nc, 1, zt, bt,
+                     s.Lp, (int64_t)s.d * s.Lp, (int64_t)s.Bp, g, snap, (int64_t)s.nc_cap * dF, dF,
+                     1, 0, 1);
   return hipGetLastError();
 }
 
@@ -899,7 +602,7 @@ hipError_t launch_update_one(const Slab &s, int j, const WsPtrs &ws, float *w_st
   hipLaunchKernelGGL(k_update<C>, dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, j, 1, 1,
                      (const __bf16 *)ws.zt, (const __bf16 *)ws.rt, (int64_t)s.Bp,
                      (int64_t)s.d * s.Bp, (int64_t)0, w_state, (__bf16 *)ws.s, dF, (int64_t)0, 0,
-                     1);
+                     1, 0);
   return hipGetLastError();
 }
 
@@ -967,6 +670,14 @@ hipError_t mf_update_scan(const Slab &s, const WsPtrs &ws, float *w_state, hipSt
 }
 hipError_t mf_update_one(const Slab &s, int j, const WsPtrs &ws, float *w_state, hipStream_t st) {
   return mfma::launch_update_one<mfma::UpdateCfg>(s, j, ws, w_state, st);
+}
+hipError_t mf_gateup_pre(const Slab &s, const __bf16 *x, const Weights &w, const WsPtrs &ws,
+                         __bf16 *at, __bf16 *ut, hipStream_t st) {
+  return mfma::launch_gateup<mfma::GateUpCfg>(s, x, w, ws, st, at, ut);
+}
+hipError_t mf_update_reverse(const Slab &s, const __bf16 *zt, const __bf16 *bt, float *g,
+                             __bf16 *snap, hipStream_t st) {
+  return mfma::launch_update_reverse<mfma::UpdateCfg>(s, zt, bt, g, snap, st);
 }
 
 }  // namespace ipttt

@@ -29,12 +29,13 @@ IPTTT_FLAG_GENERIC_KERNELS = 1
 
 EXPORTS = (
     "ipttt_workspace_bytes", "ipttt_init", "ipttt_prefill_layer", "ipttt_prefill_packed",
-    "ipttt_decode_step",
+    "ipttt_decode_step", "ipttt_backward_workspace_bytes", "ipttt_backward_layer",
     "ipttt_reset_fast_weights", "ipttt_profile_begin", "ipttt_profile_end", "ipttt_destroy",
     "ipttt_status_str", "ipttt_last_error",
 )
 
-KERNELS = ("gateup", "conv", "proj", "update", "apply", "snapshot", "gram")  # ipttt_kernel order
+KERNELS = ("gateup", "conv", "proj", "update", "apply", "snapshot", "gram",  # ipttt_kernel order
+           "bw_scan", "bw_dz", "bw_dv", "bw_dx", "bw_dw", "bw_small", "bw_misc")
 
 
 class LayerDesc(ctypes.Structure):
@@ -58,6 +59,11 @@ class LayerDesc(ctypes.Structure):
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
     ]
+
+
+class Grads(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_void_p) for k in
+                ("dx", "de", "dw_gate", "dw_up", "dproj", "dconv_w", "dw0")]
 
 
 class IptttError(RuntimeError):
@@ -90,6 +96,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ipttt_prefill_packed.restype = ctypes.c_int
     lib.ipttt_decode_step.argtypes = [vp, vp, vp, i64, i32, vp, i32, vp]
     lib.ipttt_decode_step.restype = ctypes.c_int
+    lib.ipttt_backward_workspace_bytes.argtypes = [pdesc, i32, i64]
+    lib.ipttt_backward_workspace_bytes.restype = ctypes.c_size_t
+    lib.ipttt_backward_layer.argtypes = [vp, vp, vp, vp, vp, i32, i64, ctypes.POINTER(Grads), vp,
+                                         ctypes.c_size_t, vp]
+    lib.ipttt_backward_layer.restype = ctypes.c_int
     lib.ipttt_reset_fast_weights.argtypes = [vp, i32, i32, vp]
     lib.ipttt_reset_fast_weights.restype = ctypes.c_int
     lib.ipttt_profile_begin.argtypes = [vp]
@@ -161,6 +172,19 @@ def ipttt_prefill_packed(h, x, e, o, slot: int, seq_len: int, doc_starts, stream
 def ipttt_decode_step(h, x, e, seq_stride: int, pos: int, o, batch: int, stream=None) -> None:
     _check(load().ipttt_decode_step(h, _ptr(x), _ptr(e), seq_stride, pos, _ptr(o), batch,
                                     _stream(stream)))
+
+
+def ipttt_backward_workspace_bytes(desc: LayerDesc, batch: int, seq_len: int) -> int:
+    return load().ipttt_backward_workspace_bytes(ctypes.byref(desc), batch, seq_len)
+
+
+def ipttt_backward_layer(h, x, e, d_o, d_wfinal, batch: int, seq_len: int, grads: dict,
+                         workspace, workspace_bytes: int, stream=None) -> None:
+    """grads: {"dx", "de", "dw_gate", "dw_up", "dproj", "dconv_w", "dw0"} -> fp32 buffers."""
+    g = None if grads is None else Grads(**{k: _ptr(grads[k]) for k, _ in Grads._fields_})
+    _check(load().ipttt_backward_layer(h, _ptr(x), _ptr(e), _ptr(d_o), _ptr(d_wfinal), batch,
+                                       seq_len, None if g is None else ctypes.byref(g),
+                                       _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
 def ipttt_reset_fast_weights(h, first_seq: int, n_seq: int, stream=None) -> None:
@@ -255,6 +279,29 @@ class Layer:
         ipttt_decode_step(self.handle, x_chunk, e_chunk, x_chunk.shape[1] * x_chunk.shape[2], pos, o,
                           x_chunk.shape[0], stream)
         return o
+
+    def backward(self, x, e, d_o, d_wfinal=None, workspace=None, grads=None, stream=None):
+        """Gradients through the scan of a prefill of x, e ([batch, seq_len, d]) that
+        starts from w0, for dL/dO = d_o and dL/dW_final = d_wfinal ([batch, d, d_ff]
+        fp32 or None). Returns the fp32 gradients as a dict (layouts of the inputs
+        and weights); workspace / grads may be passed in to reuse buffers."""
+        batch, seq_len, d = x.shape
+        dev = x.device
+        need = ipttt_backward_workspace_bytes(self.desc, batch, seq_len)
+        if need == 0:
+            raise IptttError(IPTTT_E_UNSUPPORTED, "backward unsupported for this layer or size")
+        if workspace is None or workspace.numel() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        if grads is None:
+            f32 = dict(dtype=torch.float32, device=dev)
+            kc = self.tensors["conv_w"].shape[1]
+            grads = dict(dx=torch.empty(x.shape, **f32), de=torch.empty(x.shape, **f32),
+                         dw_gate=torch.empty((self.d_ff, d), **f32),
+                         dw_up=torch.empty((self.d_ff, d), **f32), dproj=torch.empty((d, d), **f32),
+                         dconv_w=torch.empty((d, kc), **f32), dw0=torch.empty((d, self.d_ff), **f32))
+        ipttt_backward_layer(self.handle, x, e, d_o, d_wfinal, batch, seq_len, grads, workspace,
+                             workspace.numel(), stream)
+        return grads
 
     def close(self) -> None:
         if getattr(self, "handle", None):

@@ -165,6 +165,42 @@ ipttt_status ipttt_prefill_packed(ipttt_layer *h, const void *x, const void *e, 
 ipttt_status ipttt_decode_step(ipttt_layer *h, const void *x, const void *e, int64_t seq_stride,
                                int32_t pos, float *o, int32_t batch, void *hip_stream);
 
+/* Backward (training through the layer: continued training of a pretrained
+ * model and pretraining from scratch, explainer page §4.1 and §4.2). For a
+ * prefill of sequences 0..batch-1 that each start from w0, seq_len tokens
+ * each, and a scalar loss with gradient d_o = dL/dO ([batch][seq_len][d]
+ * fp32) and d_wfinal = dL/dW_final ([batch][d][d_ff] fp32 in the w_state
+ * layout, or NULL for zero), computes the gradients with respect to the
+ * inputs and the slow weights, differentiating through every update of the
+ * scan (eta is not trained). The forward is recomputed inside the call from
+ * x, e and w0; w_state and the layer's workspace are not touched. Every
+ * output is fp32 and overwritten:
+ *   dx, de     [batch][seq_len][d]
+ *   dw_gate, dw_up [d_ff][d]   dproj [d][d]   dconv_w [d][conv_k]   (layouts of
+ *   dw0 [d][d_ff]                           the weights, summed over the batch)
+ * workspace: device scratch of ipttt_backward_workspace_bytes() bytes,
+ * 256-byte aligned, exclusively the call's until it completes on the stream.
+ * Supported: bf16 layers on the MFMA path with the linear rule; other layers
+ * return IPTTT_E_UNSUPPORTED. Same pointer and size validation as prefill. */
+typedef struct {
+  float *dx, *de;
+  float *dw_gate, *dw_up;
+  float *dproj;
+  float *dconv_w;
+  float *dw0;
+} ipttt_grads;
+
+/* Workspace bytes of ipttt_backward_layer for `batch` sequences of seq_len
+ * tokens; 0 if the sizes are invalid or the layer's backward is unsupported.
+ * Pointers in `desc` are not read. */
+size_t ipttt_backward_workspace_bytes(const ipttt_layer_desc *desc, int32_t batch,
+                                      int64_t seq_len);
+
+ipttt_status ipttt_backward_layer(ipttt_layer *h, const void *x, const void *e, const float *d_o,
+                                  const float *d_wfinal, int32_t batch, int64_t seq_len,
+                                  const ipttt_grads *grads, void *workspace,
+                                  size_t workspace_bytes, void *hip_stream);
+
 /* w_state[s] := w0 bitwise for s in first_seq..first_seq+n_seq-1 (document
  * boundary, explainer page §3.2) and marks those slots as reset. */
 ipttt_status ipttt_reset_fast_weights(ipttt_layer *h, int32_t first_seq, int32_t n_seq,
@@ -182,7 +218,14 @@ typedef enum {
   IPTTT_K_APPLY = 4,    /* O = Z W_k                                 */
   IPTTT_K_SNAPSHOT = 5, /* bf16 / fp32 copy of W read by the apply   */
   IPTTT_K_GRAM = 6,     /* block-causal Z Z^T of a chunk group       */
-  IPTTT_K_COUNT = 7
+  IPTTT_K_BW_SCAN = 7,  /* backward: G += Z^T dO, chunks in reverse  */
+  IPTTT_K_BW_DZ = 8,    /* backward: dZ -> dA, dU                    */
+  IPTTT_K_BW_DV = 9,    /* backward: dV = eta Z G                    */
+  IPTTT_K_BW_DX = 10,   /* backward: dX                              */
+  IPTTT_K_BW_DW = 11,   /* backward: dW_gate, dW_up                  */
+  IPTTT_K_BW_SMALL = 12,/* backward: dC, dProj, conv adjoint, dW_0   */
+  IPTTT_K_BW_MISC = 13, /* backward: transposes, fills, copies       */
+  IPTTT_K_COUNT = 14
 } ipttt_kernel;
 
 ipttt_status ipttt_profile_begin(ipttt_layer *h);

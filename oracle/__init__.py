@@ -11,6 +11,7 @@ from .ipttt_oracle import (  # noqa: F401
     decode_steps,
     final_weight_entries,
     gate_up,
+    initial_weight_grad_entries,
     prefill,
     prefill_prefix_form,
     prefill_with_resets,

@@ -83,6 +83,7 @@ __all__ = [
     "silu_grad",
     "conv_chunk_backward",
     "backward",
+    "initial_weight_grad_entries",
 ]
 
 
@@ -385,3 +386,22 @@ def backward(X, E, W_g, W_u, conv_w, Proj, W_start, eta, B, dO, dW_final=None, u
         else:
             out["dW_start"] += G
     return out
+
+
+def initial_weight_grad_entries(X, W_g, W_u, dO, dW_final, rows, cols):
+    """Linear rule only: selected entries of dL/dW_0 for ONE long sequence.
+
+    With the linear update G_k = G_{k+1} + Z_k^T dO_k, so dL/dW_0 = dL/dW_final +
+    sum over all tokens of z_t^T dO_t: entry (f, c) needs one column of Z and
+    one of dO, O(L d) each. X, dO: [L, d]; dW_final: [F, d] or None; rows /
+    cols: equal-length F- and d-indices. Returns len(rows) values.
+    """
+    X, dO = _f64(X), _f64(dO)
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+    W_g, W_u = _f64(W_g), _f64(W_u)
+    ur, inv_r = np.unique(rows, return_inverse=True)
+    Zcols = gate_up(X, W_g[:, ur], W_u[:, ur])          # [L, |ur|]
+    acc = np.einsum("ti,ti->i", Zcols[:, inv_r], dO[:, cols])
+    base = np.zeros(len(rows)) if dW_final is None else _f64(dW_final)[rows, cols]
+    return base + acc

@@ -259,3 +259,66 @@ def test_decode_errors_before_device_work(lib):
         B.ipttt_decode_step(h, x, e, 128 * 64, 3, o, 0, stream=0)   # empty batch: no-op
     finally:
         B.ipttt_destroy(h)
+
+
+def test_backward_workspace_bytes(lib):
+    mem = FakeMem()
+    desc = make_desc(mem)
+    one = B.ipttt_backward_workspace_bytes(desc, 1, 128)
+    assert one > 0
+    assert B.ipttt_backward_workspace_bytes(desc, 2, 128) > one
+    assert B.ipttt_backward_workspace_bytes(desc, 1, 129) > one
+    assert B.ipttt_backward_workspace_bytes(desc, 0, 128) == 0
+    assert B.ipttt_backward_workspace_bytes(desc, 1, 0) == 0
+    # only bf16 MFMA layers with the linear rule have a backward
+    for kw in (dict(update=1), dict(in_dtype=0), dict(flags=B.IPTTT_FLAG_GENERIC_KERNELS)):
+        assert B.ipttt_backward_workspace_bytes(make_desc(mem, **kw), 1, 128) == 0
+
+
+def test_backward_errors_before_device_work(lib):
+    mem = FakeMem()
+    names = [k for k, _ in B.Grads._fields_]
+
+    def grads(**over):
+        g = {k: mem.ptr() for k in names}
+        g.update(over)
+        return g
+
+    desc = make_desc(mem)
+    h = B.ipttt_init(desc)
+    x, e, do = mem.ptr(), mem.ptr(), mem.ptr()
+    need = B.ipttt_backward_workspace_bytes(desc, 1, 128)
+    ws = mem.ptr(64)
+    try:
+        def call(batch=1, L=128, g=None, w=ws, wb=need, xx=x, dd=do, dwf=None):
+            return B.ipttt_backward_layer(h, xx, e, dd, dwf, batch, L, g or grads(), w, wb, stream=0)
+
+        for kw, status in ((dict(batch=0), B.IPTTT_E_INVALID), (dict(L=0), B.IPTTT_E_INVALID),
+                           (dict(batch=3), B.IPTTT_E_INVALID), (dict(xx=x + 2), B.IPTTT_E_INVALID),
+                           (dict(dd=None), B.IPTTT_E_INVALID), (dict(w=None), B.IPTTT_E_INVALID),
+                           (dict(w=ws + 64), B.IPTTT_E_INVALID),
+                           (dict(wb=need - 1), B.IPTTT_E_WORKSPACE),
+                           (dict(dwf=do + 2), B.IPTTT_E_INVALID)):
+            with pytest.raises(B.IptttError) as ei:
+                call(**kw)
+            assert ei.value.status == status, kw
+        for k in names:
+            for bad in (None, mem.ptr() + 2):
+                with pytest.raises(B.IptttError) as ei:
+                    call(g=grads(**{k: bad}))
+                assert ei.value.status == B.IPTTT_E_INVALID and k in str(ei.value)
+        with pytest.raises(B.IptttError) as ei:
+            B.ipttt_backward_layer(h, x, e, do, None, 1, 128, None, ws, need, stream=0)
+        assert ei.value.status == B.IPTTT_E_INVALID
+    finally:
+        B.ipttt_destroy(h)
+    for kw in (dict(update=1), dict(in_dtype=0)):
+        h = B.ipttt_init(make_desc(mem, **kw))
+        try:
+            with pytest.raises(B.IptttError) as ei:
+                B.ipttt_backward_layer(h, x, e, do, None, 1, 128, grads(), ws, 1 << 30, stream=0)
+            assert ei.value.status == B.IPTTT_E_UNSUPPORTED
+        finally:
+            B.ipttt_destroy(h)
+    assert lib.ipttt_backward_layer(None, None, None, None, None, 1, 1, None, None, 0, None) == \
+        B.IPTTT_E_INVALID

@@ -475,12 +475,24 @@ def pin_backward_linear_in_upstream(orc):
     np.testing.assert_allclose(g3["dW_start"].sum(0), ga["dW_start"], rtol=1e-12)
 
 
+def pin_initial_weight_grad_entries(orc):
+    """Sampled dL/dW_0 entries (linear rule) agree with the full backward."""
+    c = case(71, N=1, L=17, d=5, F=7)
+    r = np.random.default_rng(72)
+    dO, dWf = r.standard_normal((1, 17, 5)), r.standard_normal((1, 7, 5))
+    g = orc_grads(orc, c, dO, dWf, 0.07, 4, "linear")
+    rows, cols = r.integers(0, 7, 12), r.integers(0, 5, 12)
+    got = orc.initial_weight_grad_entries(c["X"][0], c["W_g"], c["W_u"], dO[0], dWf[0], rows, cols)
+    np.testing.assert_allclose(got, g["dW_start"][rows, cols], rtol=1e-10, atol=1e-12)
+
+
 PINS = [
     pin_gate_up_library, pin_conv_library, pin_next_token_target, pin_eta0_textbook,
     pin_single_chunk, pin_library_model, pin_prefix_form, pin_dual_form, pin_final_state,
     pin_causality, pin_brute_force, pin_continuation, pin_batch_independence,
     pin_update_direction, pin_resets, pin_decode_steps, pin_backward_autograd,
     pin_backward_finite_differences, pin_backward_eta0, pin_backward_linear_in_upstream,
+    pin_initial_weight_grad_entries,
 ]
 
 

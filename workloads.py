@@ -31,7 +31,7 @@ import dataclasses
 
 import torch
 
-SEEDS = dict(x=17, e=18, w_gate=19, w_up=20, proj=21, conv=22, w0=23)
+SEEDS = dict(x=17, e=18, w_gate=19, w_up=20, proj=21, conv=22, w0=23, d_o=24, d_wfinal=25)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -114,6 +114,19 @@ def make_inputs(w: Workload, device="cpu", seq_len=None, n_seq=None, seed_offset
     x = _randn((N, L, w.d), SEEDS["x"] + so, 1.0, w.dtype, device)
     e = _randn((N, L, w.d), SEEDS["e"] + so, 1.0, w.dtype, device)
     return x, e
+
+
+def make_upstream(w: Workload, device="cpu", seq_len=None, n_seq=None, seed_offset=0,
+                  wfinal_scale=0.1):
+    """Upstream gradients for the backward: dL/dO [n_seq, seq_len, d] ~ N(0, 1)
+    and dL/dW_final [n_seq, d, d_ff] ~ N(0, wfinal_scale^2) in the state layout,
+    both fp32."""
+    L = w.seq_len if seq_len is None else seq_len
+    N = w.n_seq if n_seq is None else n_seq
+    so = seed_offset
+    d_o = _randn((N, L, w.d), SEEDS["d_o"] + so, 1.0, "f32", device)
+    d_wf = _randn((N, w.d, w.d_ff), SEEDS["d_wfinal"] + so, wfinal_scale, "f32", device)
+    return d_o, d_wf
 
 
 def to_oracle(weights: dict):
