@@ -118,6 +118,62 @@ def kernel_work(w: wl.Workload, tokens: int, G: int = 1):
     return work
 
 
+def kernel_rates(prof: dict, work: dict, steps: int, ms_total: float, passes: int, dtype: str):
+    """Per-kernel launches, durations and rates, and the roofline entry of the
+    kernel with the largest total time among those with a work model."""
+    kernels = {}
+    for k, (n, ms) in prof.items():
+        if n == 0:
+            continue
+        avg = ms / n
+        entry = {"launches_per_step": n / steps, "avg_ms": round(avg, 4),
+                 "share": round(ms / max(ms_total, 1e-9), 4)}
+        if k in work:
+            per_pass = n / steps / passes          # launches of this kernel per pass
+            fl, by = (v / per_pass for v in work[k])
+            entry["tflops"] = round(fl / (avg * 1e-3) / 1e12, 2)
+            entry["gbps"] = round(by / (avg * 1e-3) / 1e9, 1)
+        kernels[k] = entry
+    dom = max((k for k in kernels if k in work), key=lambda k: prof[k][1])
+    per_pass = prof[dom][0] / steps / passes
+    dom_fl, dom_by = (v / per_pass for v in work[dom])
+    dom_avg_s = prof[dom][1] / prof[dom][0] * 1e-3
+    intensity = dom_fl / max(dom_by, 1)
+    ridge = PEAK[dtype] * 1e12 / (HBM_PEAK * 1e9)
+    if intensity >= ridge:
+        ach = dom_fl / dom_avg_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK[dtype], "unit": "TFLOP/s",
+                "frac": round(ach / PEAK[dtype], 4)}
+    else:
+        ach = dom_by / dom_avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK, 4)}
+    roof["algorithmic_bytes"] = round(dom_by)
+    roof["kernel"] = dom
+    return kernels, roof, dom
+
+
+def backward_work(w: wl.Workload, tokens: int):
+    """Algorithmic FLOPs and HBM bytes of one launch of each backward kernel kind
+    over `tokens` tokens (all sequences). bw_small lumps dC, dProj, the conv
+    adjoint and the dW_0 sum; bw_misc the transposes and fills."""
+    d, F, Kc = w.d, w.d_ff, w.conv_k
+    el = 2
+    chunks = -(-tokens // w.chunk)
+    snap = el * chunks * F * d
+    return {
+        "gateup": (4 * d * F * tokens, el * (tokens * d + 2 * F * d + 3 * tokens * F)),
+        "conv": (2 * Kc * d * tokens, el * (2 * tokens * d + Kc * d)),
+        "proj": (2 * d * d * tokens, el * (2 * tokens * d + d * d)),
+        "update": (2 * d * F * tokens, el * tokens * (F + d) + 8 * F * d + snap),
+        "bw_scan": (2 * d * F * tokens, el * tokens * (F + d) + 8 * F * d + snap),
+        "bw_dz": (4 * d * F * tokens, el * (2 * tokens * d + 4 * tokens * F) + 2 * snap),
+        "bw_dv": (2 * d * F * tokens, el * (tokens * F + tokens * d) + snap),
+        "bw_dx": (4 * d * F * tokens, el * (2 * tokens * F + 2 * F * d) + 4 * tokens * d),
+        "bw_dw": (4 * d * F * tokens, el * (2 * tokens * F + tokens * d) + 8 * F * d),
+    }
+
+
 def cpu_baseline(w: wl.Workload, x, e, weights, n_chunks: int):
     import numpy as np  # noqa: F401
     from threadpoolctl import threadpool_info
@@ -143,14 +199,38 @@ def cpu_baseline(w: wl.Workload, x, e, weights, n_chunks: int):
     }
 
 
+def trace_summary(path: str) -> str:
+    """Markdown table (kernel, calls, avg / min / max ms, share) of a rocprofv3
+    kernel_stats.csv, template arguments and namespaces shortened."""
+    import csv
+    import re
+    rows = sorted(csv.DictReader(open(path)), key=lambda r: -float(r["TotalDurationNs"]))
+    out = ["| kernel | calls | avg ms | min ms | max ms | share % |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = re.sub(r"ipttt::mfma::|ipttt::", "", r["Name"])
+        name = re.sub(r"\(.*$", "", name).replace("void ", "")
+        m = re.match(r"_ZN5ipttt4mfma\d+(\w+?)I", name)
+        if m:
+            name = m.group(1)
+        name = name.replace("__amd_rocclr_", "")
+        out.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e6:.3f} | "
+                   f"{float(r['MinNs']) / 1e6:.3f} | {float(r['MaxNs']) / 1e6:.3f} | "
+                   f"{float(r['Percentage']):.2f} |")
+    return "\n".join(out)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default=wl.HEADLINE, choices=sorted(wl.WORKLOADS))
+    ap.add_argument("--workload", default=None, choices=sorted(wl.WORKLOADS),
+                    help="default: the 128k / B = 1024 prefill; 32k / B = 512 with --backward")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward through the scan (ipttt_backward_layer) instead")
     ap.add_argument("--slab-chunks", type=int, default=0, help="chunks per pass (0 = all)")
-    ap.add_argument("--cpu-chunks", type=int, default=40, help="chunks in the oracle sample")
+    ap.add_argument("--cpu-chunks", type=int, default=0,
+                    help="chunks in the oracle sample (default 40; 4 with --backward)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--generic", action="store_true", help="generic FMA kernels instead of MFMA")
     ap.add_argument("--group-chunks", type=int, default=0,
@@ -158,7 +238,16 @@ def main():
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc "
                          "counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) and exit")
+    ap.add_argument("--trace-summary", metavar="KERNEL_STATS_CSV",
+                    help="print a markdown table of a rocprofv3 --stats kernel_stats.csv and exit")
     args = ap.parse_args()
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary))
+        return
+    if args.workload is None:
+        args.workload = "qwen3_4b_L32k_B512" if args.backward else wl.HEADLINE
+    if not args.cpu_chunks:
+        args.cpu_chunks = 4 if args.backward else 40
 
     if args.traffic_from:
         t = summarize_traffic(args.workload, *args.traffic_from)
@@ -179,6 +268,8 @@ def main():
 
     ipttt.load()
     w = wl.WORKLOADS[args.workload]
+    if args.backward:
+        return bench_backward(args, w)
     dev = "cuda:0"
     t0 = time.perf_counter()
     weights = wl.make_weights(w)
@@ -228,37 +319,9 @@ def main():
     passes = -(-w.n_chunks // slab)
     tok_per_pass = w.n_seq * min(w.seq_len, slab * w.chunk)
     work = kernel_work(w, tok_per_pass, G)
-    kernels = {}
-    for k, (n, ms) in prof.items():
-        if n == 0:
-            continue
-        avg = ms / n
-        entry = {"launches_per_step": n / args.steps, "avg_ms": round(avg, 4),
-                 "share": round(ms / max(ms_total, 1e-9), 4)}
-        if k in work:
-            per_pass = n / args.steps / passes          # launches of this kernel per pass
-            fl, by = (v / per_pass for v in work[k])
-            entry["tflops"] = round(fl / (avg * 1e-3) / 1e12, 2)
-            entry["gbps"] = round(by / (avg * 1e-3) / 1e9, 1)
-        kernels[k] = entry
-    dom = max((k for k in kernels if k in work), key=lambda k: prof[k][1])
-    per_pass = prof[dom][0] / args.steps / passes
-    dom_fl, dom_by = (v / per_pass for v in work[dom])
-    dom_avg_s = prof[dom][1] / prof[dom][0] * 1e-3
-    intensity = dom_fl / max(dom_by, 1)
-    ridge = PEAK[w.dtype] * 1e12 / (HBM_PEAK * 1e9)
-    if intensity >= ridge:
-        ach = dom_fl / dom_avg_s / 1e12
-        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK[w.dtype], "unit": "TFLOP/s",
-                "frac": round(ach / PEAK[w.dtype], 4)}
-    else:
-        ach = dom_by / dom_avg_s / 1e9
-        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK, 4)}
+    kernels, roof, dom = kernel_rates(prof, work, args.steps, ms_total, passes, w.dtype)
     # measured HBM bytes per launch (rocprofv3 counters, profiles/traffic_*.json)
     roof["traffic"] = None if args.generic else load_traffic(w.name, dom)
-    roof["algorithmic_bytes"] = round(dom_by)
-    roof["kernel"] = dom
 
     out = {
         "metric": METRIC,
@@ -284,6 +347,94 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, x, e, weights, args.cpu_chunks)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_backward(w: wl.Workload, x, e, weights, d_o, n_chunks: int):
+    from threadpoolctl import threadpool_info
+
+    import oracle
+
+    tokens = min(w.seq_len, n_chunks * w.chunk)
+    ow = wl.to_oracle(weights)
+    t0 = time.perf_counter()
+    oracle.backward(x[:1, :tokens].double().numpy(), e[:1, :tokens].double().numpy(), ow["W_g"],
+                    ow["W_u"], ow["conv_w"], ow["Proj"], ow["W_0"], w.eta, w.chunk,
+                    d_o[:1, :tokens].double().numpy(), update=w.update)
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"backward over the first {tokens} tokens ({tokens // w.chunk} chunks) of "
+                      f"sequence 0, float64 numpy, {dt:.1f} s"}
+
+
+def bench_backward(args, w: wl.Workload):
+    """One step = one ipttt_backward_layer call over the whole batch (forward
+    recompute from w0, reverse scan, every gradient), inputs and upstream
+    gradients resident in HBM."""
+    from chunked_weight_mlp_amd import ipttt
+
+    dev = "cuda:0"
+    weights = wl.make_weights(w)
+    x, e = wl.make_inputs(w)
+    d_o, d_wf = wl.make_upstream(w)
+    wdev = {k: v.to(dev) for k, v in weights.items()}
+    xd, ed, dod, dwfd = x.to(dev), e.to(dev), d_o.to(dev), d_wf.to(dev)
+    layer = ipttt.Layer(**wdev, chunk=w.chunk, eta=w.eta, update=w.update, max_batch=w.n_seq)
+    need = ipttt.ipttt_backward_workspace_bytes(layer.desc, w.n_seq, w.seq_len)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    grads = layer.backward(xd, ed, dod, dwfd, workspace=ws)
+    torch.cuda.synchronize()
+    print(f"[bench] backward {w.name}: workspace {need / 2**30:.1f} GiB", file=sys.stderr, flush=True)
+
+    def step():
+        layer.backward(xd, ed, dod, dwfd, workspace=ws, grads=grads)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        print(f"[bench] warmup {i + 1}/{args.warmup} done", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ipttt.ipttt_profile_begin(layer.handle)
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    prof = ipttt.ipttt_profile_end(layer.handle)
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / args.steps
+    tokens = w.n_seq * w.seq_len
+    kernels, roof, _ = kernel_rates(prof, backward_work(w, tokens), args.steps, ms_total, 1, w.dtype)
+    roof["traffic"] = None
+    d, F = w.d, w.d_ff
+    flops_tok = 22 * d * F + 6 * d * d
+    out = {
+        "metric": "fast-weight backward tokens/s per MLP layer (gradients through the scan)",
+        "value": round(tokens / (ms_step / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded Gaussian inputs, weights and upstream gradients)",
+        "config": {"workload": w.name, "mode": "backward", "d": d, "d_ff": F, "seq_len": w.seq_len,
+                   "chunk": w.chunk, "batch": w.n_seq, "update": w.update, "eta": w.eta},
+        "tflops": round(flops_tok * tokens / (ms_step * 1e-3) / 1e12, 2),
+        "roofline": roof,
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle backward on the host", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline_backward(w, x, e, weights, d_o, args.cpu_chunks)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

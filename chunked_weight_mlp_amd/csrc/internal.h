@@ -136,7 +136,12 @@ struct BwBufs {
   __bf16 *dvt;                 // [n][d][Lp] dV
   float *dc;                   // [n][Lp][d] dC
   float *part;                 // [conv runs][d][Kc] partial conv-weight gradients
+  float *part2;                // [kConvSumGroups][d][Kc] their sums by row group
+  float *dproj_part;           // [kDprojSplits][d][d] split-K partial dProj
 };
+constexpr int kConvSumGroups = 64;
+constexpr int kConvBwRun = 16;  // slab rows per thread of the conv adjoint
+constexpr int kDprojSplits = 8;
 hipError_t bw_transpose_f32(const Slab &s, const float *in, __bf16 *out, hipStream_t st);
 hipError_t bw_transpose_bf16(const Slab &s, const __bf16 *in, __bf16 *out, hipStream_t st);
 hipError_t bw_dz(const Slab &s, const BwBufs &b, hipStream_t st);
@@ -147,6 +152,7 @@ hipError_t bw_dx(const Slab &s, const BwBufs &b, const void *wg, const void *wu,
 hipError_t bw_dw(const Slab &s, const BwBufs &b, float *dwg, float *dwu, hipStream_t st);
 hipError_t bw_dproj(const Slab &s, const BwBufs &b, float *dproj, hipStream_t st);
 int64_t bw_conv_runs(const Slab &s);
+int bw_dproj_splits(const Slab &s);
 hipError_t bw_conv(const Slab &s, const BwBufs &b, const __bf16 *e, const void *conv_w, float *de,
                    float *dconv, hipStream_t st);
 hipError_t bw_sum_seq(const float *in, int n, int64_t len, float *out, hipStream_t st);

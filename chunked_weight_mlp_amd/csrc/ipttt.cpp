@@ -430,7 +430,8 @@ bool bw_supported(const ipttt_layer_desc *d) {
 }
 
 struct BwLayout {
-  size_t zt, at, ut, c, vt, wscr, gscr, snap_w, snap_g, dot, xt, dat, dut, dvt, dc, part, total;
+  size_t zt, at, ut, c, vt, wscr, gscr, snap_w, snap_g, dot, xt, dat, dut, dvt, dc, part, part2,
+      dproj_part, total;
 };
 
 // Workspace of the backward: the whole sequence in one slab of K chunks.
@@ -459,7 +460,9 @@ BwLayout bw_layout(const ipttt_layer_desc &d, int n, int64_t L) {
   w.dut = take(N * F * Lp * 2);
   w.dvt = take(N * D * Lp * 2);
   w.dc = take(N * Lp * D * 4);
-  w.part = take(N * K * (Bp / 16) * D * (size_t)d.conv_k * 4);
+  w.part = take(N * K * (Bp / ipttt::kConvBwRun) * D * (size_t)d.conv_k * 4);
+  w.part2 = take((size_t)ipttt::kConvSumGroups * D * (size_t)d.conv_k * 4);
+  w.dproj_part = take((size_t)ipttt::kDprojSplits * D * D * 4);
   w.total = off;
   return w;
 }
@@ -608,6 +611,8 @@ ipttt_status ipttt_backward_layer(ipttt_layer *h, const void *x, const void *e, 
   bb.dvt = (__bf16 *)(base + lay.dvt);
   bb.dc = (float *)(base + lay.dc);
   bb.part = (float *)(base + lay.part);
+  bb.part2 = (float *)(base + lay.part2);
+  bb.dproj_part = (float *)(base + lay.dproj_part);
   float *wscr = (float *)(base + lay.wscr), *gscr = (float *)(base + lay.gscr);
   const size_t dF = (size_t)d.d * d.d_ff;
 

@@ -15,6 +15,8 @@
 // the same accumulators, a two-level batch (sequence, chunk) and K split into
 // segments (one per sequence) for the weight gradients. The epilogue is a
 // functor that receives four consecutive output rows of one column.
+#include <algorithm>
+
 #include "mfma_common.h"
 
 namespace ipttt {
@@ -159,6 +161,17 @@ struct EpiRows {
   }
 };
 
+// fp32 partial sums: out[b2 * s2][row][col], pitch ld (one slice of a split K).
+struct EpiRowsSplit {
+  float *out;
+  int64_t s2, ld;
+  __device__ void operator()(int, int b2, int m, int n, f32x4 v) const {
+    float *o = out + b2 * s2;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) o[(int64_t)(m + r) * ld + n] = v[r];
+  }
+};
+
 // fp32 out[seq][token][col] for slab rows that are tokens (padding rows dropped).
 struct EpiTok {
   float *out;
@@ -219,7 +232,7 @@ __global__ __launch_bounds__(256) void k_transpose(Slab s, const TI *__restrict_
 // CONV_BW_RUN slab rows of one chunk: dE[t] = sum_q w[q] dC[t - q] (rows before
 // the chunk start contribute nothing), and its share of dconv[c][q] =
 // sum_t dC[t] E[t + q] (E zero past the chunk end) goes to part[run][c][q].
-constexpr int CONV_BW_RUN = 16;
+constexpr int CONV_BW_RUN = kConvBwRun;
 
 template <int KC>
 __global__ __launch_bounds__(256) void k_conv_bwd(Slab s, const float *__restrict__ dc,
@@ -292,14 +305,17 @@ __global__ __launch_bounds__(256) void k_conv_bwd(Slab s, const float *__restric
     for (int q = 0; q < KC; ++q) pp[k * KC + q] = acc[q][k];
 }
 
-// out[i] = sum over r < rows of in[r * len + i] (fixed order).
+// Row group y of gridDim.y: out[y * len + i] = sum over its rows r of
+// in[r * len + i], rows in ascending order (a fixed summation order).
 __global__ __launch_bounds__(256) void k_sum_rows(const float *__restrict__ in, int64_t rows,
                                                  int64_t len, float *__restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= len) return;
+  const int64_t per = (rows + gridDim.y - 1) / gridDim.y;
+  const int64_t r0 = blockIdx.y * per, r1 = min(rows, r0 + per);
   float a = 0.f;
-  for (int64_t r = 0; r < rows; ++r) a += in[r * len + i];
-  out[i] = a;
+  for (int64_t r = r0; r < r1; ++r) a += in[r * len + i];
+  out[blockIdx.y * len + i] = a;
 }
 
 __global__ __launch_bounds__(256) void k_fill(float *__restrict__ p, int64_t n, float v) {
@@ -428,20 +444,35 @@ hipError_t bw_dw(const Slab &s, const BwBufs &b, float *dwg, float *dwu, hipStre
   return launch_gemm<BwCfg, false, false>(g, e, st);
 }
 
+int bw_dproj_splits(const Slab &s) {
+  int sp = kDprojSplits;
+  while (sp > 1 && (s.Lp / BwCfg::BK) % sp) sp /= 2;
+  return sp;
+}
+
 hipError_t bw_dproj(const Slab &s, const BwBufs &b, float *dproj, hipStream_t st) {
+  // d x d outputs are too few tiles to fill the GPU: K (tokens) is split into
+  // sp slices whose partial sums are added in a fixed order afterwards
+  const int sp = bw_dproj_splits(s);
+  const int64_t kp = s.Lp / sp;
   GProb g{};
   g.M = s.d;
   g.N = s.d;
   g.nb1 = 1;
-  g.nb2 = 1;
+  g.nb2 = sp;
   g.nseg = s.n_seq;
   g.nph = 1;
   // dproj[c][i] = sum over tokens dV[t][c] C[t][i]: A = dVt rows c, B = C (K-major over i)
-  g.ph[0].a = kcontig(b.dvt, s.Lp, s.d, 0, 0, (int64_t)s.d * s.Lp);
-  g.ph[0].b = kmajor(b.c, s.d, s.d, 0, 0, s.Lp * s.d);
-  g.ph[0].K = (int)s.Lp;
-  EpiRows e{dproj, nullptr, 0, s.d};
-  return launch_gemm<BwCfg, false, true>(g, e, st);
+  g.ph[0].a = kcontig(b.dvt, s.Lp, s.d, 0, kp, (int64_t)s.d * s.Lp);
+  g.ph[0].b = kmajor(b.c, s.d, s.d, 0, kp * s.d, s.Lp * s.d);
+  g.ph[0].K = (int)kp;
+  const int64_t dd = (int64_t)s.d * s.d;
+  EpiRowsSplit e{b.dproj_part, dd, s.d};
+  hipError_t err = launch_gemm<BwCfg, false, true>(g, e, st);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(k_sum_rows, dim3((unsigned)((dd + 255) / 256)), dim3(256), 0, st,
+                     (const float *)b.dproj_part, (int64_t)sp, dd, dproj);
+  return hipGetLastError();
 }
 
 int64_t bw_conv_runs(const Slab &s) { return (int64_t)s.n_seq * s.nc * (s.Bp / CONV_BW_RUN); }
@@ -461,9 +492,16 @@ hipError_t bw_conv(const Slab &s, const BwBufs &b, const __bf16 *e, const void *
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  // partial sums of the runs: in row groups, then the groups (fixed order)
   const int64_t len = (int64_t)s.d * s.Kc;
-  hipLaunchKernelGGL(k_sum_rows, dim3((unsigned)((len + 255) / 256)), dim3(256), 0, st, b.part,
-                     bw_conv_runs(s), len, dconv);
+  const int64_t runs = bw_conv_runs(s);
+  const int groups = (int)std::min<int64_t>(kConvSumGroups, runs);
+  hipLaunchKernelGGL(k_sum_rows, dim3((unsigned)((len + 255) / 256), groups), dim3(256), 0, st,
+                     (const float *)b.part, runs, len, b.part2);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(k_sum_rows, dim3((unsigned)((len + 255) / 256)), dim3(256), 0, st,
+                     (const float *)b.part2, (int64_t)groups, len, dconv);
   return hipGetLastError();
 }
 static_assert(kChunkAlign % CONV_BW_RUN == 0, "conv runs must not cross a chunk");
