@@ -125,6 +125,18 @@ hipError_t mf_gateup_pre(const Slab &s, const __bf16 *x, const Weights &w, const
 hipError_t mf_update_reverse(const Slab &s, const __bf16 *zt, const __bf16 *bt, float *g,
                              __bf16 *snap, hipStream_t st);
 
+// One chunk j of the MSE rule with explicit buffers (the backward's recompute):
+// apply with the snapshot at snap (+ n * snap_seq), writing only the residual
+// eta (V - O) to rt + n * rt_seq + c * rt_ld + row (rt pre-offset to chunk j);
+// and W += Zt_j . B_j with B = bsrc (+ n * b_seq, rows c at b_ld, pre-offset
+// to chunk j), then snap_after = bf16(W) when non-null.
+hipError_t mf_apply_mse_chunk(const Slab &s, int j, const __bf16 *zt, const __bf16 *snap,
+                              int64_t snap_seq, const __bf16 *vt, __bf16 *rt, int64_t rt_seq,
+                              int64_t rt_ld, hipStream_t st);
+hipError_t mf_update_chunk(const Slab &s, int j, const __bf16 *zt, const __bf16 *bsrc,
+                           int64_t b_ld, int64_t b_seq, float *w, __bf16 *snap_after,
+                           int64_t snap_seq, hipStream_t st);
+
 // ---- backward (bf16 MFMA path, one slab holding the whole sequence) -----------
 struct BwBufs {
   const __bf16 *zt, *at, *ut;  // [n][F][Lp] Z, X W_g, X W_u (token-contiguous)
@@ -134,6 +146,8 @@ struct BwBufs {
   const __bf16 *dot, *xt;      // [n][d][Lp] dO and X, transposed
   __bf16 *dat, *dut;           // [n][F][Lp] dA, dU (dut directly follows dat)
   __bf16 *dvt;                 // [n][d][Lp] dV
+  __bf16 *dyt;                 // MSE: [n][d][Lp] dY = dO - eta Z G (gradient reaching Z W)
+  const __bf16 *rt;            // MSE: [n][d][Lp] eta (V - O) of every chunk
   float *dc;                   // [n][Lp][d] dC
   float *part;                 // [conv runs][d][Kc] partial conv-weight gradients
   float *part2;                // [kConvSumGroups][d][Kc] their sums by row group
@@ -144,7 +158,11 @@ constexpr int kConvBwRun = 16;  // slab rows per thread of the conv adjoint
 constexpr int kDprojSplits = 8;
 hipError_t bw_transpose_f32(const Slab &s, const float *in, __bf16 *out, hipStream_t st);
 hipError_t bw_transpose_bf16(const Slab &s, const __bf16 *in, __bf16 *out, hipStream_t st);
-hipError_t bw_dz(const Slab &s, const BwBufs &b, hipStream_t st);
+// dZ = a0 W_j^T + a1 G_{j+1}^T: (dO, eta V) for the linear rule, (dY, eta (V - O)) for MSE
+hipError_t bw_dz(const Slab &s, const BwBufs &b, const __bf16 *a0, const __bf16 *a1,
+                 hipStream_t st);
+// MSE rule, chunk j: dY_j, dV_j from P = Z_j G_{j+1}
+hipError_t bw_mse_p(const Slab &s, int j, const BwBufs &b, hipStream_t st);
 hipError_t bw_dv(const Slab &s, const BwBufs &b, hipStream_t st);
 hipError_t bw_dc(const Slab &s, const BwBufs &b, const void *proj, hipStream_t st);
 hipError_t bw_dx(const Slab &s, const BwBufs &b, const void *wg, const void *wu, float *dx,

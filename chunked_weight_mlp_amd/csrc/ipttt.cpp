@@ -425,13 +425,11 @@ ipttt_status dispatch(ipttt_layer *h, const void *x, const void *e, float *o, in
 
 // ---- backward ---------------------------------------------------------------
 
-bool bw_supported(const ipttt_layer_desc *d) {
-  return use_mfma(d) && d->update == IPTTT_UPDATE_LINEAR;
-}
+bool bw_supported(const ipttt_layer_desc *d) { return use_mfma(d); }
 
 struct BwLayout {
   size_t zt, at, ut, c, vt, wscr, gscr, snap_w, snap_g, dot, xt, dat, dut, dvt, dc, part, part2,
-      dproj_part, total;
+      dproj_part, dyt, rt, total;
 };
 
 // Workspace of the backward: the whole sequence in one slab of K chunks.
@@ -463,6 +461,9 @@ BwLayout bw_layout(const ipttt_layer_desc &d, int n, int64_t L) {
   w.part = take(N * K * (Bp / ipttt::kConvBwRun) * D * (size_t)d.conv_k * 4);
   w.part2 = take((size_t)ipttt::kConvSumGroups * D * (size_t)d.conv_k * 4);
   w.dproj_part = take((size_t)ipttt::kDprojSplits * D * D * 4);
+  const bool mse = d.update == IPTTT_UPDATE_MSE;
+  w.dyt = take(mse ? N * D * Lp * 2 : 0);
+  w.rt = take(mse ? N * D * Lp * 2 : 0);
   w.total = off;
   return w;
 }
@@ -549,7 +550,7 @@ ipttt_status ipttt_backward_layer(ipttt_layer *h, const void *x, const void *e, 
   if (!h) return fail(IPTTT_E_INVALID, "handle is NULL");
   const ipttt_layer_desc &d = h->desc;
   if (!bw_supported(&d))
-    return fail(IPTTT_E_UNSUPPORTED, "backward runs on bf16 MFMA layers with the linear rule");
+    return fail(IPTTT_E_UNSUPPORTED, "backward runs on bf16 MFMA layers");
   if (batch < 1 || seq_len < 1)
     return fail(IPTTT_E_INVALID, "batch=%d seq_len=%lld must be >= 1", batch, (long long)seq_len);
   if (batch > d.max_batch)
@@ -593,7 +594,8 @@ ipttt_status ipttt_backward_layer(ipttt_layer *h, const void *x, const void *e, 
   sl.L = seq_len;
   sl.x_seq_stride = seq_len * d.d;
   sl.eta = d.eta;
-  sl.mse = 0;
+  const bool mse = d.update == IPTTT_UPDATE_MSE;
+  sl.mse = mse ? 1 : 0;
   WsPtrs ws{nullptr, base + lay.zt, base + lay.c, base + lay.vt, base + lay.snap_w, nullptr, nullptr};
   Weights w{d.w_gate, d.w_up, d.proj, d.conv_w};
   BwBufs bb{};
@@ -613,6 +615,8 @@ ipttt_status ipttt_backward_layer(ipttt_layer *h, const void *x, const void *e, 
   bb.part = (float *)(base + lay.part);
   bb.part2 = (float *)(base + lay.part2);
   bb.dproj_part = (float *)(base + lay.dproj_part);
+  bb.dyt = (__bf16 *)(base + lay.dyt);
+  bb.rt = (const __bf16 *)(base + lay.rt);
   float *wscr = (float *)(base + lay.wscr), *gscr = (float *)(base + lay.gscr);
   const size_t dF = (size_t)d.d * d.d_ff;
 
@@ -626,7 +630,26 @@ ipttt_status ipttt_backward_layer(ipttt_layer *h, const void *x, const void *e, 
          "gate/up launch");
   LAUNCH(IPTTT_K_CONV, mf_conv(sl, (const __bf16 *)e, w, ws, st), "conv launch");
   LAUNCH(IPTTT_K_PROJ, mf_proj(sl, w, ws, st), "proj launch");
-  LAUNCH(IPTTT_K_UPDATE, mf_update_scan(sl, ws, wscr, st), "update scan launch");
+  const int64_t sseq = K * (int64_t)dF;  // snapshot pitch between sequences
+  __bf16 *snap_w = (__bf16 *)(base + lay.snap_w), *snap_g = (__bf16 *)(base + lay.snap_g);
+  __bf16 *rt = (__bf16 *)(base + lay.rt);
+  const int64_t tstride = (int64_t)d.d * sl.Lp;  // [n][d][Lp] pitch between sequences
+  if (!mse) {
+    LAUNCH(IPTTT_K_UPDATE, mf_update_scan(sl, ws, wscr, st), "update scan launch");
+  } else {
+    // chunk by chunk: W_j kept per chunk, residual eta (V - O_j) kept per chunk
+    LAUNCH(IPTTT_K_SNAPSHOT, gen_snapshot<__bf16>(sl, wscr, snap_w, sseq, st), "snapshot launch");
+    for (int64_t j = 0; j < K; ++j) {
+      LAUNCH(IPTTT_K_APPLY,
+             mf_apply_mse_chunk(sl, (int)j, bb.zt, snap_w + j * dF, sseq, bb.vt, rt + j * Bp,
+                                tstride, sl.Lp, st),
+             "apply launch");
+      LAUNCH(IPTTT_K_UPDATE,
+             mf_update_chunk(sl, (int)j, bb.zt, rt + j * Bp, sl.Lp, tstride, wscr,
+                             j + 1 < K ? snap_w + (j + 1) * dF : nullptr, sseq, st),
+             "update launch");
+    }
+  }
   // reverse scan: G_{j+1} per chunk, G_0 = dL/dW_0 per sequence
   LAUNCH(IPTTT_K_BW_MISC, bw_transpose_f32(sl, d_o, (__bf16 *)bb.dot, st), "dO transpose launch");
   LAUNCH(IPTTT_K_BW_MISC, bw_transpose_bf16(sl, (const __bf16 *)x, (__bf16 *)bb.xt, st),
@@ -636,11 +659,26 @@ ipttt_status ipttt_backward_layer(ipttt_layer *h, const void *x, const void *e, 
             "d_wfinal copy");
   else
     LAUNCH(IPTTT_K_BW_MISC, bw_fill(gscr, (int64_t)(batch * dF), 0.f, st), "fill launch");
-  LAUNCH(IPTTT_K_BW_SCAN, mf_update_reverse(sl, bb.zt, bb.dot, gscr, (__bf16 *)bb.snap_g, st),
-         "reverse scan launch");
-  // per-chunk gradients, then the slow weights
-  LAUNCH(IPTTT_K_BW_DZ, bw_dz(sl, bb, st), "dZ launch");
-  LAUNCH(IPTTT_K_BW_DV, bw_dv(sl, bb, st), "dV launch");
+  if (!mse) {
+    LAUNCH(IPTTT_K_BW_SCAN, mf_update_reverse(sl, bb.zt, bb.dot, gscr, snap_g, st),
+           "reverse scan launch");
+    // per-chunk gradients, then the slow weights
+    LAUNCH(IPTTT_K_BW_DZ, bw_dz(sl, bb, bb.dot, bb.vt, st), "dZ launch");
+    LAUNCH(IPTTT_K_BW_DV, bw_dv(sl, bb, st), "dV launch");
+  } else {
+    // chunk by chunk in reverse: T_j = G_{j+1}; dY_j = dO_j - eta Z_j G_{j+1},
+    // dV_j = eta Z_j G_{j+1}; G_j = G_{j+1} + Z_j^T dY_j
+    LAUNCH(IPTTT_K_BW_MISC, gen_snapshot<__bf16>(sl, gscr, snap_g + (K - 1) * dF, sseq, st),
+           "snapshot launch");
+    for (int64_t j = K - 1; j >= 0; --j) {
+      LAUNCH(IPTTT_K_BW_DV, bw_mse_p(sl, (int)j, bb, st), "dY launch");
+      LAUNCH(IPTTT_K_BW_SCAN,
+             mf_update_chunk(sl, (int)j, bb.zt, bb.dyt + j * Bp, sl.Lp, tstride, gscr,
+                             j > 0 ? snap_g + (j - 1) * dF : nullptr, sseq, st),
+             "backward update launch");
+    }
+    LAUNCH(IPTTT_K_BW_DZ, bw_dz(sl, bb, bb.dyt, bb.rt, st), "dZ launch");
+  }
   LAUNCH(IPTTT_K_BW_SMALL, bw_dc(sl, bb, d.proj, st), "dC launch");
   LAUNCH(IPTTT_K_BW_SMALL,
          bw_conv(sl, bb, (const __bf16 *)e, d.conv_w, grads->de, grads->dconv_w, st),

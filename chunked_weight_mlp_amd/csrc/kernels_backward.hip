@@ -161,6 +161,27 @@ struct EpiRows {
   }
 };
 
+// MSE rule, chunk at column col0: P = Z_j G_{j+1} -> dY = dO - eta P and
+// dV = eta P, both bf16 [n][d][Lp] (row n = channel), dO read from dOt.
+struct EpiMseP {
+  const __bf16 *dot;
+  __bf16 *dyt, *dvt;
+  int64_t seq_stride, Lp, col0;
+  float eta;
+  __device__ void operator()(int b1, int, int m, int n, f32x4 v) const {
+    const int64_t off = b1 * seq_stride + n * Lp + col0 + m;
+    const bf16x4 o = *(const bf16x4 *)(dot + off);
+    bf16x4 dy, dv;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      dy[r] = (__bf16)((float)o[r] - eta * v[r]);
+      dv[r] = (__bf16)(eta * v[r]);
+    }
+    *(bf16x4 *)(dyt + off) = dy;
+    *(bf16x4 *)(dvt + off) = dv;
+  }
+};
+
 // fp32 partial sums: out[b2 * s2][row][col], pitch ld (one slice of a split K).
 struct EpiRowsSplit {
   float *out;
@@ -352,7 +373,8 @@ hipError_t bw_transpose_bf16(const Slab &s, const __bf16 *in, __bf16 *out, hipSt
   return hipGetLastError();
 }
 
-hipError_t bw_dz(const Slab &s, const BwBufs &b, hipStream_t st) {
+hipError_t bw_dz(const Slab &s, const BwBufs &b, const __bf16 *a0, const __bf16 *a1,
+                 hipStream_t st) {
   const int64_t dF = (int64_t)s.d * s.F;
   GProb g{};
   g.M = s.Bp;
@@ -361,12 +383,13 @@ hipError_t bw_dz(const Slab &s, const BwBufs &b, hipStream_t st) {
   g.nb2 = s.nc;
   g.nseg = 1;
   g.nph = 2;
-  // phase 0: dO_j W_j^T (A = dOt columns of chunk j, B = S_j [d][F], both K-major)
-  g.ph[0].a = kmajor(b.dot, s.Lp, s.Bp, (int64_t)s.d * s.Lp, s.Bp);
+  // phase 0: dY_j W_j^T (A = a0 columns of chunk j, B = S_j [d][F], both K-major);
+  // dY = dO for the linear rule
+  g.ph[0].a = kmajor(a0, s.Lp, s.Bp, (int64_t)s.d * s.Lp, s.Bp);
   g.ph[0].b = kmajor(b.snap_w, s.F, s.F, (int64_t)s.nc_cap * dF, dF);
   g.ph[0].K = s.d;
-  // phase 1: (eta V_j) G_{j+1}^T
-  g.ph[1].a = kmajor(b.vt, s.Lp, s.Bp, (int64_t)s.d * s.Lp, s.Bp);
+  // phase 1: a1_j G_{j+1}^T with a1 = eta V (linear) or eta (V - O) = -eta R (MSE)
+  g.ph[1].a = kmajor(a1, s.Lp, s.Bp, (int64_t)s.d * s.Lp, s.Bp);
   g.ph[1].b = kmajor(b.snap_g, s.F, s.F, (int64_t)s.nc_cap * dF, dF);
   g.ph[1].K = s.d;
   EpiDZ e{b.at, b.ut, b.dat, b.dut, (int64_t)s.F * s.Lp, s.Lp, s.Bp};
@@ -389,6 +412,26 @@ hipError_t bw_dv(const Slab &s, const BwBufs &b, hipStream_t st) {
   g.ph[0].K = s.F;
   EpiRowsT e{b.dvt, (int64_t)s.d * s.Lp, s.Lp, s.Bp, s.eta};
   if (s.Bp < BwCfg::BM) return launch_gemm<BwSmallCfg, true, false>(g, e, st);
+  return launch_gemm<BwCfg, true, false>(g, e, st);
+}
+
+hipError_t bw_mse_p(const Slab &s, int j, const BwBufs &b, hipStream_t st) {
+  const int64_t dF = (int64_t)s.d * s.F;
+  GProb g{};
+  g.M = s.Bp;
+  g.N = s.d;
+  g.nb1 = s.n_seq;
+  g.nb2 = 1;
+  g.nseg = 1;
+  g.nph = 1;
+  // Z_j G_{j+1}: A = Zt columns of chunk j (K-major), B = T_j rows c (K-contiguous over f)
+  g.ph[0].a = kmajor(b.zt + (int64_t)j * s.Bp, s.Lp, s.Bp, (int64_t)s.F * s.Lp);
+  g.ph[0].b = kcontig(b.snap_g + (int64_t)j * dF, s.F, s.d, (int64_t)s.nc_cap * dF);
+  g.ph[0].K = s.F;
+  EpiMseP e{b.dot, b.dyt, b.dvt, (int64_t)s.d * s.Lp, s.Lp, (int64_t)j * s.Bp, s.eta};
+  const int64_t big = ((s.Bp + BwCfg::BM - 1) / BwCfg::BM) * ((s.d + BwCfg::BN - 1) / BwCfg::BN) *
+                      s.n_seq;
+  if (big < 512) return launch_gemm<BwSmallCfg, true, false>(g, e, st);
   return launch_gemm<BwCfg, true, false>(g, e, st);
 }
 

@@ -196,7 +196,7 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
     Slab s, int q0, int nq, const __bf16 *__restrict__ zt, const __bf16 *__restrict__ snap,
     int64_t snap_seq_stride, int64_t snap_group_stride, const __bf16 *__restrict__ pt,
     int64_t pt_seq_stride, float *__restrict__ o, const __bf16 *__restrict__ vt,
-    __bf16 *__restrict__ rt) {
+    __bf16 *__restrict__ rt, int64_t rt_seq_stride, int64_t rt_ld) {
   static_assert(C::SMEM_T_ELEMS * 2 <= 160 * 1024, "LDS overflow");
   static_assert(kChunkAlign % C::BK == 0, "chunk starts must be whole K steps");
   __shared__ __bf16 smem[C::SMEM_T_ELEMS];
@@ -288,7 +288,7 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
           bf16x4 rv;
 #pragma unroll
           for (int r = 0; r < 4; ++r) rv[r] = (__bf16)(valid[r] ? s.eta * ((float)v[r] - a4[r]) : 0.f);
-          *(bf16x4 *)(rt + (int64_t)n_seq * s.d * s.Bp + (int64_t)n * s.Bp + m) = rv;
+          *(bf16x4 *)(rt + n_seq * rt_seq_stride + n * rt_ld + m) = rv;
         }
       }
     }
@@ -542,20 +542,31 @@ hipError_t launch_proj(const Slab &s, const Weights &w, const WsPtrs &ws, hipStr
 // Groups of the slab: ceil(nc / G).
 inline int slab_groups(const Slab &s) { return (s.nc + s.G - 1) / s.G; }
 
+// Apply with every operand explicit: snapshot q0 + i at snap + n * snap_seq +
+// i * snap_group; residual (MSE) to rt + n * rt_seq + c * rt_ld + row.
+template <class C>
+hipError_t launch_apply_x(const Slab &s, int q0, int nq, const __bf16 *zt, const __bf16 *snap,
+                          int64_t snap_seq, int64_t snap_group, const __bf16 *pt, float *o,
+                          const __bf16 *vt, __bf16 *rt, int64_t rt_seq, int64_t rt_ld,
+                          hipStream_t st) {
+  const int64_t RG = (int64_t)s.G * s.Bp;
+  const int64_t nb = ((RG + C::BM - 1) / C::BM) * ((s.d + C::BN - 1) / C::BN) * nq * s.n_seq;
+  hipLaunchKernelGGL(k_apply<C>, dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, q0, nq, zt, snap,
+                     snap_seq, snap_group, pt, (int64_t)s.ng_cap * RG * RG, o, vt, rt, rt_seq,
+                     rt_ld);
+  return hipGetLastError();
+}
+
 template <class C>
 hipError_t launch_apply(const Slab &s, int q0, int nq, const WsPtrs &ws, float *o,
                         hipStream_t st) {
   const int64_t dF = (int64_t)s.d * s.F;
-  const int64_t RG = (int64_t)s.G * s.Bp;
   const int64_t snap_seq = s.mse ? dF : (int64_t)s.ng_cap * dF;
   const int64_t snap_group = s.mse ? 0 : dF;
   const __bf16 *snap = (const __bf16 *)ws.s + (s.mse ? 0 : (int64_t)q0 * dF);
-  const int64_t nb = ((RG + C::BM - 1) / C::BM) * ((s.d + C::BN - 1) / C::BN) * nq * s.n_seq;
-  hipLaunchKernelGGL(k_apply<C>, dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, q0, nq,
-                     (const __bf16 *)ws.zt, snap, snap_seq, snap_group,
-                     s.G > 1 ? (const __bf16 *)ws.p : nullptr, (int64_t)s.ng_cap * RG * RG, o,
-                     (const __bf16 *)ws.vt, s.mse ? (__bf16 *)ws.rt : nullptr);
-  return hipGetLastError();
+  return launch_apply_x<C>(s, q0, nq, (const __bf16 *)ws.zt, snap, snap_seq, snap_group,
+                           s.G > 1 ? (const __bf16 *)ws.p : nullptr, o, (const __bf16 *)ws.vt,
+                           s.mse ? (__bf16 *)ws.rt : nullptr, (int64_t)s.d * s.Bp, s.Bp, st);
 }
 
 template <class C>
@@ -661,6 +672,27 @@ hipError_t mf_apply(const Slab &s, int q0, int nq, const WsPtrs &ws, float *o, h
                              ((s.d + C::BN - 1) / C::BN) * (int64_t)nq * s.n_seq;
   if (big_blocks < 512) return mfma::launch_apply<mfma::ApplySmallCfg>(s, q0, nq, ws, o, st);
   return mfma::launch_apply<C>(s, q0, nq, ws, o, st);
+}
+hipError_t mf_apply_mse_chunk(const Slab &s, int j, const __bf16 *zt, const __bf16 *snap,
+                              int64_t snap_seq, const __bf16 *vt, __bf16 *rt, int64_t rt_seq,
+                              int64_t rt_ld, hipStream_t st) {
+  using C = mfma::ApplyCfg;
+  const int64_t big_blocks = ((s.Bp + C::BM - 1) / C::BM) * ((s.d + C::BN - 1) / C::BN) * s.n_seq;
+  if (big_blocks < 512)
+    return mfma::launch_apply_x<mfma::ApplySmallCfg>(s, j, 1, zt, snap, snap_seq, 0, nullptr,
+                                                     nullptr, vt, rt, rt_seq, rt_ld, st);
+  return mfma::launch_apply_x<C>(s, j, 1, zt, snap, snap_seq, 0, nullptr, nullptr, vt, rt, rt_seq,
+                                 rt_ld, st);
+}
+hipError_t mf_update_chunk(const Slab &s, int j, const __bf16 *zt, const __bf16 *bsrc,
+                           int64_t b_ld, int64_t b_seq, float *w, __bf16 *snap_after,
+                           int64_t snap_seq, hipStream_t st) {
+  using C = mfma::UpdateCfg;
+  const int64_t nb = ((s.F + C::BM - 1) / C::BM) * ((s.d + C::BN - 1) / C::BN) * s.n_seq;
+  hipLaunchKernelGGL(mfma::k_update<C>, dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, j, 1, 1, zt,
+                     bsrc, b_ld, b_seq, (int64_t)0, w, snap_after, snap_seq, (int64_t)0, 0,
+                     snap_after ? 1 : 0, 0);
+  return hipGetLastError();
 }
 hipError_t mf_gram(const Slab &s, const WsPtrs &ws, hipStream_t st) {
   return mfma::launch_gram<mfma::GramCfg>(s, ws, st);

@@ -180,8 +180,10 @@ ipttt_status ipttt_decode_step(ipttt_layer *h, const void *x, const void *e, int
  *   dw0 [d][d_ff]                           the weights, summed over the batch)
  * workspace: device scratch of ipttt_backward_workspace_bytes() bytes,
  * 256-byte aligned, exclusively the call's until it completes on the stream.
- * Supported: bf16 layers on the MFMA path with the linear rule; other layers
- * return IPTTT_E_UNSUPPORTED. Same pointer and size validation as prefill. */
+ * Both update rules; the MSE rule runs its reverse pass chunk by chunk (each
+ * chunk's dL/dW_j needs the next chunk's). Supported: bf16 layers on the MFMA
+ * path; other layers return IPTTT_E_UNSUPPORTED. Same pointer and size
+ * validation as prefill. */
 typedef struct {
   float *dx, *de;
   float *dw_gate, *dw_up;

@@ -270,8 +270,9 @@ def test_backward_workspace_bytes(lib):
     assert B.ipttt_backward_workspace_bytes(desc, 1, 129) > one
     assert B.ipttt_backward_workspace_bytes(desc, 0, 128) == 0
     assert B.ipttt_backward_workspace_bytes(desc, 1, 0) == 0
-    # only bf16 MFMA layers with the linear rule have a backward
-    for kw in (dict(update=1), dict(in_dtype=0), dict(flags=B.IPTTT_FLAG_GENERIC_KERNELS)):
+    # only bf16 layers on the MFMA path have a backward (either rule)
+    assert B.ipttt_backward_workspace_bytes(make_desc(mem, update=1), 1, 128) > one
+    for kw in (dict(in_dtype=0), dict(flags=B.IPTTT_FLAG_GENERIC_KERNELS)):
         assert B.ipttt_backward_workspace_bytes(make_desc(mem, **kw), 1, 128) == 0
 
 
@@ -312,7 +313,7 @@ def test_backward_errors_before_device_work(lib):
         assert ei.value.status == B.IPTTT_E_INVALID
     finally:
         B.ipttt_destroy(h)
-    for kw in (dict(update=1), dict(in_dtype=0)):
+    for kw in (dict(in_dtype=0), dict(flags=B.IPTTT_FLAG_GENERIC_KERNELS)):
         h = B.ipttt_init(make_desc(mem, **kw))
         try:
             with pytest.raises(B.IptttError) as ei:

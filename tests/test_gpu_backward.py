@@ -3,7 +3,7 @@ C ABI) against the float64 oracle's backward.
 
 Bar: relative Frobenius error 2e-2 per gradient (bf16 operands, fp32
 accumulation; the oracle works in float64 on the exact bf16 input values).
-Covered: both small and 4B layer shapes; chunk sizes that are and are not
+Covered: both update rules; small, 4B and 1.5B layer shapes; chunk sizes that are and are not
 multiples of 64 with ragged last chunks; two sequences; with and without an
 upstream gradient on the final fast weight. At the 32k workload's full size,
 in one call: an upstream gradient confined to the first two chunks must give
@@ -99,6 +99,40 @@ def test_backward_small_shapes(Bc, L, N, with_dwf):
     compare(to_pages(g), oracle_backward(w, weights, x, e, d_o, d_wf), f"B={Bc}")
 
 
+@pytest.mark.parametrize("Bc,L,N,with_dwf", [
+    (128, 700, 2, True),     # ragged last chunk, two sequences
+    (96, 500, 1, False),     # padding rows in every chunk
+    (512, 1100, 1, True),    # full-height tiles
+])
+def test_backward_mse_small_shapes(Bc, L, N, with_dwf):
+    """MSE rule: the reverse pass runs chunk by chunk (dY_j = dO_j - eta Z_j G_{j+1})."""
+    w = SMALL.replace(chunk=Bc, seq_len=L, n_seq=N, update="mse", eta=2e-3)
+    weights = wl.make_weights(w)
+    x, e = wl.make_inputs(w)
+    d_o, d_wf = wl.make_upstream(w)
+    if not with_dwf:
+        d_wf = None
+    say(f"[backward] mse d={w.d} F={w.d_ff} B={Bc} L={L} N={N} dW_final={with_dwf}")
+    layer = make_layer(w, weights, N)
+    g = layer.backward(x.to(DEV), e.to(DEV), d_o.to(DEV), None if d_wf is None else d_wf.to(DEV))
+    torch.cuda.synchronize()
+    compare(to_pages(g), oracle_backward(w, weights, x, e, d_o, d_wf), f"mse B={Bc}")
+
+
+def test_backward_mse_1p5b_shape():
+    """The 1.5B pretraining layer (d 2048, d_ff 8192, MSE rule): two sequences of
+    three chunks of 512 and a tail."""
+    w = wl.WORKLOADS["pretrain_1p5b_8x16k_B512_mse"].replace(seq_len=3 * 512 + 77, n_seq=2)
+    weights = wl.make_weights(w)
+    x, e = wl.make_inputs(w)
+    d_o, d_wf = wl.make_upstream(w)
+    layer = make_layer(w, weights, 2)
+    g = layer.backward(x.to(DEV), e.to(DEV), d_o.to(DEV), d_wf.to(DEV))
+    torch.cuda.synchronize()
+    say("[backward] 1.5B MSE: oracle")
+    compare(to_pages(g), oracle_backward(w, weights, x, e, d_o, d_wf), "1.5B mse")
+
+
 def test_backward_4b_shape():
     """4B-shaped layer (d 2560, d_ff 9728), four chunks of 512."""
     w = wl.WORKLOADS["qwen3_4b_L32k_B512"].replace(seq_len=2048)
@@ -157,3 +191,28 @@ def test_backward_full_size_32k():
     assert err <= TOL
     for k in ("dx", "de", "dw_gate", "dw_up", "dproj", "dconv_w"):
         assert torch.isfinite(g1[k]).all(), k
+
+
+def test_backward_full_size_pretrain_mse():
+    """The 8 x 16k / B = 512 MSE workload in one call. With dO confined to the
+    first two chunks of each sequence and no dW_final, G stays zero past them,
+    so the gradients equal the oracle's two-chunk backward and are exactly zero
+    for later tokens."""
+    w = wl.WORKLOADS["pretrain_1p5b_8x16k_B512_mse"]
+    weights = wl.make_weights(w)
+    x, e = wl.make_inputs(w)
+    d_o, _ = wl.make_upstream(w)
+    t2 = 2 * w.chunk
+    d_o2 = torch.zeros_like(d_o)
+    d_o2[:, :t2] = d_o[:, :t2]
+    layer = make_layer(w, weights, w.n_seq)
+    say("[backward] 8x16k MSE: GPU run")
+    g = layer.backward(x.to(DEV), e.to(DEV), d_o2.to(DEV), None)
+    torch.cuda.synchronize()
+    got = to_pages(g)
+    for k in ("dX", "dE"):
+        assert np.abs(got[k][:, t2:]).max() == 0.0, k
+        got[k] = got[k][:, :t2]
+    say("[backward] 8x16k MSE: oracle on the first two chunks of 8 sequences")
+    ref = oracle_backward(w, weights, x[:, :t2], e[:, :t2], d_o[:, :t2], None)
+    compare(got, ref, "8x16k mse first two chunks")
