@@ -97,21 +97,30 @@ def group_chunks(w: wl.Workload, requested: int, generic: bool) -> int:
 def kernel_work(w: wl.Workload, tokens: int, G: int = 1):
     """Algorithmic FLOPs and HBM bytes of one launch of each kernel over `tokens`
     tokens (all sequences of one pass), with one W snapshot per G chunks. Bytes
-    count each operand once. The apply counts the method's product Z W only; the
-    Gram kernel's work (and the apply's use of it) is what the chunk-parallel
-    form spends to skip snapshots, reported for its own rate."""
-    d, F, Kc = w.d, w.d_ff, w.conv_k
+    count each operand once per use the method makes of it: the linear scan
+    reads and writes each sequence's fp32 W once per pass and writes one bf16
+    copy per group; the MSE rule reads and writes W and its copy every chunk.
+    The apply counts the method's product Z W only; the Gram kernel's work (and
+    the apply's use of it) is what the chunk-parallel form spends to skip
+    snapshots, reported for its own rate."""
+    d, F, Kc, n = w.d, w.d_ff, w.conv_k, w.n_seq
     el = 2 if w.dtype == "bf16" else 4
-    chunks = -(-tokens // w.chunk)
+    chunks = -(-(tokens // n) // w.chunk)   # per sequence
     groups = -(-chunks // G)
     rows = G * (-(-w.chunk // 64) * 64)
+    W32, Wb = 4 * F * d, el * F * d         # one sequence's fp32 W and its copy
+    if w.update == "mse":
+        upd = el * tokens * (F + d) + n * chunks * (2 * W32 + Wb)
+        app = el * tokens * (F + d) + n * chunks * Wb + 4 * tokens * d
+    else:
+        upd = el * tokens * (F + d) + n * (2 * W32 + groups * Wb)
+        app = el * tokens * F + n * groups * Wb + 4 * tokens * d
     work = {
-        "gateup": (4 * d * F * tokens, el * (tokens * d + 2 * F * d + 2 * tokens * F)),
+        "gateup": (4 * d * F * tokens, el * (tokens * d + 2 * F * d + tokens * F)),
         "conv": (2 * Kc * d * tokens, el * (2 * tokens * d + Kc * d)),
         "proj": (2 * d * d * tokens, el * (2 * tokens * d + d * d)),
-        # linear scan: Z^T and V read once, W read and written once, a bf16 copy of W per group
-        "update": (2 * d * F * tokens, el * tokens * (F + d) + 8 * F * d + el * groups * F * d),
-        "apply": (2 * d * F * tokens, el * tokens * F + el * groups * F * d + 4 * tokens * d),
+        "update": (2 * d * F * tokens, upd),
+        "apply": (2 * d * F * tokens, app),
     }
     if G > 1:  # block-causal Z Z^T: about half of each group's rows x rows x F
         work["gram"] = (rows * F * tokens, el * tokens * F + el * tokens * rows // 2)
@@ -155,20 +164,26 @@ def kernel_rates(prof: dict, work: dict, steps: int, ms_total: float, passes: in
 
 def backward_work(w: wl.Workload, tokens: int):
     """Algorithmic FLOPs and HBM bytes of one launch of each backward kernel kind
-    over `tokens` tokens (all sequences). bw_small lumps dC, dProj, the conv
-    adjoint and the dW_0 sum; bw_misc the transposes and fills."""
-    d, F, Kc = w.d, w.d_ff, w.conv_k
+    over `tokens` tokens (all sequences); launches of a kind within one step
+    share the step's work equally. The recompute and the reverse pass keep one
+    bf16 W and one bf16 G per chunk; the MSE rule also reads and writes the fp32
+    state every chunk. bw_small (dC, dProj, the conv adjoint, the dW_0 sum) and
+    bw_misc (transposes, fills) are left without a model."""
+    d, F, Kc, n = w.d, w.d_ff, w.conv_k, w.n_seq
     el = 2
-    chunks = -(-tokens // w.chunk)
-    snap = el * chunks * F * d
+    chunks = -(-(tokens // n) // w.chunk)
+    W32, Wb = 4 * F * d, el * F * d
+    snaps = n * chunks * Wb
+    state = n * chunks * 2 * W32 if w.update == "mse" else n * 2 * W32
     return {
         "gateup": (4 * d * F * tokens, el * (tokens * d + 2 * F * d + 3 * tokens * F)),
         "conv": (2 * Kc * d * tokens, el * (2 * tokens * d + Kc * d)),
         "proj": (2 * d * d * tokens, el * (2 * tokens * d + d * d)),
-        "update": (2 * d * F * tokens, el * tokens * (F + d) + 8 * F * d + snap),
-        "bw_scan": (2 * d * F * tokens, el * tokens * (F + d) + 8 * F * d + snap),
-        "bw_dz": (4 * d * F * tokens, el * (2 * tokens * d + 4 * tokens * F) + 2 * snap),
-        "bw_dv": (2 * d * F * tokens, el * (tokens * F + tokens * d) + snap),
+        "update": (2 * d * F * tokens, el * tokens * (F + d) + state + snaps),
+        "apply": (2 * d * F * tokens, el * tokens * (F + d) + snaps),
+        "bw_scan": (2 * d * F * tokens, el * tokens * (F + d) + state + snaps),
+        "bw_dz": (4 * d * F * tokens, el * (2 * tokens * d + 4 * tokens * F) + 2 * snaps),
+        "bw_dv": (2 * d * F * tokens, el * (tokens * F + 2 * tokens * d) + snaps),
         "bw_dx": (4 * d * F * tokens, el * (2 * tokens * F + 2 * F * d) + 4 * tokens * d),
         "bw_dw": (4 * d * F * tokens, el * (2 * tokens * F + tokens * d) + 8 * F * d),
     }
