@@ -627,10 +627,11 @@ hipError_t launch_conv(const Slab &s, const __bf16 *e, const Weights &w, const W
 }
 static_assert(kChunkAlign % CONV_RUN == 0, "conv runs must not cross a chunk");
 
-// Block shapes, MFMA shapes and LDS row paddings chosen by timing on MI355X at
-// the 4B layer shape (d 2560, d_ff 9728, 16 chunks of 1024).
-using GateUpCfg = Cfg<2, 4, 64, 16, 16, 8, 1, 16>;
-using ProjCfg = Cfg<2, 4, 32, 16, 16, 8>;
+// Block shapes, MFMA shapes, LDS row layouts and stage-write points chosen by
+// timing on MI355X at the 4B layer shape (d 2560, d_ff 9728, 16 chunks of
+// 1024), alternating candidates within one run.
+using GateUpCfg = Cfg<2, 4, 64, 16, 0, 8, 1, 16>;           // swizzled LDS rows
+using ProjCfg = Cfg<2, 4, 64, 16, 0, 8, 1, 8, 64, 1>;       // swizzled, stage writes mid-step
 using ApplyCfg = Cfg<2, 4, 64, 16, 16, 8>;
 using ApplySmallCfg = Cfg<1, 2, 64, 16, 16, 8>;  // when ApplyCfg would leave most CUs idle
 using UpdateCfg = Cfg<1, 2, 64, 16, 16, 8, 1, 16>;

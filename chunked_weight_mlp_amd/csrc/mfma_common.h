@@ -69,9 +69,12 @@ __device__ __forceinline__ void set4(f32x16 &a, int g, f32x4 v) {
 }
 
 template <int WM_, int WN_, int BK_, int FM_ = 32, int PAD_ = 16, int PADT_ = 8, int OCC_ = 1,
-          int GM_ = 8, int WTN_ = 64>
+          int GM_ = 8, int WTN_ = 64, int MID_ = 0>
 struct Cfg {
   static constexpr int WM = WM_, WN = WN_, BK = BK_, FM = FM_;
+  // MFMA sub-steps of a K step done before the next step's LDS writes (0: all;
+  // the writes then follow the whole step's MFMAs)
+  static constexpr int MID = MID_;
   static constexpr int GM = GM_;  // row tiles per group in the tile order (tile_of)
   static constexpr int OCC = OCC_;  // waves per SIMD the register allocation must allow
   using M = Mfma<FM>;
@@ -81,6 +84,10 @@ struct Cfg {
   static constexpr int BM = WTM * WM, BN = WTN * WN;
   static constexpr int NTHR = 64 * WM * WN;
   static constexpr int PITCH = BK + PAD_;  // LDS row pitch in bf16
+  // PAD_ = 0: unpadded rows with the 16-byte pieces of row r stored XOR-permuted
+  // (piece q at slot q ^ swz(r)), so that the 16 rows one fragment read touches
+  // and the rows one stage write touches fall on distinct banks.
+  static constexpr bool SWZ = PAD_ == 0;
   static constexpr int KP = BK / 8;        // 16-byte pieces per row per step
   static constexpr int RPP = NTHR / KP;    // rows covered by one pass of all threads
   static constexpr int A_PIECES = BM / RPP;
@@ -99,6 +106,7 @@ struct Cfg {
   static constexpr int SMEM_TT_ELEMS = 2 * (AT_STAGE + BT_STAGE);
   static_assert(BK % 32 == 0 && BM % RPP == 0 && BN % RPP == 0, "bad tile config");
   static_assert(PAD_ % 8 == 0 && PADT_ % 4 == 0, "LDS rows must keep 16 / 8-byte alignment");
+  static_assert(!SWZ || (BK == 32 || BK == 64), "swizzled rows need 128 / BK rows per bank span");
   static_assert((BK * (BM / 8)) % NTHR == 0 && (BK * (BN / 8)) % NTHR == 0,
                 "bad transposed tile config");
 };
@@ -126,6 +134,20 @@ __device__ __forceinline__ void tile_of(int id, int nm, int nn, int &tm, int &tn
   tn = in / gm;
 }
 
+// LDS element offset within row `row` of K offset k (a multiple of 8) for a
+// K-contiguous operand tile: k itself, or with the 16-byte piece index XORed
+// by a function of the row (Cfg::SWZ). 128 / BK consecutive rows cover the 64
+// banks once, so the XOR key counts in units of that many rows.
+template <class C>
+__device__ __forceinline__ int kslot(int row, int k) {
+  if constexpr (C::SWZ) {
+    constexpr int rows_per_span = 128 / C::BK;
+    return k ^ (8 * ((row / rows_per_span) & (C::KP - 1)));
+  } else {
+    return k;
+  }
+}
+
 // Per-thread loader: the rows this thread copies into LDS (row (tid / KP) +
 // RPP i, 16-byte piece tid % KP). Rows outside the matrix point at a valid row
 // of it: every load is unconditional and nothing consumes the loaded value
@@ -142,25 +164,30 @@ struct Loader {
   }
   __device__ __forceinline__ void stash(__bf16 *stage, int r0, int q) const {
 #pragma unroll
-    for (int i = 0; i < NP; ++i) *(uint4 *)(stage + (r0 + C::RPP * i) * C::PITCH + 8 * q) = v[i];
+    for (int i = 0; i < NP; ++i) {
+      const int row = r0 + C::RPP * i;
+      *(uint4 *)(stage + row * C::PITCH + kslot<C>(row, 8 * q)) = v[i];
+    }
   }
 };
 
-template <class C>
+// MFMA sub-steps [U0, U1) of one LDS stage (all of them by default).
+template <class C, int U0 = 0, int U1 = C::BK / C::M::K>
 __device__ __forceinline__ void mma_stage(const __bf16 *As, const __bf16 *Bs, int arow0,
                                           const int (&brow)[C::NJ], int lane,
                                           typename C::acc_t (&acc)[C::MI][C::NJ]) {
   using M = typename C::M;
   const int r = M::orow(lane), kq = M::okoff(lane);
 #pragma unroll
-  for (int u = 0; u < C::BK / M::K; ++u) {
+  for (int u = U0; u < U1; ++u) {
     bf16x8 a[C::MI], b[C::NJ];
 #pragma unroll
     for (int j = 0; j < C::NJ; ++j)
-      b[j] = *(const bf16x8 *)(Bs + (brow[j] + r) * C::PITCH + M::K * u + kq);
+      b[j] = *(const bf16x8 *)(Bs + (brow[j] + r) * C::PITCH + kslot<C>(brow[j] + r, M::K * u + kq));
 #pragma unroll
     for (int i = 0; i < C::MI; ++i)
-      a[i] = *(const bf16x8 *)(As + (arow0 + C::FM * i + r) * C::PITCH + M::K * u + kq);
+      a[i] = *(const bf16x8 *)(As + (arow0 + C::FM * i + r) * C::PITCH +
+                               kslot<C>(arow0 + C::FM * i + r, M::K * u + kq));
 #pragma unroll
     for (int i = 0; i < C::MI; ++i)
 #pragma unroll
@@ -214,7 +241,7 @@ __device__ __forceinline__ bf16x8 frag_t(const __bf16 *tile, int pitch, int u, i
 }
 
 // TB = false: B tile row-major [BN][BK] (K-contiguous); true: K-major like A.
-template <class C, bool TB>
+template <class C, bool TB, int U0 = 0, int U1 = C::BK / C::M::K>
 __device__ __forceinline__ void mma_stage_t(const __bf16 *At, const __bf16 *Bs, int arow0,
                                             const int (&brow)[C::NJ], int lane,
                                             typename C::acc_t (&acc)[C::MI][C::NJ]) {
@@ -222,12 +249,13 @@ __device__ __forceinline__ void mma_stage_t(const __bf16 *At, const __bf16 *Bs, 
   const int r = M::orow(lane), kq = M::okoff(lane);
   const int trr = M::tr_row(lane), trc = M::tr_col(lane);
 #pragma unroll
-  for (int u = 0; u < C::BK / M::K; ++u) {
+  for (int u = U0; u < U1; ++u) {
     bf16x8 a[C::MI], b[C::NJ];
 #pragma unroll
     for (int j = 0; j < C::NJ; ++j)
       b[j] = TB ? frag_t<M>(Bs, C::PITCH_TB, u, brow[j], trr, trc)
-                : *(const bf16x8 *)(Bs + (brow[j] + r) * C::PITCH + M::K * u + kq);
+                : *(const bf16x8 *)(Bs + (brow[j] + r) * C::PITCH +
+                                    kslot<C>(brow[j] + r, M::K * u + kq));
 #pragma unroll
     for (int i = 0; i < C::MI; ++i) a[i] = frag_t<M>(At, C::PITCH_T, u, arow0 + C::FM * i, trr, trc);
 #pragma unroll
@@ -235,6 +263,13 @@ __device__ __forceinline__ void mma_stage_t(const __bf16 *At, const __bf16 *Bs, 
 #pragma unroll
       for (int j = 0; j < C::NJ; ++j) acc[i][j] = M::mma(a[i], b[j], acc[i][j]);
   }
+}
+
+// Sub-steps of a K step done before the next step's LDS writes (Cfg::MID).
+template <class C>
+constexpr int mid_step() {
+  constexpr int NU = C::BK / C::M::K;
+  return (C::MID > 0 && C::MID < NU) ? C::MID : NU;
 }
 
 // Full K loop over nk steps of BK with double-buffered LDS. Stage addresses are
@@ -258,11 +293,14 @@ __device__ __forceinline__ void kloop(__bf16 *smem, Loader<C, C::A_PIECES> &la,
       la.fetch((s + 1) * C::BK, q);
       lb.fetch((s + 1) * C::BK, q);
     }
-    mma_stage<C>(smem + cur * C::A_STAGE, Bbase + cur * C::B_STAGE, arow0, brow, lane, acc);
+    mma_stage<C, 0, mid_step<C>()>(smem + cur * C::A_STAGE, Bbase + cur * C::B_STAGE, arow0, brow,
+                                    lane, acc);
     if (s + 1 < nk) {
       la.stash(smem + (cur ^ 1) * C::A_STAGE, r0, q);
       lb.stash(Bbase + (cur ^ 1) * C::B_STAGE, r0, q);
     }
+    mma_stage<C, mid_step<C>()>(smem + cur * C::A_STAGE, Bbase + cur * C::B_STAGE, arow0, brow,
+                                lane, acc);
     __syncthreads();
   }
 }
@@ -285,12 +323,14 @@ __device__ __forceinline__ void kloop_t(__bf16 *smem, LoaderT<C, C::BM> &la,
       la.fetch((s + 1) * C::BK);
       lb.fetch((s + 1) * C::BK, q);
     }
-    mma_stage_t<C, false>(smem + cur * C::AT_STAGE, Bbase + cur * C::B_STAGE, arow0, brow, lane,
-                          acc);
+    mma_stage_t<C, false, 0, mid_step<C>()>(smem + cur * C::AT_STAGE, Bbase + cur * C::B_STAGE,
+                                             arow0, brow, lane, acc);
     if (s + 1 < nk) {
       la.stash(smem + (cur ^ 1) * C::AT_STAGE, tid);
       lb.stash(Bbase + (cur ^ 1) * C::B_STAGE, r0, q);
     }
+    mma_stage_t<C, false, mid_step<C>()>(smem + cur * C::AT_STAGE, Bbase + cur * C::B_STAGE, arow0,
+                                         brow, lane, acc);
     __syncthreads();
   }
 }
@@ -314,12 +354,14 @@ __device__ __forceinline__ void kloop_tt(__bf16 *smem, LoaderT<C, C::BM> &la,
       la.fetch((s + 1) * C::BK);
       lb.fetch((s + 1) * C::BK);
     }
-    mma_stage_t<C, true>(smem + cur * C::AT_STAGE, Bbase + cur * C::BT_STAGE, arow0, brow, lane,
-                         acc);
+    mma_stage_t<C, true, 0, mid_step<C>()>(smem + cur * C::AT_STAGE, Bbase + cur * C::BT_STAGE,
+                                            arow0, brow, lane, acc);
     if (s + 1 < nk) {
       la.stash(smem + (cur ^ 1) * C::AT_STAGE, tid);
       lb.stash(Bbase + (cur ^ 1) * C::BT_STAGE, tid);
     }
+    mma_stage_t<C, true, mid_step<C>()>(smem + cur * C::AT_STAGE, Bbase + cur * C::BT_STAGE, arow0,
+                                        brow, lane, acc);
     __syncthreads();
   }
 }
@@ -355,7 +397,7 @@ __device__ __forceinline__ void gstash(const LoaderT<C, COLS> &l, __bf16 *st, in
   l.stash(st, tid);
 }
 
-template <class C, bool TA, bool TB>
+template <class C, bool TA, bool TB, int U0 = 0, int U1 = C::BK / C::M::K>
 __device__ __forceinline__ void mma_stage_g(const __bf16 *As, const __bf16 *Bs, int arow0,
                                             const int (&brow)[C::NJ], int lane,
                                             typename C::acc_t (&acc)[C::MI][C::NJ]) {
@@ -363,16 +405,18 @@ __device__ __forceinline__ void mma_stage_g(const __bf16 *As, const __bf16 *Bs, 
   const int r = M::orow(lane), kq = M::okoff(lane);
   const int trr = M::tr_row(lane), trc = M::tr_col(lane);
 #pragma unroll
-  for (int u = 0; u < C::BK / M::K; ++u) {
+  for (int u = U0; u < U1; ++u) {
     bf16x8 a[C::MI], b[C::NJ];
 #pragma unroll
     for (int j = 0; j < C::NJ; ++j)
       b[j] = TB ? frag_t<M>(Bs, C::PITCH_TB, u, brow[j], trr, trc)
-                : *(const bf16x8 *)(Bs + (brow[j] + r) * C::PITCH + M::K * u + kq);
+                : *(const bf16x8 *)(Bs + (brow[j] + r) * C::PITCH +
+                                    kslot<C>(brow[j] + r, M::K * u + kq));
 #pragma unroll
     for (int i = 0; i < C::MI; ++i)
       a[i] = TA ? frag_t<M>(As, C::PITCH_T, u, arow0 + C::FM * i, trr, trc)
-                : *(const bf16x8 *)(As + (arow0 + C::FM * i + r) * C::PITCH + M::K * u + kq);
+                : *(const bf16x8 *)(As + (arow0 + C::FM * i + r) * C::PITCH +
+                                    kslot<C>(arow0 + C::FM * i + r, M::K * u + kq));
 #pragma unroll
     for (int i = 0; i < C::MI; ++i)
 #pragma unroll
@@ -399,11 +443,14 @@ __device__ __forceinline__ void kloop_g(__bf16 *smem, typename GLoaders<C, TA, T
       gfetch(la, (s + 1) * C::BK, q);
       gfetch(lb, (s + 1) * C::BK, q);
     }
-    mma_stage_g<C, TA, TB>(smem + cur * GL::A_ST, Bbase + cur * GL::B_ST, arow0, brow, lane, acc);
+    mma_stage_g<C, TA, TB, 0, mid_step<C>()>(smem + cur * GL::A_ST, Bbase + cur * GL::B_ST, arow0,
+                                              brow, lane, acc);
     if (s + 1 < nk) {
       gstash(la, smem + (cur ^ 1) * GL::A_ST, tid, r0, q);
       gstash(lb, Bbase + (cur ^ 1) * GL::B_ST, tid, r0, q);
     }
+    mma_stage_g<C, TA, TB, mid_step<C>()>(smem + cur * GL::A_ST, Bbase + cur * GL::B_ST, arow0,
+                                          brow, lane, acc);
     __syncthreads();
   }
 }
