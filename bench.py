@@ -243,6 +243,9 @@ def main():
                     help="default: the 128k / B = 1024 prefill; 32k / B = 512 with --backward")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward through the scan (ipttt_backward_layer) instead")
+    ap.add_argument("--decode", action="store_true",
+                    help="time token-by-token decode (ipttt_decode_step) over whole chunks")
+    ap.add_argument("--decode-batch", type=int, default=1, help="sequences decoded together")
     ap.add_argument("--slab-chunks", type=int, default=0, help="chunks per pass (0 = all)")
     ap.add_argument("--cpu-chunks", type=int, default=0,
                     help="chunks in the oracle sample (default 40; 4 with --backward)")
@@ -285,6 +288,8 @@ def main():
     w = wl.WORKLOADS[args.workload]
     if args.backward:
         return bench_backward(args, w)
+    if args.decode:
+        return bench_decode(args, w)
     dev = "cuda:0"
     t0 = time.perf_counter()
     weights = wl.make_weights(w)
@@ -450,6 +455,90 @@ def bench_backward(args, w: wl.Workload):
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle backward on the host", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline_backward(w, x, e, weights, d_o, args.cpu_chunks)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+def bench_decode(args, w: wl.Workload):
+    """One step = one whole chunk decoded token by token for `--decode-batch`
+    sequences: B calls of ipttt_decode_step, the last of which also runs the
+    chunk's update. Each call's apply reads every sequence's fp32 fast weight,
+    so the per-token cost is bound by HBM (or the 256 MB Infinity Cache, which
+    can hold one 4B-layer state)."""
+    from chunked_weight_mlp_amd import ipttt
+
+    dev = "cuda:0"
+    nb, Bc = args.decode_batch, w.chunk
+    weights = wl.make_weights(w)
+    x, e = wl.make_inputs(w, seq_len=Bc, n_seq=nb)
+    wdev = {k: v.to(dev) for k, v in weights.items()}
+    xc, ec = x.to(dev).contiguous(), e.to(dev).contiguous()
+    layer = ipttt.Layer(**wdev, chunk=Bc, eta=w.eta, update=w.update, max_batch=nb)
+    layer.reset()
+    o = torch.empty((nb, w.d), dtype=torch.float32, device=dev)
+
+    def step():
+        for pos in range(Bc):
+            layer.decode_step(xc, ec, pos, o)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        print(f"[bench] warmup {i + 1}/{args.warmup} done", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ipttt.ipttt_profile_begin(layer.handle)
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    prof = ipttt.ipttt_profile_end(layer.handle)
+    ms_total = ev0.elapsed_time(ev1)
+    tokens = nb * Bc * args.steps
+    d, F = w.d, w.d_ff
+    el = 2 if w.dtype == "bf16" else 4
+    # decode apply: every sequence's fp32 W, its z, its output row
+    n_apply, ms_apply = prof["apply"]
+    apply_bytes = nb * (4 * d * F + el * F + 4 * d)
+    ach = apply_bytes / (ms_apply / n_apply * 1e-3) / 1e9
+    kernels = {k: {"launches_per_step": n / args.steps, "avg_ms": round(ms / n, 5),
+                   "share": round(ms / max(ms_total, 1e-9), 4)} for k, (n, ms) in prof.items() if n}
+    out = {
+        "metric": "fast-weight decode tokens/s per MLP layer (one token per sequence per call)",
+        "value": round(tokens / (ms_total * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_total / args.steps, 4),
+        "ms_per_token_call": round(ms_total / (args.steps * Bc), 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded Gaussian inputs and weights)",
+        "config": {"workload": w.name, "mode": "decode", "d": d, "d_ff": F, "chunk": Bc,
+                   "batch": nb, "update": w.update, "eta": w.eta},
+        "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK, "unit": "GB/s",
+                     "frac": round(ach / HBM_PEAK, 4), "traffic": None,
+                     "algorithmic_bytes": apply_bytes, "kernel": "decode apply"},
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        from threadpoolctl import threadpool_info
+        ow = wl.to_oracle(weights)
+        t0 = time.perf_counter()
+        oracle.decode_steps(x[0].double().numpy(), e[0].double().numpy(), ow["W_g"], ow["W_u"],
+                            ow["conv_w"], ow["Proj"], ow["W_0"], w.eta, Bc, update=w.update)
+        dt = time.perf_counter() - t0
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        out["cpu_baseline"] = {"value": Bc / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                               "sample": f"decode_steps over one chunk of {Bc} tokens of one sequence, "
+                                         f"float64 numpy, {dt:.1f} s"}
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

@@ -27,6 +27,28 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// 8 consecutive elements p[k .. k+7] as floats: 16-byte vector loads when all
+// 8 are inside the row (k + 8 <= n) and p + k is 16-byte aligned, else element
+// by element (zero past n).
+template <typename T>
+__device__ __forceinline__ void load8(const T *p, int k, int n, float (&v)[8]) {
+  if (k + 8 <= n && ((uintptr_t)(p + k) & 15u) == 0) {
+    if constexpr (sizeof(T) == 2) {
+      typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+      const b8 x = *(const b8 *)(p + k);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = (float)x[q];
+    } else {
+      const float4 a = *(const float4 *)(p + k), b = *(const float4 *)(p + k + 4);
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = k + q < n ? to_f(p[k + q]) : 0.f;
+  }
+}
+
 // one wave per d_ff row f; sequences [b0, b0 + nb)
 template <typename T>
 __global__ __launch_bounds__(256) void k_dec_gateup(const T *__restrict__ x, int64_t x_stride,
@@ -40,20 +62,17 @@ __global__ __launch_bounds__(256) void k_dec_gateup(const T *__restrict__ x, int
   const T *gr = wg + (int64_t)f * d, *ur = wu + (int64_t)f * d;
   for (int k = 8 * lane; k < d; k += 8 * 64) {
     float wgv[8], wuv[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      wgv[q] = k + q < d ? to_f(gr[k + q]) : 0.f;
-      wuv[q] = k + q < d ? to_f(ur[k + q]) : 0.f;
-    }
+    load8(gr, k, d, wgv);
+    load8(ur, k, d, wuv);
 #pragma unroll
     for (int b = 0; b < MAXB; ++b) {
       if (b >= nb) break;
-      const T *xr = x + (int64_t)(b0 + b) * x_stride;
+      float xv[8];
+      load8(x + (int64_t)(b0 + b) * x_stride, k, d, xv);
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
-        const float xv = k + q < d ? to_f(xr[k + q]) : 0.f;
-        g[b] = fmaf(xv, wgv[q], g[b]);
-        u[b] = fmaf(xv, wuv[q], u[b]);
+        g[b] = fmaf(xv[q], wgv[q], g[b]);
+        u[b] = fmaf(xv[q], wuv[q], u[b]);
       }
     }
   }
@@ -65,7 +84,8 @@ __global__ __launch_bounds__(256) void k_dec_gateup(const T *__restrict__ x, int
   }
 }
 
-// one wave per (sequence b, output column c)
+// one wave per (sequence b, output column c): 8 fast-weight entries per lane
+// per step, read as two 16-byte vectors
 template <typename T>
 __global__ __launch_bounds__(256) void k_dec_apply(const T *__restrict__ z,
                                                    const float *__restrict__ w, int batch, int d,
@@ -77,11 +97,12 @@ __global__ __launch_bounds__(256) void k_dec_apply(const T *__restrict__ z,
   const float *wr = w + ((int64_t)b * d + c) * F;
   const T *zr = z + (int64_t)b * F;
   float acc = 0.f;
-  for (int f = 4 * lane; f < F; f += 4 * 64) {
+  for (int f = 8 * lane; f < F; f += 8 * 64) {
+    float wv[8], zv[8];
+    load8(wr, f, F, wv);
+    load8(zr, f, F, zv);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (f + q < F) acc = fmaf(to_f(zr[f + q]), to_f(from_f<T>(wr[f + q])), acc);
-    }
+    for (int q = 0; q < 8; ++q) acc = fmaf(zv[q], to_f(from_f<T>(wv[q])), acc);
   }
   acc = wave_sum(acc);
   if (lane == 0) o[(int64_t)b * d + c] = acc;
