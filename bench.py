@@ -23,14 +23,19 @@ import torch  # noqa: E402
 import workloads as wl  # noqa: E402
 
 METRIC = "fast-weight prefill tokens/s per MLP layer at L=128k,B=1024; % MFMA/HBM roofline"
-KERNEL_SRC = os.path.join(ROOT, "chunked_weight_mlp_amd", "csrc", "kernels_mfma.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "chunked_weight_mlp_amd", "csrc", f)
+               for f in ("kernels_mfma.hip", "mfma_common.h")]
 KERNEL_TAGS = {"gateup": "k_gateup", "conv": "k_conv", "proj": "k_proj", "update": "k_update",
                "apply": "k_apply", "gram": "k_gram", "copy": "copyBuffer"}
 
 
 def kernel_source_hash() -> str:
+    """Hash of the sources the measured kernels are built from."""
     import hashlib
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def traffic_path(workload: str) -> str:
@@ -72,8 +77,9 @@ def summarize_traffic(workload: str, fetch_csv: str, write_csv: str) -> dict:
 
 
 def load_traffic(workload: str, kernel: str):
-    """Traffic of `kernel` if a summary exists for this workload and the kernels
-    have not changed since the counters were taken; else None."""
+    """Traffic of `kernel` if a summary exists for this workload and the kernel
+    sources (kernels_mfma.hip, mfma_common.h) have not changed since the
+    counters were taken; else None."""
     path = traffic_path(workload)
     if not os.path.exists(path):
         return None
@@ -214,6 +220,15 @@ def cpu_baseline(w: wl.Workload, x, e, weights, n_chunks: int):
     }
 
 
+def packed_doc_starts(w: wl.Workload, n_docs: int):
+    """n_docs - 1 seeded document starts in (0, L): lengths drawn uniformly
+    around L / n_docs, so documents end mid-chunk."""
+    import numpy as np
+    r = np.random.default_rng(31)
+    cuts = np.sort(r.choice(np.arange(1, w.seq_len), size=n_docs - 1, replace=False))
+    return [int(c) for c in cuts]
+
+
 def trace_summary(path: str) -> str:
     """Markdown table (kernel, calls, avg / min / max ms, share) of a rocprofv3
     kernel_stats.csv, template arguments and namespaces shortened."""
@@ -246,6 +261,9 @@ def main():
     ap.add_argument("--decode", action="store_true",
                     help="time token-by-token decode (ipttt_decode_step) over whole chunks")
     ap.add_argument("--decode-batch", type=int, default=1, help="sequences decoded together")
+    ap.add_argument("--packed-docs", type=int, default=0,
+                    help="time ipttt_prefill_packed on one sequence cut into this many documents "
+                         "at seeded random positions (the fast weight resets at each)")
     ap.add_argument("--slab-chunks", type=int, default=0, help="chunks per pass (0 = all)")
     ap.add_argument("--cpu-chunks", type=int, default=0,
                     help="chunks in the oracle sample (default 40; 4 with --backward)")
@@ -304,9 +322,16 @@ def main():
                         flags=ipttt.IPTTT_FLAG_GENERIC_KERNELS if args.generic else 0)
     o = torch.empty(xd.shape, dtype=torch.float32, device=dev)
 
+    starts = packed_doc_starts(w, args.packed_docs) if args.packed_docs > 1 else None
+    if starts is not None and w.n_seq != 1:
+        sys.exit("--packed-docs needs a one-sequence workload")
+
     def step():
         layer.reset()
-        layer.prefill(xd, ed, o)
+        if starts is None:
+            layer.prefill(xd, ed, o)
+        else:
+            layer.prefill_packed(xd[0], ed[0], starts, o=o[0])
 
     for i in range(args.warmup):
         step()
@@ -338,6 +363,9 @@ def main():
         slab = slab // G * G   # the library runs whole groups per pass
     passes = -(-w.n_chunks // slab)
     tok_per_pass = w.n_seq * min(w.seq_len, slab * w.chunk)
+    if starts is not None:  # one scan per document; the model uses their mean length
+        passes = len(starts) + 1
+        tok_per_pass = w.seq_len // passes
     work = kernel_work(w, tok_per_pass, G)
     kernels, roof, dom = kernel_rates(prof, work, args.steps, ms_total, passes, w.dtype)
     # measured HBM bytes per launch (rocprofv3 counters, profiles/traffic_*.json)
@@ -358,6 +386,7 @@ def main():
         "data": "synthetic (seeded Gaussian inputs and weights of the workload's shape)",
         "config": {"workload": w.name, "d": w.d, "d_ff": w.d_ff, "seq_len": w.seq_len,
                    "chunk": w.chunk, "batch": w.n_seq, "update": w.update, "eta": w.eta,
+                   "packed_docs": args.packed_docs or 1,
                    "chunks_per_pass": slab, "chunks_per_snapshot": G,
                    "kernels": "generic" if args.generic else "mfma"},
         "tflops": round(w.flops_per_token() * tokens / (ms_step * 1e-3) / 1e12, 2),
