@@ -370,6 +370,12 @@ def main():
     kernels, roof, dom = kernel_rates(prof, work, args.steps, ms_total, passes, w.dtype)
     # measured HBM bytes per launch (rocprofv3 counters, profiles/traffic_*.json)
     roof["traffic"] = None if args.generic else load_traffic(w.name, dom)
+    # the fast-weight step on its own (apply + update, and the Gram product of
+    # chunk groups): algorithmic 4 d d_ff FLOPs per token
+    n3_ms = sum(prof[k][1] for k in ("update", "apply", "gram", "snapshot") if prof[k][0]) / args.steps
+    n3_fl = 4 * w.d * w.d_ff * tokens
+    n3 = {"ms_per_step": round(n3_ms, 4), "tflops": round(n3_fl / (n3_ms * 1e-3) / 1e12, 2),
+          "frac_of_peak": round(n3_fl / (n3_ms * 1e-3) / 1e12 / PEAK[w.dtype], 4)}
 
     out = {
         "metric": METRIC,
@@ -391,6 +397,7 @@ def main():
                    "kernels": "generic" if args.generic else "mfma"},
         "tflops": round(w.flops_per_token() * tokens / (ms_step * 1e-3) / 1e12, 2),
         "roofline": roof,
+        "fast_weight_step": n3,
         "kernels": kernels,
     }
     if not args.no_cpu_baseline:
