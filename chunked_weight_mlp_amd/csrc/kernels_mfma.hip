@@ -42,7 +42,7 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
     const __bf16 *__restrict__ wu, __bf16 *__restrict__ zt, __bf16 *__restrict__ at,
     __bf16 *__restrict__ ut) {
   static_assert(C::SMEM_ELEMS * 2 <= 160 * 1024, "LDS overflow");
-  __shared__ __bf16 smem[C::SMEM_ELEMS];
+  __shared__ __attribute__((aligned(1024))) __bf16 smem[C::SMEM_ELEMS];
   using M = typename C::M;
   constexpr int FT = C::BN / 2;  // d_ff columns per block
   const int P = s.nc * s.Bp;
@@ -53,27 +53,24 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
   int tm, tn;
   tile_of<C::GM>(id % per_seq, nm, nn, tm, tn);
   const int m0 = tm * C::BM, f0 = tn * FT;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WN, wn = wave % C::WN;
-  const int r0 = tid / C::KP;
 
-  Loader<C, C::A_PIECES> la;
-  Loader<C, C::B_PIECES> lb;
+  // A rows: the slab rows' tokens of X; B rows [0, FT): gate rows f0..,
+  // [FT, 2 FT): the matching up rows
+  DmaLoader<C, C::BM> la;
+  DmaLoader<C, C::BN> lb;
   const __bf16 *xs = x + n_seq * s.x_seq_stride;
-#pragma unroll
-  for (int i = 0; i < C::A_PIECES; ++i) {
-    const int p = m0 + r0 + C::RPP * i;
+  la.init(wave, lane, [&](int r) {
+    const int p = m0 + r;
     const int64_t t = p < P ? slab_row_token(s, p) : -1;
-    la.ptr[i] = xs + (t >= 0 ? t : 0) * s.d;
-  }
-  // B rows [0, FT): gate rows f0.., [FT, 2 FT): the matching up rows
-#pragma unroll
-  for (int i = 0; i < C::B_PIECES; ++i) {
-    const int rr = r0 + C::RPP * i;
+    return xs + (t >= 0 ? t : 0) * s.d;
+  });
+  lb.init(wave, lane, [&](int rr) {
     const int f = f0 + (rr < FT ? rr : rr - FT);
-    const bool ok = f < s.F;
-    lb.ptr[i] = (rr < FT ? wg : wu) + (int64_t)(ok ? f : 0) * s.d;
-  }
+    return (rr < FT ? wg : wu) + (int64_t)(f < s.F ? f : 0) * s.d;
+  });
   // a wave's first NJ/2 B tiles are gate rows, the other NJ/2 the matching up rows
   constexpr int HJ = C::NJ / 2;
   constexpr int WF = C::WTN / 2;  // d_ff columns per wave
@@ -85,7 +82,8 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
   }
   typename C::acc_t acc[C::MI][C::NJ];
   zero_acc<C>(acc);
-  kloop<C>(smem, la, lb, s.d / C::BK, tid, wm * C::WTM, brow, acc);
+  kloop_dma<C, 2>(smem, la, lb, s.d / C::BK, wave, lane, wm * C::WTM, brow, acc,
+                  [](int st, int64_t &ka, int64_t &kb) { ka = kb = (int64_t)st * C::BK; });
 
   __bf16 *zts = zt + (int64_t)n_seq * s.F * s.Lp;
 #pragma unroll
@@ -133,7 +131,7 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
     Slab s, const __bf16 *__restrict__ c, const __bf16 *__restrict__ proj,
     __bf16 *__restrict__ vt, float scale) {
   static_assert(C::SMEM_ELEMS * 2 <= 160 * 1024, "LDS overflow");
-  __shared__ __bf16 smem[C::SMEM_ELEMS];
+  __shared__ __attribute__((aligned(1024))) __bf16 smem[C::SMEM_ELEMS];
   using M = typename C::M;
   const int P = s.nc * s.Bp;
   const int nm = (P + C::BM - 1) / C::BM, nn = (s.d + C::BN - 1) / C::BN;
@@ -143,28 +141,21 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
   int tm, tn;
   tile_of<C::GM>(id % per_seq, nm, nn, tm, tn);
   const int m0 = tm * C::BM, n0 = tn * C::BN;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WN, wn = wave % C::WN;
-  const int r0 = tid / C::KP;
-  Loader<C, C::A_PIECES> la;
-  Loader<C, C::B_PIECES> lb;
+  DmaLoader<C, C::BM> la;
+  DmaLoader<C, C::BN> lb;
   const __bf16 *cs = c + (int64_t)n_seq * s.Lp * s.d;
-#pragma unroll
-  for (int i = 0; i < C::A_PIECES; ++i) {
-    const int p = m0 + r0 + C::RPP * i;
-    la.ptr[i] = cs + (int64_t)(p < P ? p : 0) * s.d;
-  }
-#pragma unroll
-  for (int i = 0; i < C::B_PIECES; ++i) {
-    const int n = n0 + r0 + C::RPP * i;
-    lb.ptr[i] = proj + (int64_t)(n < s.d ? n : 0) * s.d;
-  }
+  la.init(wave, lane, [&](int r) { return cs + (int64_t)(m0 + r < P ? m0 + r : 0) * s.d; });
+  lb.init(wave, lane, [&](int r) { return proj + (int64_t)(n0 + r < s.d ? n0 + r : 0) * s.d; });
   int brow[C::NJ];
 #pragma unroll
   for (int j = 0; j < C::NJ; ++j) brow[j] = wn * C::WTN + C::FM * j;
   typename C::acc_t acc[C::MI][C::NJ];
   zero_acc<C>(acc);
-  kloop<C>(smem, la, lb, s.d / C::BK, tid, wm * C::WTM, brow, acc);
+  kloop_dma<C, 2>(smem, la, lb, s.d / C::BK, wave, lane, wm * C::WTM, brow, acc,
+                  [](int st, int64_t &ka, int64_t &kb) { ka = kb = (int64_t)st * C::BK; });
 
   __bf16 *vts = vt + (int64_t)n_seq * s.d * s.Lp;
 #pragma unroll
@@ -378,7 +369,7 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
     float *__restrict__ w, __bf16 *__restrict__ snap, int64_t snap_seq_stride,
     int64_t snap_group_stride, int snap_each_group, int snap_after, int reverse) {
   static_assert(C::SMEM_ELEMS * 2 <= 160 * 1024, "LDS overflow");
-  __shared__ __bf16 smem[C::SMEM_ELEMS];
+  __shared__ __attribute__((aligned(1024))) __bf16 smem[C::SMEM_ELEMS];
   using M = typename C::M;
   const int nm = (s.F + C::BM - 1) / C::BM, nn = (s.d + C::BN - 1) / C::BN;
   const int per_seq = nm * nn;
@@ -387,9 +378,9 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
   int tm, tn;
   tile_of<C::GM>(id % per_seq, nm, nn, tm, tn);
   const int f0 = tm * C::BM, c0 = tn * C::BN;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WN, wn = wave % C::WN;
-  const int r0 = tid / C::KP;
   const int64_t dF = (int64_t)s.d * s.F;
   float *ws = w + n_seq * dF;
 
@@ -407,7 +398,7 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
              (f < s.F && c < s.d) ? *(const f32x4 *)(ws + (int64_t)c * s.F + f)
                                   : f32x4{0.f, 0.f, 0.f, 0.f});
       }
-  auto write_snap = [&](__bf16 *dst) {
+  auto write_snap = [&](__bf16 *dst) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < C::MI; ++i)
 #pragma unroll
@@ -426,32 +417,33 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
         }
   };
 
-  Loader<C, C::A_PIECES> la;
-  Loader<C, C::B_PIECES> lb;
+  // A rows: Zt rows f (token-contiguous); B rows: bsrc rows c. One K loop over
+  // every step of the chunks; step st is K step r of chunk jc (walked last to
+  // first when reverse).
+  const __bf16 *zts = zt + (int64_t)n_seq * s.F * s.Lp;
+  const __bf16 *bs = bsrc + n_seq * b_seq_stride;
+  DmaLoader<C, C::BM> la;
+  DmaLoader<C, C::BN> lb;
+  la.init(wave, lane, [&](int r) { return zts + (int64_t)(f0 + r < s.F ? f0 + r : 0) * s.Lp; });
+  lb.init(wave, lane, [&](int r) { return bs + (int64_t)(c0 + r < s.d ? c0 + r : 0) * b_ld; });
   int brow[C::NJ];
 #pragma unroll
   for (int jj = 0; jj < C::NJ; ++jj) brow[jj] = wn * C::WTN + C::FM * jj;
-  const int steps = s.Bp / C::BK;
-  const __bf16 *zts = zt + (int64_t)n_seq * s.F * s.Lp;
-  const __bf16 *bs = bsrc + n_seq * b_seq_stride;
-  for (int it = 0; it < n_chunks; it += G) {
-    const int jc = reverse ? n_chunks - 1 - it : it;
-    const int j = j_first + jc;
-    const int nch = min(G, n_chunks - jc);
-    if (snap_each_group)
-      write_snap(snap + n_seq * snap_seq_stride + (int64_t)(jc / G) * snap_group_stride);
-#pragma unroll
-    for (int i = 0; i < C::A_PIECES; ++i) {
-      const int f = f0 + r0 + C::RPP * i;
-      la.ptr[i] = zts + (int64_t)(f < s.F ? f : 0) * s.Lp + (int64_t)j * s.Bp;
-    }
-#pragma unroll
-    for (int i = 0; i < C::B_PIECES; ++i) {
-      const int c = c0 + r0 + C::RPP * i;
-      lb.ptr[i] = bs + (int64_t)(c < s.d ? c : 0) * b_ld + jc * b_chunk_stride;
-    }
-    kloop<C>(smem, la, lb, nch * steps, tid, wm * C::WTM, brow, acc);
-  }
+  const int spc = s.Bp / C::BK;  // K steps per chunk
+  const int spg = G * spc;       // K steps per group
+  auto koff = [&](int st, int64_t &ka, int64_t &kb) __attribute__((always_inline)) {
+    const int q = st / spc, r = st - q * spc;
+    const int jc = reverse ? n_chunks - 1 - q : q;
+    ka = (int64_t)(j_first + jc) * s.Bp + r * C::BK;
+    kb = (int64_t)jc * b_chunk_stride + r * C::BK;
+  };
+  auto pre = [&](int st) __attribute__((always_inline)) {
+    if (!snap_each_group || st % spg) return;
+    const int q = st / spg;  // reverse walks single chunks (G = 1)
+    const int g = reverse ? n_chunks - 1 - q : q;
+    write_snap(snap + n_seq * snap_seq_stride + (int64_t)g * snap_group_stride);
+  };
+  kloop_dma_pl<C, 2>(smem, la, lb, n_chunks * spc, wave, lane, wm * C::WTM, brow, acc, koff, pre);
   if (snap_after) write_snap(snap + n_seq * snap_seq_stride);
 #pragma unroll
   for (int i = 0; i < C::MI; ++i)
@@ -630,11 +622,11 @@ static_assert(kChunkAlign % CONV_RUN == 0, "conv runs must not cross a chunk");
 // Block shapes, MFMA shapes, LDS row layouts and stage-write points chosen by
 // timing on MI355X at the 4B layer shape (d 2560, d_ff 9728, 16 chunks of
 // 1024), alternating candidates within one run.
-using GateUpCfg = Cfg<2, 4, 64, 16, 0, 8, 1, 16>;           // swizzled LDS rows
-using ProjCfg = Cfg<2, 4, 64, 16, 0, 8, 1, 8, 64, 1>;       // swizzled, stage writes mid-step
+using GateUpCfg = Cfg<2, 4, 64, 16, 0, 8, 1, 16>;  // direct LDS copies, swizzled rows
+using ProjCfg = Cfg<2, 4, 64, 16, 0, 8, 1, 8>;     // direct LDS copies, swizzled rows
 using ApplyCfg = Cfg<2, 4, 64, 16, 16, 8>;
 using ApplySmallCfg = Cfg<1, 2, 64, 16, 16, 8>;  // when ApplyCfg would leave most CUs idle
-using UpdateCfg = Cfg<1, 2, 64, 16, 16, 8, 1, 16>;
+using UpdateCfg = Cfg<1, 2, 64, 16, 0, 8, 1, 16>;  // direct copies, pipelined fragments
 using GramCfg = Cfg<2, 4, 64, 16, 16, 8>;
 static_assert(kChunkAlign % UpdateCfg::BK == 0, "chunk pitch must be whole update K steps");
 // The Gram computes, per m tile, the columns the apply's m tiles read: its m

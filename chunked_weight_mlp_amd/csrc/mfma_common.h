@@ -455,6 +455,212 @@ __device__ __forceinline__ void kloop_g(__bf16 *smem, typename GLoaders<C, TA, T
   }
 }
 
+// ---- direct global -> LDS loads (K-contiguous operands, swizzled rows) -------
+// global_load_lds_dwordx4 moves 16 bytes per lane from global memory into LDS
+// at a wave-uniform base + 16 x lane without passing through registers, so the
+// K loop needs no staging registers and no LDS write instructions. The copies
+// are counted by vmcnt; the loops below wait for them explicitly (vector
+// memory loads complete in issue order) and then pass a block barrier.
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void gbl_cvoid_t;
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+// The memory clobber keeps LDS reads of the landed stage below it.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Block barrier after this wave's LDS reads have completed: after it no wave
+// still reads a stage that the next copies overwrite.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Copies ROWS rows x BK elements of one operand per stage. One instruction
+// fills 1 KB = RPI rows; instruction i of wave w fills rows (i NW + w) RPI ..
+// + RPI. Lane l writes row (l / KP), LDS slot (l % KP); the swizzled layout
+// puts logical piece kslot(row, slot) there (the XOR is its own inverse), so
+// the lane loads that piece. Rows outside the matrix point at a valid row
+// (masked at the epilogue, as with the register loaders).
+template <class C, int ROWS>
+struct DmaLoader {
+  static constexpr int NW = C::NTHR / 64;
+  static constexpr int RPI = 512 / C::BK;
+  static constexpr int NI = ROWS / (RPI * NW);  // instructions per wave per stage
+  static_assert(C::SWZ, "direct LDS copies need unpadded (swizzled) rows");
+  static_assert(ROWS % (RPI * NW) == 0, "rows must split evenly over the waves");
+  const __bf16 *ptr[NI];  // this lane's source at K offset 0
+  // rowptr(r): start of tile row r (K offset 0)
+  template <class RowPtr>
+  __device__ __forceinline__ void init(int wave, int lane, RowPtr rowptr) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int row = (i * NW + wave) * RPI + lane / C::KP;
+      ptr[i] = rowptr(row) + kslot<C>(row, 8 * (lane % C::KP));
+    }
+  }
+  // wave must be wave-uniform (readfirstlane), as the LDS base is
+  __device__ __forceinline__ void issue(__bf16 *stage, int wave, int64_t koff) const {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      __builtin_amdgcn_global_load_lds((gbl_cvoid_t *)(ptr[i] + koff),
+                                       (lds_void_t *)(stage + (i * NW + wave) * RPI * C::BK), 16, 0,
+                                       0);
+  }
+};
+
+// K loop over nk steps with NS LDS stages filled by direct copies, NS - 1
+// steps ahead. koff(s, ka, kb) gives the element offsets of step s along the
+// A and B rows. One barrier per step.
+template <class C, int NS, class Koff>
+__device__ __forceinline__ void kloop_dma(__bf16 *smem, const DmaLoader<C, C::BM> &la,
+                                          const DmaLoader<C, C::BN> &lb, int nk, int wave,
+                                          int lane, int arow0, const int (&brow)[C::NJ],
+                                          typename C::acc_t (&acc)[C::MI][C::NJ], Koff koff) {
+  constexpr int AS = C::BM * C::BK, ST = AS + C::BN * C::BK;
+  constexpr int IPW = DmaLoader<C, C::BM>::NI + DmaLoader<C, C::BN>::NI;
+  int64_t ka, kb;
+#pragma unroll
+  for (int p = 0; p < NS - 1; ++p)
+    if (p < nk) {
+      koff(p, ka, kb);
+      la.issue(smem + p * ST, wave, ka);
+      lb.issue(smem + p * ST + AS, wave, kb);
+    }
+  int cur = 0, nxt = NS - 1;
+  for (int s = 0; s < nk; ++s) {
+    if (s + NS - 2 < nk)
+      wait_vm<(NS - 2) * IPW>();  // step s landed; later steps may be in flight
+    else
+      wait_vm<0>();
+    lds_barrier();
+    if (s + NS - 1 < nk) {
+      koff(s + NS - 1, ka, kb);
+      la.issue(smem + nxt * ST, wave, ka);
+      lb.issue(smem + nxt * ST + AS, wave, kb);
+    }
+    mma_stage<C>(smem + cur * ST, smem + cur * ST + AS, arow0, brow, lane, acc);
+    cur = cur + 1 == NS ? 0 : cur + 1;
+    nxt = nxt + 1 == NS ? 0 : nxt + 1;
+  }
+  lds_barrier();  // the stages are free for a following loop
+}
+
+// The operand fragments of one MFMA sub-step (K = M::K) of a stage.
+template <class C>
+struct Frags {
+  bf16x8 a[C::MI], b[C::NJ];
+};
+template <class C>
+__device__ __forceinline__ void load_frags(const __bf16 *As, const __bf16 *Bs, int u, int arow0,
+                                           const int (&brow)[C::NJ], int lane, Frags<C> &f) {
+  using M = typename C::M;
+  const int r = M::orow(lane), kq = M::okoff(lane);
+#pragma unroll
+  for (int j = 0; j < C::NJ; ++j)
+    f.b[j] = *(const bf16x8 *)(Bs + (brow[j] + r) * C::PITCH +
+                               kslot<C>(brow[j] + r, M::K * u + kq));
+#pragma unroll
+  for (int i = 0; i < C::MI; ++i)
+    f.a[i] = *(const bf16x8 *)(As + (arow0 + C::FM * i + r) * C::PITCH +
+                               kslot<C>(arow0 + C::FM * i + r, M::K * u + kq));
+}
+template <class C>
+__device__ __forceinline__ void mma_frags(const Frags<C> &f,
+                                          typename C::acc_t (&acc)[C::MI][C::NJ]) {
+  using M = typename C::M;
+#pragma unroll
+  for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+    for (int j = 0; j < C::NJ; ++j) acc[i][j] = M::mma(f.a[i], f.b[j], acc[i][j]);
+}
+// An asm statement that reads f: the compiler waits for f's loads before it.
+// After a direct LDS copy the compiler's next LDS wait drains every LDS read
+// in flight; placed where f is known to have landed, this absorbs that wait,
+// so the MFMAs that follow do not also wait for the next prefetch.
+template <class C>
+__device__ __forceinline__ void touch(const Frags<C> &f) {
+#pragma unroll
+  for (int i = 0; i < C::MI; ++i) asm volatile("" ::"v"(f.a[i]));
+#pragma unroll
+  for (int j = 0; j < C::NJ; ++j) asm volatile("" ::"v"(f.b[j]));
+}
+
+// Software-pipelined K loop for one wave per SIMD (no other wave hides LDS
+// latency): the fragments of sub-step u + 1 load while sub-step u's MFMAs run,
+// and the barrier sits between a stage's last fragment loads and its last
+// MFMAs, so the next stage's first fragments load behind those. NS stages are
+// filled by direct copies NS steps ahead; pre(s) runs before step s's MFMAs
+// (the accumulators then hold steps 0 .. s - 1). sched_barrier keeps each
+// prefetch ahead of the MFMAs it overlaps.
+template <class C, int NS, class Koff, class Pre>
+__device__ __forceinline__ void kloop_dma_pl(__bf16 *smem, const DmaLoader<C, C::BM> &la,
+                                             const DmaLoader<C, C::BN> &lb, int nk, int wave,
+                                             int lane, int arow0, const int (&brow)[C::NJ],
+                                             typename C::acc_t (&acc)[C::MI][C::NJ], Koff koff,
+                                             Pre pre) {
+  constexpr int NU = C::BK / C::M::K;
+  static_assert(NU >= 2, "two or more MFMA sub-steps per stage");
+  constexpr int AS = C::BM * C::BK, ST = AS + C::BN * C::BK;
+  constexpr int IPW = DmaLoader<C, C::BM>::NI + DmaLoader<C, C::BN>::NI;
+  int64_t ka, kb;
+#pragma unroll
+  for (int p = 0; p < NS; ++p)
+    if (p < nk) {
+      koff(p, ka, kb);
+      la.issue(smem + p * ST, wave, ka);
+      lb.issue(smem + p * ST + AS, wave, kb);
+    }
+  if (NS - 1 < nk)
+    wait_vm<(NS - 1) * IPW>();
+  else
+    wait_vm<0>();
+  lds_barrier();
+  Frags<C> f[2];
+  load_frags<C>(smem, smem + AS, 0, arow0, brow, lane, f[0]);
+  // keep this load apart from the loop's prefetch (the compiler would
+  // otherwise merge the two into one load at the loop head)
+#pragma unroll
+  for (int i = 0; i < C::MI; ++i) asm volatile("" : "+v"(f[0].a[i]));
+#pragma unroll
+  for (int j = 0; j < C::NJ; ++j) asm volatile("" : "+v"(f[0].b[j]));
+  int cur = 0;
+  for (int s = 0; s < nk; ++s) {
+    const __bf16 *st = smem + cur * ST;
+#pragma unroll
+    for (int u = 0; u + 1 < NU; ++u) {
+      touch<C>(f[u & 1]);
+      load_frags<C>(st, st + AS, u + 1, arow0, brow, lane, f[(u + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (u == 0) pre(s);
+      mma_frags<C>(f[u & 1], acc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (s + NS - 1 < nk)
+      wait_vm<(NS - 2) * IPW>();  // step s + 1 landed
+    else
+      wait_vm<0>();
+    lds_barrier();
+    touch<C>(f[(NU - 1) & 1]);
+    if (s + NS < nk) {  // refill this step's stage
+      koff(s + NS, ka, kb);
+      la.issue(smem + cur * ST, wave, ka);
+      lb.issue(smem + cur * ST + AS, wave, kb);
+    }
+    cur = cur + 1 == NS ? 0 : cur + 1;
+    // the next step's first fragments (after the last step: an unused read of
+    // a valid stage)
+    load_frags<C>(smem + cur * ST, smem + cur * ST + AS, 0, arow0, brow, lane, f[NU & 1]);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_frags<C>(f[(NU - 1) & 1], acc);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  lds_barrier();
+}
+
 // Token of slab row p (slab rows fit in 32 bits), or -1 for a padding row.
 __device__ __forceinline__ int64_t slab_row_token(const Slab &s, int p) {
   const int j = p / s.Bp, i = p - j * s.Bp;
