@@ -82,8 +82,12 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
   }
   typename C::acc_t acc[C::MI][C::NJ];
   zero_acc<C>(acc);
-  kloop_dma<C, 2>(smem, la, lb, s.d / C::BK, wave, lane, wm * C::WTM, brow, acc,
-                  [](int st, int64_t &ka, int64_t &kb) { ka = kb = (int64_t)st * C::BK; });
+  kloop_dma<2>(
+      smem, la, lb, s.d / C::BK, wave,
+      [](int st, int64_t &ka, int64_t &kb) { ka = kb = (int64_t)st * C::BK; },
+      [&](const __bf16 *As, const __bf16 *Bs) {
+        mma_stage<C>(As, Bs, wm * C::WTM, brow, lane, acc);
+      });
 
   __bf16 *zts = zt + (int64_t)n_seq * s.F * s.Lp;
 #pragma unroll
@@ -154,8 +158,12 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
   for (int j = 0; j < C::NJ; ++j) brow[j] = wn * C::WTN + C::FM * j;
   typename C::acc_t acc[C::MI][C::NJ];
   zero_acc<C>(acc);
-  kloop_dma<C, 2>(smem, la, lb, s.d / C::BK, wave, lane, wm * C::WTM, brow, acc,
-                  [](int st, int64_t &ka, int64_t &kb) { ka = kb = (int64_t)st * C::BK; });
+  kloop_dma<2>(
+      smem, la, lb, s.d / C::BK, wave,
+      [](int st, int64_t &ka, int64_t &kb) { ka = kb = (int64_t)st * C::BK; },
+      [&](const __bf16 *As, const __bf16 *Bs) {
+        mma_stage<C>(As, Bs, wm * C::WTM, brow, lane, acc);
+      });
 
   __bf16 *vts = vt + (int64_t)n_seq * s.d * s.Lp;
 #pragma unroll
@@ -431,19 +439,90 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
   for (int jj = 0; jj < C::NJ; ++jj) brow[jj] = wn * C::WTN + C::FM * jj;
   const int spc = s.Bp / C::BK;  // K steps per chunk
   const int spg = G * spc;       // K steps per group
-  auto koff = [&](int st, int64_t &ka, int64_t &kb) __attribute__((always_inline)) {
-    const int q = st / spc, r = st - q * spc;
-    const int jc = reverse ? n_chunks - 1 - q : q;
-    ka = (int64_t)(j_first + jc) * s.Bp + r * C::BK;
-    kb = (int64_t)jc * b_chunk_stride + r * C::BK;
+  // koff is called for steps 0, 1, 2, ... in order: walk (chunk, step) counters
+  int kq = 0, kr = 0;
+  auto koff = [&](int, int64_t &ka, int64_t &kb) __attribute__((always_inline)) {
+    const int jc = reverse ? n_chunks - 1 - kq : kq;
+    ka = (int64_t)(j_first + jc) * s.Bp + kr * C::BK;
+    kb = (int64_t)jc * b_chunk_stride + kr * C::BK;
+    if (++kr == spc) {
+      kr = 0;
+      ++kq;
+    }
   };
-  auto pre = [&](int st) __attribute__((always_inline)) {
-    if (!snap_each_group || st % spg) return;
-    const int q = st / spg;  // reverse walks single chunks (G = 1)
-    const int g = reverse ? n_chunks - 1 - q : q;
-    write_snap(snap + n_seq * snap_seq_stride + (int64_t)g * snap_group_stride);
+  // Per-group snapshots: at the group's first K step the tile is rounded to
+  // bf16 into registers (NSP pieces of 4 values per lane); the pieces then go
+  // out in NSLOT slots at evenly spaced steps of the group (after the step's
+  // barrier), so the copies stream out behind the MFMAs instead of stalling
+  // every block at the same step. A slot holds the PPS row tiles i of one
+  // column tile jj: whole 128-byte lines of the d_ff-contiguous snapshot rows.
+  // Slots a short last group has not reached are stored after the loop;
+  // groups of fewer than NSLOT steps store the whole tile at their first step.
+  constexpr int NSP = C::MI * C::NJ * M::NG, NSLOT = 8, PPS = NSP / NSLOT;
+  static_assert(M::NG == 1 && C::MI % PPS == 0 && C::NJ * (C::MI / PPS) == NSLOT,
+                "snapshot slots must be whole column tiles of PPS row tiles");
+  uint2 sbuf[NSP];
+  __bf16 *sdst = snap + n_seq * snap_seq_stride;  // the pending snapshot
+  const int fl = f0 + wm * C::WTM + M::rrow(lane, 0), cl = c0 + wn * C::WTN + M::rcol(lane);
+  auto store_piece = [&](int q) __attribute__((always_inline)) {
+    const int i = q / (C::NJ * M::NG), jj = q / M::NG % C::NJ, g = q % M::NG;
+    const int f = fl + C::FM * i + M::rrow(lane, g) - M::rrow(lane, 0);
+    const int c = cl + C::FM * jj;
+    if (f < s.F && c < s.d) *(uint2 *)(sdst + (int64_t)c * s.F + f) = sbuf[q];
   };
-  kloop_dma_pl<C, 2>(smem, la, lb, n_chunks * spc, wave, lane, wm * C::WTM, brow, acc, koff, pre);
+  auto slot_piece = [](int k, int e) { return ((k / C::NJ) * PPS + e) * C::NJ + k % C::NJ; };
+  auto store_slot = [&](int slot) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < NSLOT; ++k)
+      if (slot == k)
+#pragma unroll
+        for (int e = 0; e < PPS; ++e) store_piece(slot_piece(k, e));
+  };
+  int gr = 0, gq = 0;            // K step within the group, group (walk order)
+  int nslot = NSLOT, nstep = 0;  // next slot to store and the group step it is due at
+  auto pre = [&](int) __attribute__((always_inline)) {
+    if (!snap_each_group || gr != 0) return;
+    const int g = reverse ? n_chunks - 1 - gq : gq;  // reverse walks single chunks (G = 1)
+    sdst = snap + n_seq * snap_seq_stride + (int64_t)g * snap_group_stride;
+#pragma unroll
+    for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+      for (int jj = 0; jj < C::NJ; ++jj)
+#pragma unroll
+        for (int g2 = 0; g2 < M::NG; ++g2) {
+          const f32x4 a4 = get4(acc[i][jj], g2);
+          bf16x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (__bf16)a4[e];
+          sbuf[(i * C::NJ + jj) * M::NG + g2] = __builtin_bit_cast(uint2, v);
+        }
+    if (spg >= NSLOT) {
+      nslot = 0;
+      nstep = 0;
+    } else {
+#pragma unroll
+      for (int q = 0; q < NSP; ++q) store_piece(q);
+    }
+  };
+  auto post = [&](int) __attribute__((always_inline)) {
+    if (!snap_each_group) return;
+    if (nslot < NSLOT && gr == nstep) {
+      store_slot(nslot);
+      ++nslot;
+      nstep = nslot * spg / NSLOT;
+    }
+    if (++gr == spg) {
+      gr = 0;
+      ++gq;
+    }
+  };
+  const int nk = n_chunks * spc;
+  kloop_dma_pl<C, 2>(smem, la, lb, nk, wave, lane, wm * C::WTM, brow, acc, koff, pre, post);
+#pragma unroll
+  for (int k = 0; k < NSLOT; ++k)
+    if (k >= nslot)
+#pragma unroll
+      for (int e = 0; e < PPS; ++e) store_piece(slot_piece(k, e));
   if (snap_after) write_snap(snap + n_seq * snap_seq_stride);
 #pragma unroll
   for (int i = 0; i < C::MI; ++i)

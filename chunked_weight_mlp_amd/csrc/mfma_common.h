@@ -257,7 +257,8 @@ __device__ __forceinline__ void mma_stage_t(const __bf16 *At, const __bf16 *Bs, 
                 : *(const bf16x8 *)(Bs + (brow[j] + r) * C::PITCH +
                                     kslot<C>(brow[j] + r, M::K * u + kq));
 #pragma unroll
-    for (int i = 0; i < C::MI; ++i) a[i] = frag_t<M>(At, C::PITCH_T, u, arow0 + C::FM * i, trr, trc);
+    for (int i = 0; i < C::MI; ++i)
+      a[i] = frag_t<M>(At, C::PITCH_T, u, arow0 + C::FM * i, trr, trc);
 #pragma unroll
     for (int i = 0; i < C::MI; ++i)
 #pragma unroll
@@ -492,6 +493,7 @@ struct DmaLoader {
   static constexpr int NI = ROWS / (RPI * NW);  // instructions per wave per stage
   static_assert(C::SWZ, "direct LDS copies need unpadded (swizzled) rows");
   static_assert(ROWS % (RPI * NW) == 0, "rows must split evenly over the waves");
+  static constexpr int STAGE = ROWS * C::BK;  // elements per stage
   const __bf16 *ptr[NI];  // this lane's source at K offset 0
   // rowptr(r): start of tile row r (K offset 0)
   template <class RowPtr>
@@ -512,16 +514,14 @@ struct DmaLoader {
   }
 };
 
-// K loop over nk steps with NS LDS stages filled by direct copies, NS - 1
-// steps ahead. koff(s, ka, kb) gives the element offsets of step s along the
-// A and B rows. One barrier per step.
-template <class C, int NS, class Koff>
-__device__ __forceinline__ void kloop_dma(__bf16 *smem, const DmaLoader<C, C::BM> &la,
-                                          const DmaLoader<C, C::BN> &lb, int nk, int wave,
-                                          int lane, int arow0, const int (&brow)[C::NJ],
-                                          typename C::acc_t (&acc)[C::MI][C::NJ], Koff koff) {
-  constexpr int AS = C::BM * C::BK, ST = AS + C::BN * C::BK;
-  constexpr int IPW = DmaLoader<C, C::BM>::NI + DmaLoader<C, C::BN>::NI;
+// K loop over nk steps with NS LDS stages (A then B) filled by direct copies,
+// NS - 1 steps ahead. koff(s, ka, kb) gives step s's element offsets for the A
+// and B sources; mma(As, Bs) runs one stage. One barrier per step.
+template <int NS, class LA, class LB, class Koff, class Mma>
+__device__ __forceinline__ void kloop_dma(__bf16 *smem, const LA &la, const LB &lb, int nk,
+                                          int wave, Koff koff, Mma mma) {
+  constexpr int AS = LA::STAGE, ST = LA::STAGE + LB::STAGE;
+  constexpr int IPW = LA::NI + LB::NI;
   int64_t ka, kb;
 #pragma unroll
   for (int p = 0; p < NS - 1; ++p)
@@ -542,7 +542,7 @@ __device__ __forceinline__ void kloop_dma(__bf16 *smem, const DmaLoader<C, C::BM
       la.issue(smem + nxt * ST, wave, ka);
       lb.issue(smem + nxt * ST + AS, wave, kb);
     }
-    mma_stage<C>(smem + cur * ST, smem + cur * ST + AS, arow0, brow, lane, acc);
+    mma(smem + cur * ST, smem + cur * ST + AS);
     cur = cur + 1 == NS ? 0 : cur + 1;
     nxt = nxt + 1 == NS ? 0 : nxt + 1;
   }
@@ -594,14 +594,16 @@ __device__ __forceinline__ void touch(const Frags<C> &f) {
 // and the barrier sits between a stage's last fragment loads and its last
 // MFMAs, so the next stage's first fragments load behind those. NS stages are
 // filled by direct copies NS steps ahead; pre(s) runs before step s's MFMAs
-// (the accumulators then hold steps 0 .. s - 1). sched_barrier keeps each
-// prefetch ahead of the MFMAs it overlaps.
-template <class C, int NS, class Koff, class Pre>
+// (the accumulators then hold steps 0 .. s - 1) and post(s) after step s's
+// barrier, ahead of the next copies (the next step's vmcnt wait covers any
+// global stores it issues). sched_barrier keeps each prefetch ahead of the
+// MFMAs it overlaps.
+template <class C, int NS, class Koff, class Pre, class Post>
 __device__ __forceinline__ void kloop_dma_pl(__bf16 *smem, const DmaLoader<C, C::BM> &la,
                                              const DmaLoader<C, C::BN> &lb, int nk, int wave,
                                              int lane, int arow0, const int (&brow)[C::NJ],
                                              typename C::acc_t (&acc)[C::MI][C::NJ], Koff koff,
-                                             Pre pre) {
+                                             Pre pre, Post post) {
   constexpr int NU = C::BK / C::M::K;
   static_assert(NU >= 2, "two or more MFMA sub-steps per stage");
   constexpr int AS = C::BM * C::BK, ST = AS + C::BN * C::BK;
@@ -645,6 +647,7 @@ __device__ __forceinline__ void kloop_dma_pl(__bf16 *smem, const DmaLoader<C, C:
       wait_vm<0>();
     lds_barrier();
     touch<C>(f[(NU - 1) & 1]);
+    post(s);
     if (s + NS < nk) {  // refill this step's stage
       koff(s + NS, ka, kb);
       la.issue(smem + cur * ST, wave, ka);
