@@ -701,7 +701,7 @@ static_assert(kChunkAlign % CONV_RUN == 0, "conv runs must not cross a chunk");
 // Block shapes, MFMA shapes, LDS row layouts and stage-write points chosen by
 // timing on MI355X at the 4B layer shape (d 2560, d_ff 9728, 16 chunks of
 // 1024), alternating candidates within one run.
-using GateUpCfg = Cfg<2, 4, 64, 16, 0, 8, 1, 16>;  // direct LDS copies, swizzled rows
+using GateUpCfg = Cfg<2, 4, 64, 16, 0, 8, 1, 4>;   // direct LDS copies, swizzled rows
 using ProjCfg = Cfg<2, 4, 64, 16, 0, 8, 1, 8>;     // direct LDS copies, swizzled rows
 using ApplyCfg = Cfg<2, 4, 64, 16, 16, 8>;
 using ApplySmallCfg = Cfg<1, 2, 64, 16, 16, 8>;  // when ApplyCfg would leave most CUs idle
