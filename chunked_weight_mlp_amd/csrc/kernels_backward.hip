@@ -48,7 +48,7 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
     GProb g, Epi epi) {
   using GL = GLoaders<C, TA, TB>;
   static_assert(GL::SMEM * 2 <= 160 * 1024, "LDS overflow");
-  __shared__ __bf16 smem[GL::SMEM];
+  __shared__ __attribute__((aligned(1024))) __bf16 smem[GL::SMEM];
   using M = typename C::M;
   const int nm = (g.M + C::BM - 1) / C::BM, nn = (g.N + C::BN - 1) / C::BN;
   const int per = nm * nn;
@@ -74,6 +74,21 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
     for (int sg = 0; sg < g.nseg; ++sg) {
       const __bf16 *pa = A.p + b1 * A.s1 + b2 * A.s2 + sg * A.sseg;
       const __bf16 *pb = Bo.p + b1 * Bo.s1 + b2 * Bo.s2 + sg * Bo.sseg;
+      if constexpr (!TA && !TB && C::SWZ) {
+        // both operands K-contiguous: direct LDS copies into swizzled rows
+        const int wv = __builtin_amdgcn_readfirstlane(wave);
+        DmaLoader<C, C::BM> da;
+        DmaLoader<C, C::BN> db;
+        da.init(wv, lane, [&](int r) { return pa + min((int64_t)m0 + r, A.lim - 1) * A.ld; });
+        db.init(wv, lane, [&](int r) { return pb + min((int64_t)n0 + r, Bo.lim - 1) * Bo.ld; });
+        kloop_dma<2>(
+            smem, da, db, g.ph[ph].K / C::BK, wv,
+            [](int st, int64_t &ka, int64_t &kb) { ka = kb = (int64_t)st * C::BK; },
+            [&](const __bf16 *As, const __bf16 *Bs) {
+              mma_stage<C>(As, Bs, wm * C::WTM, brow, lane, acc);
+            });
+        continue;
+      }
       if constexpr (TA) {
         la.ld = A.ld;
 #pragma unroll
@@ -218,6 +233,7 @@ hipError_t launch_gemm(const GProb &g, const Epi &epi, hipStream_t st) {
 
 using BwCfg = Cfg<2, 4, 64, 16, 16, 8>;
 using BwSmallCfg = Cfg<1, 2, 64, 16, 16, 8>;  // chunk-batched problems with short chunks
+using BwNTCfg = Cfg<2, 4, 64, 16, 0, 8>;       // both operands K-contiguous: direct copies
 
 // ---- elementwise / vector kernels --------------------------------------------
 
@@ -484,7 +500,7 @@ hipError_t bw_dw(const Slab &s, const BwBufs &b, float *dwg, float *dwu, hipStre
   g.ph[0].b = kcontig(b.xt, s.Lp, s.d, 0, 0, (int64_t)s.d * s.Lp);
   g.ph[0].K = (int)s.Lp;
   EpiRows e{dwg, dwu, 0, s.d};
-  return launch_gemm<BwCfg, false, false>(g, e, st);
+  return launch_gemm<BwNTCfg, false, false>(g, e, st);
 }
 
 int bw_dproj_splits(const Slab &s) {
