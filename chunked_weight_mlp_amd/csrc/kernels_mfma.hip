@@ -4,13 +4,16 @@
 // wave grid, the K step, the MFMA shape and the wave tile (Cfg): WM x WN
 // waves, each computing a 128 x WTN output tile from FM x FM MFMA tiles
 // (v_mfma_f32_32x32x16_bf16 or v_mfma_f32_16x16x32_bf16), so a block covers
-// (128 WM) x (WTN WN). K is staged through LDS BK at a time in two buffers;
-// the global loads of step s+1 are in flight while step s runs on MFMA. Both
-// operands are K-contiguous in memory ("NT"): a lane's MFMA operand is 8
-// consecutive K values (one 16-byte LDS read). LDS rows are padded (PAD
-// elements) so that the fragment reads of consecutive lanes, which walk down
-// consecutive rows, spread over the banks; shapes and paddings were picked by
-// timing on MI355X.
+// (128 WM) x (WTN WN). K is staged through LDS BK at a time in two buffers,
+// the next step's copies in flight while a step runs on MFMA. gate/up, proj
+// and the update fill the buffers with direct global-to-LDS copies into
+// unpadded rows whose 16-byte pieces are XOR-swizzled (kslot); the update,
+// one wave per SIMD, also prefetches each MFMA sub-step's fragments into
+// registers behind the previous sub-step. The apply and the Gram stage
+// through registers into padded rows (PAD / PADT elements). A K-contiguous
+// operand gives each lane 8 consecutive K values with one 16-byte LDS read; a
+// K-major one is read with ds_read_b64_tr_b16. Shapes, paddings and staging
+// were picked by timing on MI355X.
 //
 // Kernels:
 //   k_gateup   Z = SiLU(X W_g) * (X W_u)   M = slab rows, N = d_ff (half the
@@ -25,9 +28,10 @@
 //   k_gram     P^T = block-causal Z_q Z_q^T of each group (G > 1), both
 //              operands read transposed; only the tiles the apply reads.
 //   k_update   W^T tile (BM d_ff rows x BN d columns, fp32) held in the
-//              accumulators across the chunks of a slab: per group of G
-//              chunks, optionally write the bf16 snapshot S_q, then
-//              accumulate Zt . Vt over the group's tokens.
+//              accumulators across the chunks of a slab, one K loop over all
+//              of them: per group of G chunks, optionally the bf16 snapshot
+//              S_q (streamed out over the group's K steps), then Zt . Vt
+//              over the group's tokens.
 //   k_conv     depthwise conv of E, vector loads, sliding window.
 
 #include "mfma_common.h"

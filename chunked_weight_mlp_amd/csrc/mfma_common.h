@@ -1,9 +1,11 @@
 // MFMA building blocks shared by the bf16 kernels (gfx950 / CDNA4): MFMA tile
-// shapes and their lane maps, the block configuration Cfg, global -> LDS
-// loaders for K-contiguous and K-major (transposed) operands, one LDS stage of
-// MFMAs for each operand layout, the double-buffered K loops, XCD-aware block
-// numbering and the slab row -> token map. Device code only; included by the
-// .hip files that build kernels from these pieces.
+// shapes and their lane maps, the block configuration Cfg, register-staged
+// global -> LDS loaders for K-contiguous and K-major (transposed) operands and
+// direct global -> LDS copies for K-contiguous ones, one LDS stage of MFMAs for
+// each operand layout, the double-buffered K loops (register-staged, direct
+// copies, direct copies with pipelined fragments), XCD-aware block numbering
+// and the slab row -> token map. Device code only; included by the .hip files
+// that build kernels from these pieces.
 #pragma once
 
 #include <type_traits>
@@ -273,39 +275,12 @@ constexpr int mid_step() {
   return (C::MID > 0 && C::MID < NU) ? C::MID : NU;
 }
 
-// Full K loop over nk steps of BK with double-buffered LDS. Stage addresses are
-// formed arithmetically from the __shared__ base so the compiler keeps them in
-// the LDS address space (ds_read / ds_write, not flat).
-template <class C>
-__device__ __forceinline__ void kloop(__bf16 *smem, Loader<C, C::A_PIECES> &la,
-                                      Loader<C, C::B_PIECES> &lb, int nk, int tid, int arow0,
-                                      const int (&brow)[C::NJ],
-                                      typename C::acc_t (&acc)[C::MI][C::NJ]) {
-  __bf16 *const Bbase = smem + 2 * C::A_STAGE;
-  const int lane = tid & 63, r0 = tid / C::KP, q = tid % C::KP;
-  la.fetch(0, q);
-  lb.fetch(0, q);
-  la.stash(smem, r0, q);
-  lb.stash(Bbase, r0, q);
-  __syncthreads();
-  for (int s = 0; s < nk; ++s) {
-    const int cur = s & 1;
-    if (s + 1 < nk) {
-      la.fetch((s + 1) * C::BK, q);
-      lb.fetch((s + 1) * C::BK, q);
-    }
-    mma_stage<C, 0, mid_step<C>()>(smem + cur * C::A_STAGE, Bbase + cur * C::B_STAGE, arow0, brow,
-                                    lane, acc);
-    if (s + 1 < nk) {
-      la.stash(smem + (cur ^ 1) * C::A_STAGE, r0, q);
-      lb.stash(Bbase + (cur ^ 1) * C::B_STAGE, r0, q);
-    }
-    mma_stage<C, mid_step<C>()>(smem + cur * C::A_STAGE, Bbase + cur * C::B_STAGE, arow0, brow,
-                                lane, acc);
-    __syncthreads();
-  }
-}
-
+// Register-staged K loops over nk steps of BK with double-buffered LDS: the
+// next step's global loads go to registers before this step's MFMAs and to
+// LDS after them (or after MID sub-steps). Stage addresses are formed
+// arithmetically from the __shared__ base so the compiler keeps them in the
+// LDS address space (ds_read / ds_write, not flat).
+// A K-major (transposed) operand and a K-contiguous B operand (the apply):
 template <class C>
 __device__ __forceinline__ void kloop_t(__bf16 *smem, LoaderT<C, C::BM> &la,
                                         Loader<C, C::B_PIECES> &lb, int nk, int tid, int arow0,
