@@ -10,6 +10,7 @@ the launch stream during the timed steps.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -90,6 +91,52 @@ def load_traffic(workload: str, kernel: str):
     return None if b is None else b["total"]
 PEAK = {"bf16": 2500.0, "f32": 157.3}  # dense TFLOP/s (MFMA bf16, fp32)
 HBM_PEAK = 8000.0                       # GB/s
+
+
+def achievable_peaks() -> dict:
+    """The chip's achievable rates, measured here by the library's micro-benchmarks
+    (ipttt_probe): bf16 MFMA issue at two waves per SIMD for each MFMA shape, with
+    no memory traffic, and a streaming read of 4 GiB (more than the caches hold).
+    Best of a few launches, HIP events on the launch stream."""
+    from chunked_weight_mlp_amd import ipttt
+    dev = "cuda:0"
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    out_buf = torch.empty(1 << 20, dtype=torch.float32, device=dev)
+    nbytes = 4 << 30
+    src = torch.zeros(nbytes // 4, dtype=torch.float32, device=dev)
+
+    def best(kind, n, a, reps=4):
+        rates = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            work = ipttt.ipttt_probe(kind, n, a, ctypes.c_void_p(out_buf.data_ptr()),
+                                     out_buf.numel() * 4, sp)
+            e1.record(stream)
+            e1.synchronize()
+            rates.append(work / (e0.elapsed_time(e1) * 1e-3))
+        return max(rates)
+
+    m16 = best(ipttt.IPTTT_PROBE_MFMA16, 20000, None) / 1e12
+    m32 = best(ipttt.IPTTT_PROBE_MFMA32, 20000, None) / 1e12
+    rd = best(ipttt.IPTTT_PROBE_READ, nbytes, ctypes.c_void_p(src.data_ptr())) / 1e9
+    del src
+    return {"mfma16_bf16_tflops": round(m16, 1), "mfma32_bf16_tflops": round(m32, 1),
+            "mfma_bf16_tflops": round(max(m16, m32), 1), "hbm_read_gbps": round(rd, 1),
+            "source": "ipttt_probe micro-benchmarks on this GPU"}
+
+
+def achievable_fracs(ach: dict, roof: dict, n3_tflops=None) -> dict:
+    """The dominant kernel (and the fast-weight step) against the measured rates."""
+    if roof["unit"] == "TFLOP/s":
+        dom = roof["achieved"] / ach["mfma_bf16_tflops"]
+    else:
+        dom = roof["achieved"] / ach["hbm_read_gbps"]
+    out = dict(ach, dominant_frac=round(dom, 4))
+    if n3_tflops is not None:
+        out["fast_weight_step_frac"] = round(n3_tflops / ach["mfma_bf16_tflops"], 4)
+    return out
 
 
 def group_chunks(w: wl.Workload, requested: int, generic: bool) -> int:
@@ -268,6 +315,8 @@ def main():
     ap.add_argument("--cpu-chunks", type=int, default=0,
                     help="chunks in the oracle sample (default 40; 4 with --backward)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probe", action="store_true",
+                    help="skip the achievable-peak micro-benchmarks")
     ap.add_argument("--generic", action="store_true", help="generic FMA kernels instead of MFMA")
     ap.add_argument("--group-chunks", type=int, default=0,
                     help="chunks per W snapshot of the linear scan (0 = library choice, 1 = plain)")
@@ -400,6 +449,8 @@ def main():
         "fast_weight_step": n3,
         "kernels": kernels,
     }
+    if not args.no_probe:
+        out["achievable"] = achievable_fracs(achievable_peaks(), roof, n3["tflops"])
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, x, e, weights, args.cpu_chunks)
@@ -488,6 +539,8 @@ def bench_backward(args, w: wl.Workload):
         "roofline": roof,
         "kernels": kernels,
     }
+    if not args.no_probe:
+        out["achievable"] = achievable_fracs(achievable_peaks(), out["roofline"])
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle backward on the host", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline_backward(w, x, e, weights, d_o, args.cpu_chunks)
@@ -563,6 +616,8 @@ def bench_decode(args, w: wl.Workload):
                      "algorithmic_bytes": apply_bytes, "kernel": "decode apply"},
         "kernels": kernels,
     }
+    if not args.no_probe:
+        out["achievable"] = achievable_fracs(achievable_peaks(), out["roofline"])
     if not args.no_cpu_baseline:
         import oracle
         from threadpoolctl import threadpool_info

@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libipttt.so")
 SOURCES = ["ipttt.cpp", "kernels_generic.hip", "kernels_mfma.hip", "kernels_decode.hip",
-           "kernels_backward.hip"]
+           "kernels_backward.hip", "probe.hip"]
 ARCH = "gfx950"
 
 

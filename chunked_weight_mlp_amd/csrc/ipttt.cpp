@@ -275,6 +275,18 @@ ipttt_status ipttt_profile_end(ipttt_layer *h, int32_t *launches, double *ms) {
   return st;
 }
 
+ipttt_status ipttt_probe(int32_t kind, int64_t n, const void *src, void *dst, size_t dst_bytes,
+                         double *work, void *hip_stream) {
+  if (kind != IPTTT_PROBE_MFMA16 && kind != IPTTT_PROBE_MFMA32 && kind != IPTTT_PROBE_READ)
+    return fail(IPTTT_E_INVALID, "unknown probe kind %d", kind);
+  if (!dst || !work || n < 1) return fail(IPTTT_E_INVALID, "dst and work must be non-NULL, n >= 1");
+  if (kind == IPTTT_PROBE_READ && !src) return fail(IPTTT_E_INVALID, "read probe needs src");
+  const hipError_t e =
+      ipttt::probe_launch(kind, n, src, dst, dst_bytes, work, (hipStream_t)hip_stream);
+  if (e == hipErrorInvalidValue) return fail(IPTTT_E_INVALID, "probe buffers do not fit");
+  return hip_status(e, "probe launch");
+}
+
 ipttt_status ipttt_reset_fast_weights(ipttt_layer *h, int32_t first_seq, int32_t n_seq,
                                       void *hip_stream) {
   if (!h) return fail(IPTTT_E_INVALID, "handle is NULL");

@@ -30,9 +30,12 @@ IPTTT_FLAG_GENERIC_KERNELS = 1
 EXPORTS = (
     "ipttt_workspace_bytes", "ipttt_init", "ipttt_prefill_layer", "ipttt_prefill_packed",
     "ipttt_decode_step", "ipttt_backward_workspace_bytes", "ipttt_backward_layer",
-    "ipttt_reset_fast_weights", "ipttt_profile_begin", "ipttt_profile_end", "ipttt_destroy",
-    "ipttt_status_str", "ipttt_last_error",
+    "ipttt_reset_fast_weights", "ipttt_profile_begin", "ipttt_profile_end", "ipttt_probe",
+    "ipttt_destroy", "ipttt_status_str", "ipttt_last_error",
 )
+IPTTT_PROBE_MFMA16 = 0
+IPTTT_PROBE_MFMA32 = 1
+IPTTT_PROBE_READ = 2
 
 KERNELS = ("gateup", "conv", "proj", "update", "apply", "snapshot", "gram",  # ipttt_kernel order
            "bw_scan", "bw_dz", "bw_dv", "bw_dx", "bw_dw", "bw_small", "bw_misc")
@@ -107,6 +110,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ipttt_profile_begin.restype = ctypes.c_int
     lib.ipttt_profile_end.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_double)]
     lib.ipttt_profile_end.restype = ctypes.c_int
+    lib.ipttt_probe.argtypes = [i32, i64, vp, vp, ctypes.c_size_t, ctypes.POINTER(ctypes.c_double), vp]
+    lib.ipttt_probe.restype = ctypes.c_int
     lib.ipttt_destroy.argtypes = [vp]
     lib.ipttt_destroy.restype = None
     lib.ipttt_status_str.argtypes = [ctypes.c_int]
@@ -193,6 +198,14 @@ def ipttt_reset_fast_weights(h, first_seq: int, n_seq: int, stream=None) -> None
 
 def ipttt_profile_begin(h) -> None:
     _check(load().ipttt_profile_begin(h))
+
+
+def ipttt_probe(kind: int, n: int, src, dst, dst_bytes: int, stream=None) -> float:
+    """Enqueues one micro-benchmark launch (measurement only); returns its FLOPs
+    (MFMA probes) or bytes read (read probe)."""
+    work = ctypes.c_double(0.0)
+    _check(load().ipttt_probe(kind, n, src, dst, dst_bytes, ctypes.byref(work), stream))
+    return work.value
 
 
 def ipttt_profile_end(h) -> dict:

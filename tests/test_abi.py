@@ -323,3 +323,16 @@ def test_backward_errors_before_device_work(lib):
             B.ipttt_destroy(h)
     assert lib.ipttt_backward_layer(None, None, None, None, None, 1, 1, None, None, 0, None) == \
         B.IPTTT_E_INVALID
+
+
+def test_probe_errors_before_device_work(lib):
+    """The measurement probes reject bad arguments before touching the device."""
+    mem = FakeMem()
+    buf = mem.ptr()
+    for kind, n, src, dst, work_ok in ((7, 10, None, buf, True),     # unknown kind
+                                       (B.IPTTT_PROBE_MFMA16, 0, None, buf, True),   # n < 1
+                                       (B.IPTTT_PROBE_MFMA32, 10, None, None, True),  # no dst
+                                       (B.IPTTT_PROBE_READ, 16, None, buf, True),    # read without src
+                                       (B.IPTTT_PROBE_MFMA16, 10, None, buf, False)):  # no work
+        work = ctypes.byref(ctypes.c_double()) if work_ok else None
+        assert lib.ipttt_probe(kind, n, src, dst, 1 << 20, work, None) == B.IPTTT_E_INVALID
