@@ -40,7 +40,7 @@ namespace ipttt {
 namespace mfma {
 
 // ---------------------------------------------------------------------------
-template <class C>
+template <class C, bool PL = false>
 __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC))) void k_gateup(
     Slab s, const __bf16 *__restrict__ x, const __bf16 *__restrict__ wg,
     const __bf16 *__restrict__ wu, __bf16 *__restrict__ zt, __bf16 *__restrict__ at,
@@ -86,12 +86,14 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
   }
   typename C::acc_t acc[C::MI][C::NJ];
   zero_acc<C>(acc);
-  kloop_dma<2>(
-      smem, la, lb, s.d / C::BK, wave,
-      [](int st, int64_t &ka, int64_t &kb) { ka = kb = (int64_t)st * C::BK; },
-      [&](const __bf16 *As, const __bf16 *Bs) {
-        mma_stage<C>(As, Bs, wm * C::WTM, brow, lane, acc);
-      });
+  const auto koff = [](int st, int64_t &ka, int64_t &kb) { ka = kb = (int64_t)st * C::BK; };
+  if constexpr (PL)
+    kloop_dma_pl<C, 2, true>(smem, la, lb, s.d / C::BK, wave, lane, wm * C::WTM, brow, acc, koff,
+                       [](int) {}, [](int) {});
+  else
+    kloop_dma<2>(smem, la, lb, s.d / C::BK, wave, koff, [&](const __bf16 *As, const __bf16 *Bs) {
+      mma_stage<C>(As, Bs, wm * C::WTM, brow, lane, acc);
+    });
 
   __bf16 *zts = zt + (int64_t)n_seq * s.F * s.Lp;
 #pragma unroll
@@ -134,7 +136,7 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
 }
 
 // ---------------------------------------------------------------------------
-template <class C>
+template <class C, bool PL = false>
 __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC))) void k_proj(
     Slab s, const __bf16 *__restrict__ c, const __bf16 *__restrict__ proj,
     __bf16 *__restrict__ vt, float scale) {
@@ -162,12 +164,14 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
   for (int j = 0; j < C::NJ; ++j) brow[j] = wn * C::WTN + C::FM * j;
   typename C::acc_t acc[C::MI][C::NJ];
   zero_acc<C>(acc);
-  kloop_dma<2>(
-      smem, la, lb, s.d / C::BK, wave,
-      [](int st, int64_t &ka, int64_t &kb) { ka = kb = (int64_t)st * C::BK; },
-      [&](const __bf16 *As, const __bf16 *Bs) {
-        mma_stage<C>(As, Bs, wm * C::WTM, brow, lane, acc);
-      });
+  const auto koff = [](int st, int64_t &ka, int64_t &kb) { ka = kb = (int64_t)st * C::BK; };
+  if constexpr (PL)
+    kloop_dma_pl<C, 2, true>(smem, la, lb, s.d / C::BK, wave, lane, wm * C::WTM, brow, acc, koff,
+                       [](int) {}, [](int) {});
+  else
+    kloop_dma<2>(smem, la, lb, s.d / C::BK, wave, koff, [&](const __bf16 *As, const __bf16 *Bs) {
+      mma_stage<C>(As, Bs, wm * C::WTM, brow, lane, acc);
+    });
 
   __bf16 *vts = vt + (int64_t)n_seq * s.d * s.Lp;
 #pragma unroll
@@ -521,7 +525,7 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
     }
   };
   const int nk = n_chunks * spc;
-  kloop_dma_pl<C, 2>(smem, la, lb, nk, wave, lane, wm * C::WTM, brow, acc, koff, pre, post);
+  kloop_dma_pl<C, 2, false>(smem, la, lb, nk, wave, lane, wm * C::WTM, brow, acc, koff, pre, post);
 #pragma unroll
   for (int k = 0; k < NSLOT; ++k)
     if (k >= nslot)
@@ -595,21 +599,21 @@ __global__ __launch_bounds__(256) void k_conv(Slab s, const __bf16 *__restrict__
 }
 
 // ---- launchers (templated on the block configuration) ---------------------
-template <class C>
+template <class C, bool PL = false>
 hipError_t launch_gateup(const Slab &s, const __bf16 *x, const Weights &w, const WsPtrs &ws,
                          hipStream_t st, __bf16 *at = nullptr, __bf16 *ut = nullptr) {
   const int64_t P = (int64_t)s.nc * s.Bp;
   const int64_t nb = ((P + C::BM - 1) / C::BM) * ((s.F + C::BN / 2 - 1) / (C::BN / 2)) * s.n_seq;
-  hipLaunchKernelGGL(k_gateup<C>, dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, x,
+  hipLaunchKernelGGL((k_gateup<C, PL>), dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, x,
                      (const __bf16 *)w.w_gate, (const __bf16 *)w.w_up, (__bf16 *)ws.zt, at, ut);
   return hipGetLastError();
 }
 
-template <class C>
+template <class C, bool PL = false>
 hipError_t launch_proj(const Slab &s, const Weights &w, const WsPtrs &ws, hipStream_t st) {
   const int64_t P = (int64_t)s.nc * s.Bp;
   const int64_t nb = ((P + C::BM - 1) / C::BM) * ((s.d + C::BN - 1) / C::BN) * s.n_seq;
-  hipLaunchKernelGGL(k_proj<C>, dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, (const __bf16 *)ws.c,
+  hipLaunchKernelGGL((k_proj<C, PL>), dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, (const __bf16 *)ws.c,
                      (const __bf16 *)w.proj, (__bf16 *)ws.vt, s.mse ? 1.f : s.eta);
   return hipGetLastError();
 }
@@ -737,10 +741,10 @@ hipError_t mf_conv(const Slab &s, const __bf16 *e, const Weights &w, const WsPtr
 }
 hipError_t mf_gateup(const Slab &s, const __bf16 *x, const Weights &w, const WsPtrs &ws,
                      hipStream_t st) {
-  return mfma::launch_gateup<mfma::GateUpCfg>(s, x, w, ws, st);
+  return mfma::launch_gateup<mfma::GateUpCfg, true>(s, x, w, ws, st);
 }
 hipError_t mf_proj(const Slab &s, const Weights &w, const WsPtrs &ws, hipStream_t st) {
-  return mfma::launch_proj<mfma::ProjCfg>(s, w, ws, st);
+  return mfma::launch_proj<mfma::ProjCfg, true>(s, w, ws, st);
 }
 hipError_t mf_apply(const Slab &s, int q0, int nq, const WsPtrs &ws, float *o, hipStream_t st) {
   using C = mfma::ApplyCfg;
@@ -781,7 +785,7 @@ hipError_t mf_update_one(const Slab &s, int j, const WsPtrs &ws, float *w_state,
 }
 hipError_t mf_gateup_pre(const Slab &s, const __bf16 *x, const Weights &w, const WsPtrs &ws,
                          __bf16 *at, __bf16 *ut, hipStream_t st) {
-  return mfma::launch_gateup<mfma::GateUpCfg>(s, x, w, ws, st, at, ut);
+  return mfma::launch_gateup<mfma::GateUpCfg, true>(s, x, w, ws, st, at, ut);
 }
 hipError_t mf_update_reverse(const Slab &s, const __bf16 *zt, const __bf16 *bt, float *g,
                              __bf16 *snap, hipStream_t st) {

@@ -564,16 +564,40 @@ __device__ __forceinline__ void touch(const Frags<C> &f) {
   for (int j = 0; j < C::NJ; ++j) asm volatile("" ::"v"(f.b[j]));
 }
 
-// Software-pipelined K loop for one wave per SIMD (no other wave hides LDS
-// latency): the fragments of sub-step u + 1 load while sub-step u's MFMAs run,
-// and the barrier sits between a stage's last fragment loads and its last
-// MFMAs, so the next stage's first fragments load behind those. NS stages are
-// filled by direct copies NS steps ahead; pre(s) runs before step s's MFMAs
-// (the accumulators then hold steps 0 .. s - 1) and post(s) after step s's
-// barrier, ahead of the next copies (the next step's vmcnt wait covers any
-// global stores it issues). sched_barrier keeps each prefetch ahead of the
-// MFMAs it overlaps.
-template <class C, int NS, class Koff, class Pre, class Post>
+// Scheduling pattern for one MFMA sub-step: NV direct copies, then ND LDS
+// fragment reads, each issued between two of the NM MFMAs, so that the issue of
+// the memory instructions hides under MFMA execution instead of delaying the
+// first MFMA (all waves leave a barrier together, so no other wave has MFMAs
+// ready to fill that gap). Applies to the scheduling region it ends.
+template <int NV, int ND, int NM>
+__device__ __forceinline__ void interleave_mfma() {
+  static_assert(NV + ND <= NM, "more memory instructions than MFMAs to hide them");
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // VMEM
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+  }
+#pragma unroll
+  for (int k = 0; k < ND; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, NM - NV - ND, 0);
+}
+
+// Software-pipelined K loop: the fragments of sub-step u + 1 load while
+// sub-step u's MFMAs run, and the barrier sits between a stage's last fragment
+// loads and its last MFMAs, so the next stage's first fragments and the
+// refill of the stage just consumed load behind those MFMAs. NS stages are
+// filled by direct copies NS steps ahead; the last NS steps (no refill) run as
+// a peeled tail, so every step of the main loop is one straight block. IL:
+// the copies and fragment reads are interleaved with the MFMAs (two waves per
+// SIMD, where all waves leave each barrier together); otherwise they are all
+// issued ahead of the MFMAs (one wave per SIMD, measured faster there).
+// pre(s) runs before step s's MFMAs (the accumulators then hold steps
+// 0 .. s - 1) and post(s) after step s's barrier, ahead of the refill (the
+// next step's vmcnt wait covers any global stores it issues).
+template <class C, int NS, bool IL, class Koff, class Pre, class Post>
 __device__ __forceinline__ void kloop_dma_pl(__bf16 *smem, const DmaLoader<C, C::BM> &la,
                                              const DmaLoader<C, C::BN> &lb, int nk, int wave,
                                              int lane, int arow0, const int (&brow)[C::NJ],
@@ -583,6 +607,7 @@ __device__ __forceinline__ void kloop_dma_pl(__bf16 *smem, const DmaLoader<C, C:
   static_assert(NU >= 2, "two or more MFMA sub-steps per stage");
   constexpr int AS = C::BM * C::BK, ST = AS + C::BN * C::BK;
   constexpr int IPW = DmaLoader<C, C::BM>::NI + DmaLoader<C, C::BN>::NI;
+  constexpr int NFR = C::MI + C::NJ, NMF = C::MI * C::NJ;
   int64_t ka, kb;
 #pragma unroll
   for (int p = 0; p < NS; ++p)
@@ -605,15 +630,17 @@ __device__ __forceinline__ void kloop_dma_pl(__bf16 *smem, const DmaLoader<C, C:
 #pragma unroll
   for (int j = 0; j < C::NJ; ++j) asm volatile("" : "+v"(f[0].b[j]));
   int cur = 0;
-  for (int s = 0; s < nk; ++s) {
+  const auto step = [&](int s, auto refill) __attribute__((always_inline)) {
+    constexpr bool RF = decltype(refill)::value;
     const __bf16 *st = smem + cur * ST;
 #pragma unroll
     for (int u = 0; u + 1 < NU; ++u) {
       touch<C>(f[u & 1]);
       load_frags<C>(st, st + AS, u + 1, arow0, brow, lane, f[(u + 1) & 1]);
-      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (!IL) __builtin_amdgcn_sched_barrier(0);
       if (u == 0) pre(s);
       mma_frags<C>(f[u & 1], acc);
+      if constexpr (IL) interleave_mfma<0, NFR, NMF>();
       __builtin_amdgcn_sched_barrier(0);
     }
     if (s + NS - 1 < nk)
@@ -623,7 +650,7 @@ __device__ __forceinline__ void kloop_dma_pl(__bf16 *smem, const DmaLoader<C, C:
     lds_barrier();
     touch<C>(f[(NU - 1) & 1]);
     post(s);
-    if (s + NS < nk) {  // refill this step's stage
+    if constexpr (RF) {  // refill this step's stage
       koff(s + NS, ka, kb);
       la.issue(smem + cur * ST, wave, ka);
       lb.issue(smem + cur * ST + AS, wave, kb);
@@ -632,10 +659,14 @@ __device__ __forceinline__ void kloop_dma_pl(__bf16 *smem, const DmaLoader<C, C:
     // the next step's first fragments (after the last step: an unused read of
     // a valid stage)
     load_frags<C>(smem + cur * ST, smem + cur * ST + AS, 0, arow0, brow, lane, f[NU & 1]);
-    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (!IL) __builtin_amdgcn_sched_barrier(0);
     mma_frags<C>(f[(NU - 1) & 1], acc);
+    if constexpr (IL) interleave_mfma<RF ? IPW : 0, NFR, NMF>();
     __builtin_amdgcn_sched_barrier(0);
-  }
+  };
+  int s = 0;
+  for (; s < nk - NS; ++s) step(s, std::true_type());
+  for (; s < nk; ++s) step(s, std::false_type());
   lds_barrier();
 }
 
