@@ -142,7 +142,7 @@ struct EpiDZ {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float A = (float)a[r], U = (float)u[r];
-      const float sg = __frcp_rn(1.f + __expf(-A));
+      const float sg = fast_sigmoid(A);
       da[r] = (__bf16)(v[r] * U * sg * (1.f + A * (1.f - sg)));
       du[r] = (__bf16)(v[r] * A * sg);
     }

@@ -34,47 +34,59 @@
 //              over the group's tokens.
 //   k_conv     depthwise conv of E, vector loads, sliding window.
 
+#include <algorithm>
+
 #include "mfma_common.h"
 
 namespace ipttt {
 namespace mfma {
 
 // ---------------------------------------------------------------------------
-template <class C, bool PL = false>
+// PERS: persistent blocks (one per CU), each running a range of its XCD's
+// tiles back to back through kloop_dma_pl_tiles.
+template <class C, bool PL = false, bool PERS = false>
 __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC))) void k_gateup(
     Slab s, const __bf16 *__restrict__ x, const __bf16 *__restrict__ wg,
     const __bf16 *__restrict__ wu, __bf16 *__restrict__ zt, __bf16 *__restrict__ at,
     __bf16 *__restrict__ ut) {
   static_assert(C::SMEM_ELEMS * 2 <= 160 * 1024, "LDS overflow");
+  static_assert(PL || !PERS, "persistent blocks use the pipelined loop");
   __shared__ __attribute__((aligned(1024))) __bf16 smem[C::SMEM_ELEMS];
   using M = typename C::M;
   constexpr int FT = C::BN / 2;  // d_ff columns per block
   const int P = s.nc * s.Bp;
   const int nm = (P + C::BM - 1) / C::BM, nn = (s.F + FT - 1) / FT;
   const int per_seq = nm * nn;
-  const int id = xcd_remap(blockIdx.x, gridDim.x);
-  const int n_seq = id / per_seq;
-  int tm, tn;
-  tile_of<C::GM>(id % per_seq, nm, nn, tm, tn);
-  const int m0 = tm * C::BM, f0 = tn * FT;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WN, wn = wave % C::WN;
+  // tile of logical index id: sequence, first slab row, first d_ff column
+  const auto tile = [&](int id, int &n_seq, int &m0, int &f0) __attribute__((always_inline)) {
+    n_seq = id / per_seq;
+    int tm, tn;
+    tile_of<C::GM>(id % per_seq, nm, nn, tm, tn);
+    m0 = tm * C::BM;
+    f0 = tn * FT;
+  };
 
   // A rows: the slab rows' tokens of X; B rows [0, FT): gate rows f0..,
   // [FT, 2 FT): the matching up rows
   DmaLoader<C, C::BM> la;
   DmaLoader<C, C::BN> lb;
-  const __bf16 *xs = x + n_seq * s.x_seq_stride;
-  la.init(wave, lane, [&](int r) {
-    const int p = m0 + r;
-    const int64_t t = p < P ? slab_row_token(s, p) : -1;
-    return xs + (t >= 0 ? t : 0) * s.d;
-  });
-  lb.init(wave, lane, [&](int rr) {
-    const int f = f0 + (rr < FT ? rr : rr - FT);
-    return (rr < FT ? wg : wu) + (int64_t)(f < s.F ? f : 0) * s.d;
-  });
+  const auto init = [&](int id) __attribute__((always_inline)) {
+    int n_seq, m0, f0;
+    tile(id, n_seq, m0, f0);
+    const __bf16 *xs = x + n_seq * s.x_seq_stride;
+    la.init(wave, lane, [&](int r) {
+      const int p = m0 + r;
+      const int64_t t = p < P ? slab_row_token(s, p) : -1;
+      return xs + (t >= 0 ? t : 0) * s.d;
+    });
+    lb.init(wave, lane, [&](int rr) {
+      const int f = f0 + (rr < FT ? rr : rr - FT);
+      return (rr < FT ? wg : wu) + (int64_t)(f < s.F ? f : 0) * s.d;
+    });
+  };
   // a wave's first NJ/2 B tiles are gate rows, the other NJ/2 the matching up rows
   constexpr int HJ = C::NJ / 2;
   constexpr int WF = C::WTN / 2;  // d_ff columns per wave
@@ -85,54 +97,82 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
     brow[j + HJ] = FT + wn * WF + C::FM * j;
   }
   typename C::acc_t acc[C::MI][C::NJ];
-  zero_acc<C>(acc);
-  const auto koff = [](int st, int64_t &ka, int64_t &kb) { ka = kb = (int64_t)st * C::BK; };
-  if constexpr (PL)
-    kloop_dma_pl<C, 2, true>(smem, la, lb, s.d / C::BK, wave, lane, wm * C::WTM, brow, acc, koff,
-                       [](int) {}, [](int) {});
-  else
-    kloop_dma<2>(smem, la, lb, s.d / C::BK, wave, koff, [&](const __bf16 *As, const __bf16 *Bs) {
-      mma_stage<C>(As, Bs, wm * C::WTM, brow, lane, acc);
-    });
 
-  __bf16 *zts = zt + (int64_t)n_seq * s.F * s.Lp;
+  const auto epilogue = [&](int id) __attribute__((always_inline)) {
+    int n_seq, m0, f0;
+    tile(id, n_seq, m0, f0);
+    __bf16 *zts = zt + (int64_t)n_seq * s.F * s.Lp;
 #pragma unroll
-  for (int i = 0; i < C::MI; ++i)
+    for (int i = 0; i < C::MI; ++i)
 #pragma unroll
-    for (int g = 0; g < M::NG; ++g) {
-      // rows p .. p + 3 lie in one chunk (Bp is a multiple of 4); chunk-padding
-      // rows and tokens past the sequence end are written as exact zeros
-      const int p = m0 + wm * C::WTM + C::FM * i + M::rrow(lane, g);
-      const int jc = p / s.Bp, ic = p - jc * s.Bp;
-      const int64_t t0 = s.tok0 + (int64_t)jc * s.B + ic;
-      bool real[4];
+      for (int g = 0; g < M::NG; ++g) {
+        // rows p .. p + 3 lie in one chunk (Bp is a multiple of 4); chunk-padding
+        // rows and tokens past the sequence end are written as exact zeros
+        const int p = m0 + wm * C::WTM + C::FM * i + M::rrow(lane, g);
+        const int jc = p / s.Bp, ic = p - jc * s.Bp;
+        const int64_t t0 = s.tok0 + (int64_t)jc * s.B + ic;
+        bool real[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) real[r] = jc < s.nc && ic + r < s.B && t0 + r < s.L;
-      if (p >= P) continue;
+        for (int r = 0; r < 4; ++r) real[r] = jc < s.nc && ic + r < s.B && t0 + r < s.L;
+        if (p >= P) continue;
 #pragma unroll
-      for (int j = 0; j < HJ; ++j) {
-        const int f = f0 + wn * WF + C::FM * j + M::rcol(lane);
-        if (f < s.F) {
-          const f32x4 gv = get4(acc[i][j], g), uv = get4(acc[i][j + HJ], g);
-          bf16x4 v;
+        for (int j = 0; j < HJ; ++j) {
+          const int f = f0 + wn * WF + C::FM * j + M::rcol(lane);
+          if (f < s.F) {
+            const f32x4 gv = get4(acc[i][j], g), uv = get4(acc[i][j + HJ], g);
+            bf16x4 v;
 #pragma unroll
-          for (int r = 0; r < 4; ++r)  // SiLU(a) = a / (1 + e^-a), fast reciprocal
-            v[r] = (__bf16)(real[r] ? gv[r] * __frcp_rn(1.f + __expf(-gv[r])) * uv[r] : 0.f);
-          *(bf16x4 *)(zts + (int64_t)f * s.Lp + p) = v;
-          if (at) {  // pre-activations, for the backward
-            bf16x4 va, vu;
+            for (int r = 0; r < 4; ++r)  // SiLU(a) = a sigmoid(a)
+              v[r] = (__bf16)(real[r] ? gv[r] * fast_sigmoid(gv[r]) * uv[r] : 0.f);
+            *(bf16x4 *)(zts + (int64_t)f * s.Lp + p) = v;
+            if (at) {  // pre-activations, for the backward
+              bf16x4 va, vu;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              va[r] = (__bf16)(real[r] ? gv[r] : 0.f);
-              vu[r] = (__bf16)(real[r] ? uv[r] : 0.f);
+              for (int r = 0; r < 4; ++r) {
+                va[r] = (__bf16)(real[r] ? gv[r] : 0.f);
+                vu[r] = (__bf16)(real[r] ? uv[r] : 0.f);
+              }
+              const int64_t off = (int64_t)n_seq * s.F * s.Lp + (int64_t)f * s.Lp + p;
+              *(bf16x4 *)(at + off) = va;
+              *(bf16x4 *)(ut + off) = vu;
             }
-            const int64_t off = (int64_t)n_seq * s.F * s.Lp + (int64_t)f * s.Lp + p;
-            *(bf16x4 *)(at + off) = va;
-            *(bf16x4 *)(ut + off) = vu;
           }
         }
       }
-    }
+  };
+
+  const auto koff = [](int st, int64_t &ka, int64_t &kb) { ka = kb = (int64_t)st * C::BK; };
+  if constexpr (PERS) {
+    // the hardware hands block b to XCD b % 8; that XCD's blocks share its
+    // contiguous range of logical tiles, block k of them taking tiles
+    // lo + k, lo + k + nbx, ... so that concurrent blocks hold neighbouring tiles
+    const int ntiles = per_seq * s.n_seq;
+    const int xc = blockIdx.x % 8, k = blockIdx.x / 8;
+    const int nbx = gridDim.x / 8 + (xc < (int)(gridDim.x % 8));
+    const int per = ntiles / 8, rem = ntiles % 8;
+    const int lo = xc * per + min(xc, rem), hi = lo + per + (xc < rem);
+    const int nt = hi - lo - k > 0 ? (hi - lo - k + nbx - 1) / nbx : 0;
+    if (nt == 0) return;
+    kloop_dma_pl_tiles<C, 2, true, C::MI + C::NJ>(
+        smem, la, lb, nt, s.d / C::BK, wave, acc,
+        [&](const __bf16 *As, const __bf16 *Bs, int u, Frags<C> &f) __attribute__((always_inline)) {
+          load_frags<C>(As, Bs, u, wm * C::WTM, brow, lane, f);
+        },
+        koff, [&](int t) __attribute__((always_inline)) { init(lo + k + t * nbx); },
+        [&](int t) __attribute__((always_inline)) { epilogue(lo + k + t * nbx); });
+  } else {
+    const int id = xcd_remap(blockIdx.x, gridDim.x);
+    init(id);
+    zero_acc<C>(acc);
+    if constexpr (PL)
+      kloop_dma_pl<C, 2, true>(smem, la, lb, s.d / C::BK, wave, lane, wm * C::WTM, brow, acc,
+                               koff, [](int) {}, [](int) {});
+    else
+      kloop_dma<2>(smem, la, lb, s.d / C::BK, wave, koff, [&](const __bf16 *As, const __bf16 *Bs) {
+        mma_stage<C>(As, Bs, wm * C::WTM, brow, lane, acc);
+      });
+    epilogue(id);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -222,16 +262,28 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
   const int R = min(s.G, s.nc - j_first) * s.Bp;  // its rows (the slab's last group may be short)
   if (m0 >= R) return;
   const int64_t row0 = (int64_t)j_first * s.Bp;  // its first slab row
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WN, wn = wave % C::WN;
   const int r0 = tid / C::KP;
+  int brow[C::NJ];
+#pragma unroll
+  for (int jj = 0; jj < C::NJ; ++jj) brow[jj] = wn * C::WTN + C::FM * jj;
+  typename C::acc_t acc[C::MI][C::NJ];
+  zero_acc<C>(acc);
+  const __bf16 *zts = zt + (int64_t)n_seq * s.F * s.Lp;
+  const __bf16 *ss = snap + n_seq * snap_seq_stride + ql * snap_group_stride;
+  const __bf16 *vts = vt + (int64_t)n_seq * s.d * s.Lp;
+  // rows of the tile see the group's tokens before their own chunk (G > 1);
+  // the tile's last chunk starts at cs_last, so the second K phase runs over
+  // group rows [0, cs_last), where P is zero until a row's chunk is complete.
+  const int cs_last = (min(m0 + C::BM, R) - 1) / s.Bp * s.Bp;
+  const __bf16 *pts = pt ? pt + n_seq * pt_seq_stride + (int64_t)q * RG * RG : nullptr;
   // A = Z read from Zt (token-contiguous rows of d_ff): K row f, M columns =
   // the group's slab rows. Columns past the workspace rows are clamped in
   // bounds; the rows they feed are past the group and are dropped.
   LA la;
   Loader<C, C::B_PIECES> lb;
-  const __bf16 *zts = zt + (int64_t)n_seq * s.F * s.Lp;
-  const __bf16 *ss = snap + n_seq * snap_seq_stride + ql * snap_group_stride;
   la.ld = s.Lp;
 #pragma unroll
   for (int i = 0; i < LA::NP; ++i)
@@ -241,32 +293,19 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
     const int n = n0 + r0 + C::RPP * i;
     lb.ptr[i] = ss + (int64_t)(n < s.d ? n : 0) * s.F;
   }
-  int brow[C::NJ];
-#pragma unroll
-  for (int jj = 0; jj < C::NJ; ++jj) brow[jj] = wn * C::WTN + C::FM * jj;
-  typename C::acc_t acc[C::MI][C::NJ];
-  zero_acc<C>(acc);
   kloop_t<C>(smem, la, lb, s.F / C::BK, tid, wm * C::WTM, brow, acc);
 
-  const __bf16 *vts = vt + (int64_t)n_seq * s.d * s.Lp;
-  if (pt) {
-    // rows of the tile see the group's tokens before their own chunk; the
-    // tile's last chunk starts at cs_last, so K runs over group rows
-    // [0, cs_last) and P is zero where a row's chunk is not yet complete.
-    const int cs_last = (min(m0 + C::BM, R) - 1) / s.Bp * s.Bp;
-    if (cs_last > 0) {
-      const __bf16 *pts = pt + n_seq * pt_seq_stride + (int64_t)q * RG * RG;
-      la.ld = RG;
+  if (pts && cs_last > 0) {
+    la.ld = RG;
 #pragma unroll
-      for (int i = 0; i < LA::NP; ++i)
-        la.ptr[i] = pts + (int64_t)LA::krow(tid, i) * RG + min(m0 + LA::col(tid, i), RG - 8);
+    for (int i = 0; i < LA::NP; ++i)
+      la.ptr[i] = pts + (int64_t)LA::krow(tid, i) * RG + min(m0 + LA::col(tid, i), RG - 8);
 #pragma unroll
-      for (int i = 0; i < C::B_PIECES; ++i) {
-        const int n = n0 + r0 + C::RPP * i;
-        lb.ptr[i] = vts + (int64_t)(n < s.d ? n : 0) * s.Lp + row0;
-      }
-      kloop_t<C>(smem, la, lb, cs_last / C::BK, tid, wm * C::WTM, brow, acc);
+    for (int i = 0; i < C::B_PIECES; ++i) {
+      const int n = n0 + r0 + C::RPP * i;
+      lb.ptr[i] = vts + (int64_t)(n < s.d ? n : 0) * s.Lp + row0;
     }
+    kloop_t<C>(smem, la, lb, cs_last / C::BK, tid, wm * C::WTM, brow, acc);
   }
 
   float *os = o ? o + n_seq * s.x_seq_stride : nullptr;  // nullptr: residual only
@@ -599,12 +638,29 @@ __global__ __launch_bounds__(256) void k_conv(Slab s, const __bf16 *__restrict__
 }
 
 // ---- launchers (templated on the block configuration) ---------------------
-template <class C, bool PL = false>
+// Compute units of the current device (cached per device).
+inline int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cus[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+template <class C, bool PL = false, bool PERS = false>
 hipError_t launch_gateup(const Slab &s, const __bf16 *x, const Weights &w, const WsPtrs &ws,
                          hipStream_t st, __bf16 *at = nullptr, __bf16 *ut = nullptr) {
   const int64_t P = (int64_t)s.nc * s.Bp;
-  const int64_t nb = ((P + C::BM - 1) / C::BM) * ((s.F + C::BN / 2 - 1) / (C::BN / 2)) * s.n_seq;
-  hipLaunchKernelGGL((k_gateup<C, PL>), dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, x,
+  const int64_t ntiles =
+      ((P + C::BM - 1) / C::BM) * ((s.F + C::BN / 2 - 1) / (C::BN / 2)) * s.n_seq;
+  // persistent: one block per CU (the stages fill most of a CU's LDS)
+  const int64_t nb = PERS ? std::min<int64_t>(ntiles, device_cus()) : ntiles;
+  hipLaunchKernelGGL((k_gateup<C, PL, PERS>), dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, x,
                      (const __bf16 *)w.w_gate, (const __bf16 *)w.w_up, (__bf16 *)ws.zt, at, ut);
   return hipGetLastError();
 }
@@ -741,7 +797,7 @@ hipError_t mf_conv(const Slab &s, const __bf16 *e, const Weights &w, const WsPtr
 }
 hipError_t mf_gateup(const Slab &s, const __bf16 *x, const Weights &w, const WsPtrs &ws,
                      hipStream_t st) {
-  return mfma::launch_gateup<mfma::GateUpCfg, true>(s, x, w, ws, st);
+  return mfma::launch_gateup<mfma::GateUpCfg, true, true>(s, x, w, ws, st);
 }
 hipError_t mf_proj(const Slab &s, const Weights &w, const WsPtrs &ws, hipStream_t st) {
   return mfma::launch_proj<mfma::ProjCfg, true>(s, w, ws, st);
@@ -785,7 +841,7 @@ hipError_t mf_update_one(const Slab &s, int j, const WsPtrs &ws, float *w_state,
 }
 hipError_t mf_gateup_pre(const Slab &s, const __bf16 *x, const Weights &w, const WsPtrs &ws,
                          __bf16 *at, __bf16 *ut, hipStream_t st) {
-  return mfma::launch_gateup<mfma::GateUpCfg, true>(s, x, w, ws, st, at, ut);
+  return mfma::launch_gateup<mfma::GateUpCfg, true, true>(s, x, w, ws, st, at, ut);
 }
 hipError_t mf_update_reverse(const Slab &s, const __bf16 *zt, const __bf16 *bt, float *g,
                              __bf16 *snap, hipStream_t st) {

@@ -115,6 +115,14 @@ struct Cfg {
 
 __device__ __forceinline__ uint4 ld16(const __bf16 *p) { return *(const uint4 *)p; }
 
+// Logistic sigmoid 1 / (1 + e^-a) with the hardware exponential and reciprocal
+// (v_exp_f32, v_rcp_f32: about 1 ulp each in fp32, far below the bf16 rounding
+// every use here ends in); a correctly rounded reciprocal expands to a full
+// division sequence per element.
+__device__ __forceinline__ float fast_sigmoid(float a) {
+  return __builtin_amdgcn_rcpf(1.f + __expf(-a));
+}
+
 // Logical block index: the hardware hands consecutive workgroups to the 8 XCDs
 // in turn; give each XCD a contiguous range of logical tiles so that tiles
 // that share operands also share that XCD's L2.
@@ -597,17 +605,18 @@ __device__ __forceinline__ void interleave_mfma() {
 // pre(s) runs before step s's MFMAs (the accumulators then hold steps
 // 0 .. s - 1) and post(s) after step s's barrier, ahead of the refill (the
 // next step's vmcnt wait covers any global stores it issues).
-template <class C, int NS, bool IL, class Koff, class Pre, class Post>
-__device__ __forceinline__ void kloop_dma_pl(__bf16 *smem, const DmaLoader<C, C::BM> &la,
-                                             const DmaLoader<C, C::BN> &lb, int nk, int wave,
-                                             int lane, int arow0, const int (&brow)[C::NJ],
-                                             typename C::acc_t (&acc)[C::MI][C::NJ], Koff koff,
-                                             Pre pre, Post post) {
+// ldf(As, Bs, u, f) reads sub-step u's fragments of a stage; ND is the number
+// of LDS read instructions it issues.
+template <class C, int NS, bool IL, int ND, class LA, class LB, class Ldf, class Koff, class Pre,
+          class Post>
+__device__ __forceinline__ void kloop_dma_pl(__bf16 *smem, const LA &la, const LB &lb, int nk,
+                                             int wave, typename C::acc_t (&acc)[C::MI][C::NJ],
+                                             Ldf ldf, Koff koff, Pre pre, Post post) {
   constexpr int NU = C::BK / C::M::K;
   static_assert(NU >= 2, "two or more MFMA sub-steps per stage");
-  constexpr int AS = C::BM * C::BK, ST = AS + C::BN * C::BK;
-  constexpr int IPW = DmaLoader<C, C::BM>::NI + DmaLoader<C, C::BN>::NI;
-  constexpr int NFR = C::MI + C::NJ, NMF = C::MI * C::NJ;
+  constexpr int AS = LA::STAGE, ST = AS + LB::STAGE;
+  constexpr int IPW = LA::NI + LB::NI;
+  constexpr int NFR = ND, NMF = C::MI * C::NJ;
   int64_t ka, kb;
 #pragma unroll
   for (int p = 0; p < NS; ++p)
@@ -622,7 +631,7 @@ __device__ __forceinline__ void kloop_dma_pl(__bf16 *smem, const DmaLoader<C, C:
     wait_vm<0>();
   lds_barrier();
   Frags<C> f[2];
-  load_frags<C>(smem, smem + AS, 0, arow0, brow, lane, f[0]);
+  ldf(smem, smem + AS, 0, f[0]);
   // keep this load apart from the loop's prefetch (the compiler would
   // otherwise merge the two into one load at the loop head)
 #pragma unroll
@@ -636,7 +645,7 @@ __device__ __forceinline__ void kloop_dma_pl(__bf16 *smem, const DmaLoader<C, C:
 #pragma unroll
     for (int u = 0; u + 1 < NU; ++u) {
       touch<C>(f[u & 1]);
-      load_frags<C>(st, st + AS, u + 1, arow0, brow, lane, f[(u + 1) & 1]);
+      ldf(st, st + AS, u + 1, f[(u + 1) & 1]);
       if constexpr (!IL) __builtin_amdgcn_sched_barrier(0);
       if (u == 0) pre(s);
       mma_frags<C>(f[u & 1], acc);
@@ -658,7 +667,7 @@ __device__ __forceinline__ void kloop_dma_pl(__bf16 *smem, const DmaLoader<C, C:
     cur = cur + 1 == NS ? 0 : cur + 1;
     // the next step's first fragments (after the last step: an unused read of
     // a valid stage)
-    load_frags<C>(smem + cur * ST, smem + cur * ST + AS, 0, arow0, brow, lane, f[NU & 1]);
+    ldf(smem + cur * ST, smem + cur * ST + AS, 0, f[NU & 1]);
     if constexpr (!IL) __builtin_amdgcn_sched_barrier(0);
     mma_frags<C>(f[(NU - 1) & 1], acc);
     if constexpr (IL) interleave_mfma<RF ? IPW : 0, NFR, NMF>();
@@ -668,6 +677,114 @@ __device__ __forceinline__ void kloop_dma_pl(__bf16 *smem, const DmaLoader<C, C:
   for (; s < nk - NS; ++s) step(s, std::true_type());
   for (; s < nk; ++s) step(s, std::false_type());
   lds_barrier();
+}
+
+// Persistent form of kloop_dma_pl: the block runs nt tiles of nk K steps each
+// as one stream of nt nk steps. Copies run NS steps ahead across tile
+// boundaries, so a tile's first stages land during the previous tile's last
+// steps, and epi(t) (tile t's epilogue, from the accumulators) runs between
+// tile t's last MFMAs and tile t + 1's first, with t + 1's first fragments
+// already in registers; its stores drain under the next tile's MFMAs.
+// next(t) points the loaders at tile t (called before tile t's first copy);
+// koff(s, ka, kb) gives step s's offsets within a tile.
+template <class C, int NS, bool IL, int ND, class LA, class LB, class Ldf, class Koff, class Next,
+          class Epi>
+__device__ __forceinline__ void kloop_dma_pl_tiles(__bf16 *smem, LA &la, LB &lb, int nt, int nk,
+                                                   int wave,
+                                                   typename C::acc_t (&acc)[C::MI][C::NJ],
+                                                   Ldf ldf, Koff koff, Next next, Epi epi) {
+  constexpr int NU = C::BK / C::M::K;
+  static_assert(NU >= 2, "two or more MFMA sub-steps per stage");
+  constexpr int AS = LA::STAGE, ST = AS + LB::STAGE;
+  constexpr int IPW = LA::NI + LB::NI;
+  constexpr int NFR = ND, NMF = C::MI * C::NJ;
+  const int total = nt * nk;
+  int lt = 0, ls = 0;  // tile and step of the next copy
+  const auto advance = [&]() __attribute__((always_inline)) {
+    if (ls == nk && lt + 1 < nt) {  // the next copy starts the next tile
+      ls = 0;
+      next(++lt);
+    }
+  };
+  int64_t ka, kb;
+  next(0);
+#pragma unroll
+  for (int p = 0; p < NS; ++p)
+    if (p < total) {
+      koff(ls++, ka, kb);
+      la.issue(smem + p * ST, wave, ka);
+      lb.issue(smem + p * ST + AS, wave, kb);
+      advance();
+    }
+  if (NS - 1 < total)
+    wait_vm<(NS - 1) * IPW>();
+  else
+    wait_vm<0>();
+  lds_barrier();
+  zero_acc<C>(acc);
+  Frags<C> f[2];
+  ldf(smem, smem + AS, 0, f[0]);
+#pragma unroll
+  for (int i = 0; i < C::MI; ++i) asm volatile("" : "+v"(f[0].a[i]));
+#pragma unroll
+  for (int j = 0; j < C::NJ; ++j) asm volatile("" : "+v"(f[0].b[j]));
+  int cur = 0, ct = 0, cs = 0;  // stage, tile and step being computed
+  const auto step = [&](int g, auto refill) __attribute__((always_inline)) {
+    constexpr bool RF = decltype(refill)::value;
+    const __bf16 *st = smem + cur * ST;
+#pragma unroll
+    for (int u = 0; u + 1 < NU; ++u) {
+      touch<C>(f[u & 1]);
+      ldf(st, st + AS, u + 1, f[(u + 1) & 1]);
+      if constexpr (!IL) __builtin_amdgcn_sched_barrier(0);
+      mma_frags<C>(f[u & 1], acc);
+      if constexpr (IL) interleave_mfma<0, NFR, NMF>();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (g + NS - 1 < total)
+      wait_vm<(NS - 2) * IPW>();  // step g + 1 landed
+    else
+      wait_vm<0>();
+    lds_barrier();
+    touch<C>(f[(NU - 1) & 1]);
+    if constexpr (RF) {  // refill this step's stage with step g + NS
+      koff(ls++, ka, kb);
+      la.issue(smem + cur * ST, wave, ka);
+      lb.issue(smem + cur * ST + AS, wave, kb);
+    }
+    cur = cur + 1 == NS ? 0 : cur + 1;
+    ldf(smem + cur * ST, smem + cur * ST + AS, 0, f[NU & 1]);
+    if constexpr (!IL) __builtin_amdgcn_sched_barrier(0);
+    mma_frags<C>(f[(NU - 1) & 1], acc);
+    if constexpr (IL) interleave_mfma<RF ? IPW : 0, NFR, NMF>();
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (RF) advance();
+    if (++cs == nk) {
+      epi(ct);
+      zero_acc<C>(acc);
+      cs = 0;
+      ++ct;
+    }
+  };
+  int g = 0;
+  for (; g < total - NS; ++g) step(g, std::true_type());
+  for (; g < total; ++g) step(g, std::false_type());
+  lds_barrier();
+}
+
+// Both operands K-contiguous (swizzled rows).
+template <class C, int NS, bool IL, class Koff, class Pre, class Post>
+__device__ __forceinline__ void kloop_dma_pl(__bf16 *smem, const DmaLoader<C, C::BM> &la,
+                                             const DmaLoader<C, C::BN> &lb, int nk, int wave,
+                                             int lane, int arow0, const int (&brow)[C::NJ],
+                                             typename C::acc_t (&acc)[C::MI][C::NJ], Koff koff,
+                                             Pre pre, Post post) {
+  kloop_dma_pl<C, NS, IL, C::MI + C::NJ>(
+      smem, la, lb, nk, wave, acc,
+      [&](const __bf16 *As, const __bf16 *Bs, int u, Frags<C> &f) __attribute__((always_inline)) {
+        load_frags<C>(As, Bs, u, arow0, brow, lane, f);
+      },
+      koff, pre, post);
 }
 
 // Token of slab row p (slab rows fit in 32 bits), or -1 for a padding row.
