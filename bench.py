@@ -284,11 +284,15 @@ def trace_summary(path: str) -> str:
     rows = sorted(csv.DictReader(open(path)), key=lambda r: -float(r["TotalDurationNs"]))
     out = ["| kernel | calls | avg ms | min ms | max ms | share % |", "|---|---|---|---|---|---|"]
     for r in rows:
-        name = re.sub(r"ipttt::mfma::|ipttt::", "", r["Name"])
+        name = r["Name"].replace("(anonymous namespace)::", "")
+        name = re.sub(r"ipttt::mfma::|ipttt::", "", name)
         name = re.sub(r"\(.*$", "", name).replace("void ", "")
-        m = re.match(r"_ZN5ipttt4mfma\d+(\w+?)I", name)
-        if m:
-            name = m.group(1)
+        if name.startswith("_Z"):  # not demangled (bf16 template arguments): the kernel's identifier
+            m = re.search(r"\d(k_\w+?)I", name)
+            if m:
+                name = m.group(1)
+        if "_Accum" in name:  # bf16 template arguments the profiler could not render
+            name = name.split("<")[0]
         name = name.replace("__amd_rocclr_", "")
         out.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e6:.3f} | "
                    f"{float(r['MinNs']) / 1e6:.3f} | {float(r['MaxNs']) / 1e6:.3f} | "
