@@ -231,8 +231,10 @@ hipError_t launch_gemm(const GProb &g, const Epi &epi, hipStream_t st) {
   return hipGetLastError();
 }
 
-using BwCfg = Cfg<2, 4, 64, 16, 16, 8>;
-using BwSmallCfg = Cfg<1, 2, 64, 16, 16, 8>;  // chunk-batched problems with short chunks
+// transposed operands: K-major rows padded by 16 elements (conflict-free
+// transposing reads, as for the forward's apply)
+using BwCfg = Cfg<2, 4, 64, 16, 16, 16>;
+using BwSmallCfg = Cfg<1, 2, 64, 16, 16, 16>;  // chunk-batched problems with short chunks
 using BwNTCfg = Cfg<2, 4, 64, 16, 0, 8>;       // both operands K-contiguous: direct copies
 
 // ---- elementwise / vector kernels --------------------------------------------

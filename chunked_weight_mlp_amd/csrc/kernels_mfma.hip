@@ -767,10 +767,13 @@ static_assert(kChunkAlign % CONV_RUN == 0, "conv runs must not cross a chunk");
 // 1024), alternating candidates within one run.
 using GateUpCfg = Cfg<2, 4, 64, 16, 0, 8, 1, 4>;   // direct LDS copies, swizzled rows
 using ProjCfg = Cfg<2, 4, 64, 16, 0, 8, 1, 8>;     // direct LDS copies, swizzled rows
-using ApplyCfg = Cfg<2, 4, 64, 16, 16, 8>;
-using ApplySmallCfg = Cfg<1, 2, 64, 16, 16, 8>;  // when ApplyCfg would leave most CUs idle
+// K-major (transposed) rows are padded by 16 elements: the four K rows one
+// 16-lane transposing read touches then start 8 banks apart and never share a
+// bank (a pad of 8 leaves every such read 2-way conflicted).
+using ApplyCfg = Cfg<2, 4, 64, 16, 16, 16>;
+using ApplySmallCfg = Cfg<1, 2, 64, 16, 16, 16>;  // when ApplyCfg would leave most CUs idle
 using UpdateCfg = Cfg<1, 2, 64, 16, 0, 8, 1, 16>;  // direct copies, pipelined fragments
-using GramCfg = Cfg<2, 4, 64, 16, 16, 8>;
+using GramCfg = Cfg<2, 4, 64, 16, 16, 16>;
 static_assert(kChunkAlign % UpdateCfg::BK == 0, "chunk pitch must be whole update K steps");
 // The Gram computes, per m tile, the columns the apply's m tiles read: its m
 // tiles must be unions of whole apply m tiles.
