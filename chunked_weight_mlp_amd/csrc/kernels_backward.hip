@@ -75,18 +75,17 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
       const __bf16 *pa = A.p + b1 * A.s1 + b2 * A.s2 + sg * A.sseg;
       const __bf16 *pb = Bo.p + b1 * Bo.s1 + b2 * Bo.s2 + sg * Bo.sseg;
       if constexpr (!TA && !TB && C::SWZ) {
-        // both operands K-contiguous: direct LDS copies into swizzled rows
+        // both operands K-contiguous: direct LDS copies into swizzled rows,
+        // pipelined fragments interleaved with the MFMAs
         const int wv = __builtin_amdgcn_readfirstlane(wave);
         DmaLoader<C, C::BM> da;
         DmaLoader<C, C::BN> db;
         da.init(wv, lane, [&](int r) { return pa + min((int64_t)m0 + r, A.lim - 1) * A.ld; });
         db.init(wv, lane, [&](int r) { return pb + min((int64_t)n0 + r, Bo.lim - 1) * Bo.ld; });
-        kloop_dma<2>(
-            smem, da, db, g.ph[ph].K / C::BK, wv,
-            [](int st, int64_t &ka, int64_t &kb) { ka = kb = (int64_t)st * C::BK; },
-            [&](const __bf16 *As, const __bf16 *Bs) {
-              mma_stage<C>(As, Bs, wm * C::WTM, brow, lane, acc);
-            });
+        kloop_dma_pl<C, 2, true>(
+            smem, da, db, g.ph[ph].K / C::BK, wv, lane, wm * C::WTM, brow, acc,
+            [](int st, int64_t &ka, int64_t &kb) { ka = kb = (int64_t)st * C::BK; }, [](int) {},
+            [](int) {});
         continue;
       }
       if constexpr (TA) {
