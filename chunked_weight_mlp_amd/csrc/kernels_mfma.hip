@@ -42,15 +42,54 @@ namespace ipttt {
 namespace mfma {
 
 // ---------------------------------------------------------------------------
+// Runs a GEMM kernel's tiles (logical ids 0 .. ntiles - 1) with both operands
+// staged by direct copies: init(id) points the loaders at tile id,
+// epilogue(id) writes it from the accumulators. PERS: persistent blocks (one
+// per CU) walk their XCD's tiles as one stream of K steps
+// (kloop_dma_pl_tiles). The hardware hands block b to XCD b % 8; that XCD's
+// blocks share its contiguous range of logical tiles, block k of them taking
+// tiles lo + k, lo + k + nbx, ..., so concurrent blocks hold neighbouring
+// tiles. Otherwise one tile per block, numbered by xcd_remap.
+template <class C, bool PERS, class Init, class Epi>
+__device__ __forceinline__ void run_tiles(__bf16 *smem, DmaLoader<C, C::BM> &la,
+                                          DmaLoader<C, C::BN> &lb, int ntiles, int nk, int wave,
+                                          int lane, int arow0, const int (&brow)[C::NJ],
+                                          typename C::acc_t (&acc)[C::MI][C::NJ], Init init,
+                                          Epi epilogue) {
+  const auto koff = [](int st, int64_t &ka, int64_t &kb) { ka = kb = (int64_t)st * C::BK; };
+  if constexpr (PERS) {
+    const int xc = blockIdx.x % 8, k = blockIdx.x / 8;
+    const int nbx = gridDim.x / 8 + (xc < (int)(gridDim.x % 8));
+    const int per = ntiles / 8, rem = ntiles % 8;
+    const int lo = xc * per + min(xc, rem), hi = lo + per + (xc < rem);
+    const int nt = hi - lo - k > 0 ? (hi - lo - k + nbx - 1) / nbx : 0;
+    if (nt == 0) return;
+    kloop_dma_pl_tiles<C, 2, true, C::MI + C::NJ>(
+        smem, la, lb, nt, nk, wave, acc,
+        [&](const __bf16 *As, const __bf16 *Bs, int u, Frags<C> &f) __attribute__((always_inline)) {
+          load_frags<C>(As, Bs, u, arow0, brow, lane, f);
+        },
+        koff, [&](int t) __attribute__((always_inline)) { init(lo + k + t * nbx); },
+        [&](int t) __attribute__((always_inline)) { epilogue(lo + k + t * nbx); });
+  } else {
+    const int id = xcd_remap(blockIdx.x, gridDim.x);
+    init(id);
+    zero_acc<C>(acc);
+    kloop_dma_pl<C, 2, true>(smem, la, lb, nk, wave, lane, arow0, brow, acc, koff, [](int) {},
+                             [](int) {});
+    epilogue(id);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // PERS: persistent blocks (one per CU), each running a range of its XCD's
-// tiles back to back through kloop_dma_pl_tiles.
-template <class C, bool PL = false, bool PERS = false>
+// tiles back to back through kloop_dma_pl_tiles; otherwise one tile per block.
+template <class C, bool PERS>
 __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC))) void k_gateup(
     Slab s, const __bf16 *__restrict__ x, const __bf16 *__restrict__ wg,
     const __bf16 *__restrict__ wu, __bf16 *__restrict__ zt, __bf16 *__restrict__ at,
     __bf16 *__restrict__ ut) {
   static_assert(C::SMEM_ELEMS * 2 <= 160 * 1024, "LDS overflow");
-  static_assert(PL || !PERS, "persistent blocks use the pipelined loop");
   __shared__ __attribute__((aligned(1024))) __bf16 smem[C::SMEM_ELEMS];
   using M = typename C::M;
   constexpr int FT = C::BN / 2;  // d_ff columns per block
@@ -141,42 +180,12 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
       }
   };
 
-  const auto koff = [](int st, int64_t &ka, int64_t &kb) { ka = kb = (int64_t)st * C::BK; };
-  if constexpr (PERS) {
-    // the hardware hands block b to XCD b % 8; that XCD's blocks share its
-    // contiguous range of logical tiles, block k of them taking tiles
-    // lo + k, lo + k + nbx, ... so that concurrent blocks hold neighbouring tiles
-    const int ntiles = per_seq * s.n_seq;
-    const int xc = blockIdx.x % 8, k = blockIdx.x / 8;
-    const int nbx = gridDim.x / 8 + (xc < (int)(gridDim.x % 8));
-    const int per = ntiles / 8, rem = ntiles % 8;
-    const int lo = xc * per + min(xc, rem), hi = lo + per + (xc < rem);
-    const int nt = hi - lo - k > 0 ? (hi - lo - k + nbx - 1) / nbx : 0;
-    if (nt == 0) return;
-    kloop_dma_pl_tiles<C, 2, true, C::MI + C::NJ>(
-        smem, la, lb, nt, s.d / C::BK, wave, acc,
-        [&](const __bf16 *As, const __bf16 *Bs, int u, Frags<C> &f) __attribute__((always_inline)) {
-          load_frags<C>(As, Bs, u, wm * C::WTM, brow, lane, f);
-        },
-        koff, [&](int t) __attribute__((always_inline)) { init(lo + k + t * nbx); },
-        [&](int t) __attribute__((always_inline)) { epilogue(lo + k + t * nbx); });
-  } else {
-    const int id = xcd_remap(blockIdx.x, gridDim.x);
-    init(id);
-    zero_acc<C>(acc);
-    if constexpr (PL)
-      kloop_dma_pl<C, 2, true>(smem, la, lb, s.d / C::BK, wave, lane, wm * C::WTM, brow, acc,
-                               koff, [](int) {}, [](int) {});
-    else
-      kloop_dma<2>(smem, la, lb, s.d / C::BK, wave, koff, [&](const __bf16 *As, const __bf16 *Bs) {
-        mma_stage<C>(As, Bs, wm * C::WTM, brow, lane, acc);
-      });
-    epilogue(id);
-  }
+  run_tiles<C, PERS>(smem, la, lb, per_seq * s.n_seq, s.d / C::BK, wave, lane, wm * C::WTM, brow,
+                     acc, init, epilogue);
 }
 
 // ---------------------------------------------------------------------------
-template <class C, bool PL = false>
+template <class C, bool PERS>
 __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC))) void k_proj(
     Slab s, const __bf16 *__restrict__ c, const __bf16 *__restrict__ proj,
     __bf16 *__restrict__ vt, float scale) {
@@ -186,50 +195,52 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
   const int P = s.nc * s.Bp;
   const int nm = (P + C::BM - 1) / C::BM, nn = (s.d + C::BN - 1) / C::BN;
   const int per_seq = nm * nn;
-  const int id = xcd_remap(blockIdx.x, gridDim.x);
-  const int n_seq = id / per_seq;
-  int tm, tn;
-  tile_of<C::GM>(id % per_seq, nm, nn, tm, tn);
-  const int m0 = tm * C::BM, n0 = tn * C::BN;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WN, wn = wave % C::WN;
+  const auto tile = [&](int id, int &n_seq, int &m0, int &n0) __attribute__((always_inline)) {
+    n_seq = id / per_seq;
+    int tm, tn;
+    tile_of<C::GM>(id % per_seq, nm, nn, tm, tn);
+    m0 = tm * C::BM;
+    n0 = tn * C::BN;
+  };
   DmaLoader<C, C::BM> la;
   DmaLoader<C, C::BN> lb;
-  const __bf16 *cs = c + (int64_t)n_seq * s.Lp * s.d;
-  la.init(wave, lane, [&](int r) { return cs + (int64_t)(m0 + r < P ? m0 + r : 0) * s.d; });
-  lb.init(wave, lane, [&](int r) { return proj + (int64_t)(n0 + r < s.d ? n0 + r : 0) * s.d; });
+  const auto init = [&](int id) __attribute__((always_inline)) {
+    int n_seq, m0, n0;
+    tile(id, n_seq, m0, n0);
+    const __bf16 *cs = c + (int64_t)n_seq * s.Lp * s.d;
+    la.init(wave, lane, [&](int r) { return cs + (int64_t)(m0 + r < P ? m0 + r : 0) * s.d; });
+    lb.init(wave, lane, [&](int r) { return proj + (int64_t)(n0 + r < s.d ? n0 + r : 0) * s.d; });
+  };
   int brow[C::NJ];
 #pragma unroll
   for (int j = 0; j < C::NJ; ++j) brow[j] = wn * C::WTN + C::FM * j;
   typename C::acc_t acc[C::MI][C::NJ];
-  zero_acc<C>(acc);
-  const auto koff = [](int st, int64_t &ka, int64_t &kb) { ka = kb = (int64_t)st * C::BK; };
-  if constexpr (PL)
-    kloop_dma_pl<C, 2, true>(smem, la, lb, s.d / C::BK, wave, lane, wm * C::WTM, brow, acc, koff,
-                       [](int) {}, [](int) {});
-  else
-    kloop_dma<2>(smem, la, lb, s.d / C::BK, wave, koff, [&](const __bf16 *As, const __bf16 *Bs) {
-      mma_stage<C>(As, Bs, wm * C::WTM, brow, lane, acc);
-    });
-
-  __bf16 *vts = vt + (int64_t)n_seq * s.d * s.Lp;
+  const auto epilogue = [&](int id) __attribute__((always_inline)) {
+    int n_seq, m0, n0;
+    tile(id, n_seq, m0, n0);
+    __bf16 *vts = vt + (int64_t)n_seq * s.d * s.Lp;
 #pragma unroll
-  for (int i = 0; i < C::MI; ++i)
+    for (int i = 0; i < C::MI; ++i)
 #pragma unroll
-    for (int j = 0; j < C::NJ; ++j)
+      for (int j = 0; j < C::NJ; ++j)
 #pragma unroll
-      for (int g = 0; g < M::NG; ++g) {
-        const int p = m0 + wm * C::WTM + C::FM * i + M::rrow(lane, g);
-        const int n = n0 + wn * C::WTN + C::FM * j + M::rcol(lane);
-        if (p < P && n < s.d) {
-          const f32x4 a4 = get4(acc[i][j], g);
-          bf16x4 v;
+        for (int g = 0; g < M::NG; ++g) {
+          const int p = m0 + wm * C::WTM + C::FM * i + M::rrow(lane, g);
+          const int n = n0 + wn * C::WTN + C::FM * j + M::rcol(lane);
+          if (p < P && n < s.d) {
+            const f32x4 a4 = get4(acc[i][j], g);
+            bf16x4 v;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = (__bf16)(scale * a4[r]);
-          *(bf16x4 *)(vts + (int64_t)n * s.Lp + p) = v;
+            for (int r = 0; r < 4; ++r) v[r] = (__bf16)(scale * a4[r]);
+            *(bf16x4 *)(vts + (int64_t)n * s.Lp + p) = v;
+          }
         }
-      }
+  };
+  run_tiles<C, PERS>(smem, la, lb, per_seq * s.n_seq, s.d / C::BK, wave, lane, wm * C::WTM, brow,
+                     acc, init, epilogue);
 }
 
 // ---------------------------------------------------------------------------
@@ -652,25 +663,27 @@ inline int device_cus() {
   return cus[dev];
 }
 
-template <class C, bool PL = false, bool PERS = false>
+// persistent kernels run one block per CU (their stages fill most of a CU's LDS)
+template <class C, bool PERS>
 hipError_t launch_gateup(const Slab &s, const __bf16 *x, const Weights &w, const WsPtrs &ws,
                          hipStream_t st, __bf16 *at = nullptr, __bf16 *ut = nullptr) {
   const int64_t P = (int64_t)s.nc * s.Bp;
   const int64_t ntiles =
       ((P + C::BM - 1) / C::BM) * ((s.F + C::BN / 2 - 1) / (C::BN / 2)) * s.n_seq;
-  // persistent: one block per CU (the stages fill most of a CU's LDS)
   const int64_t nb = PERS ? std::min<int64_t>(ntiles, device_cus()) : ntiles;
-  hipLaunchKernelGGL((k_gateup<C, PL, PERS>), dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, x,
+  hipLaunchKernelGGL((k_gateup<C, PERS>), dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, x,
                      (const __bf16 *)w.w_gate, (const __bf16 *)w.w_up, (__bf16 *)ws.zt, at, ut);
   return hipGetLastError();
 }
 
-template <class C, bool PL = false>
+template <class C, bool PERS>
 hipError_t launch_proj(const Slab &s, const Weights &w, const WsPtrs &ws, hipStream_t st) {
   const int64_t P = (int64_t)s.nc * s.Bp;
-  const int64_t nb = ((P + C::BM - 1) / C::BM) * ((s.d + C::BN - 1) / C::BN) * s.n_seq;
-  hipLaunchKernelGGL((k_proj<C, PL>), dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, (const __bf16 *)ws.c,
-                     (const __bf16 *)w.proj, (__bf16 *)ws.vt, s.mse ? 1.f : s.eta);
+  const int64_t ntiles = ((P + C::BM - 1) / C::BM) * ((s.d + C::BN - 1) / C::BN) * s.n_seq;
+  const int64_t nb = PERS ? std::min<int64_t>(ntiles, device_cus()) : ntiles;
+  hipLaunchKernelGGL((k_proj<C, PERS>), dim3((unsigned)nb), dim3(C::NTHR), 0, st, s,
+                     (const __bf16 *)ws.c, (const __bf16 *)w.proj, (__bf16 *)ws.vt,
+                     s.mse ? 1.f : s.eta);
   return hipGetLastError();
 }
 
@@ -800,7 +813,7 @@ hipError_t mf_conv(const Slab &s, const __bf16 *e, const Weights &w, const WsPtr
 }
 hipError_t mf_gateup(const Slab &s, const __bf16 *x, const Weights &w, const WsPtrs &ws,
                      hipStream_t st) {
-  return mfma::launch_gateup<mfma::GateUpCfg, true, true>(s, x, w, ws, st);
+  return mfma::launch_gateup<mfma::GateUpCfg, true>(s, x, w, ws, st);
 }
 hipError_t mf_proj(const Slab &s, const Weights &w, const WsPtrs &ws, hipStream_t st) {
   return mfma::launch_proj<mfma::ProjCfg, true>(s, w, ws, st);
@@ -844,7 +857,7 @@ hipError_t mf_update_one(const Slab &s, int j, const WsPtrs &ws, float *w_state,
 }
 hipError_t mf_gateup_pre(const Slab &s, const __bf16 *x, const Weights &w, const WsPtrs &ws,
                          __bf16 *at, __bf16 *ut, hipStream_t st) {
-  return mfma::launch_gateup<mfma::GateUpCfg, true, true>(s, x, w, ws, st, at, ut);
+  return mfma::launch_gateup<mfma::GateUpCfg, true>(s, x, w, ws, st, at, ut);
 }
 hipError_t mf_update_reverse(const Slab &s, const __bf16 *zt, const __bf16 *bt, float *g,
                              __bf16 *snap, hipStream_t st) {

@@ -2,8 +2,8 @@
 // shapes and their lane maps, the block configuration Cfg, register-staged
 // global -> LDS loaders for K-contiguous and K-major (transposed) operands and
 // direct global -> LDS copies for K-contiguous ones, one LDS stage of MFMAs for
-// each operand layout, the double-buffered K loops (register-staged, direct
-// copies, direct copies with pipelined fragments), XCD-aware block numbering
+// each operand layout, the double-buffered K loops (register-staged; direct
+// copies with pipelined fragments, per tile or persistent), XCD-aware block numbering
 // and the slab row -> token map. Device code only; included by the .hip files
 // that build kernels from these pieces.
 #pragma once
@@ -496,41 +496,6 @@ struct DmaLoader {
                                        0);
   }
 };
-
-// K loop over nk steps with NS LDS stages (A then B) filled by direct copies,
-// NS - 1 steps ahead. koff(s, ka, kb) gives step s's element offsets for the A
-// and B sources; mma(As, Bs) runs one stage. One barrier per step.
-template <int NS, class LA, class LB, class Koff, class Mma>
-__device__ __forceinline__ void kloop_dma(__bf16 *smem, const LA &la, const LB &lb, int nk,
-                                          int wave, Koff koff, Mma mma) {
-  constexpr int AS = LA::STAGE, ST = LA::STAGE + LB::STAGE;
-  constexpr int IPW = LA::NI + LB::NI;
-  int64_t ka, kb;
-#pragma unroll
-  for (int p = 0; p < NS - 1; ++p)
-    if (p < nk) {
-      koff(p, ka, kb);
-      la.issue(smem + p * ST, wave, ka);
-      lb.issue(smem + p * ST + AS, wave, kb);
-    }
-  int cur = 0, nxt = NS - 1;
-  for (int s = 0; s < nk; ++s) {
-    if (s + NS - 2 < nk)
-      wait_vm<(NS - 2) * IPW>();  // step s landed; later steps may be in flight
-    else
-      wait_vm<0>();
-    lds_barrier();
-    if (s + NS - 1 < nk) {
-      koff(s + NS - 1, ka, kb);
-      la.issue(smem + nxt * ST, wave, ka);
-      lb.issue(smem + nxt * ST + AS, wave, kb);
-    }
-    mma(smem + cur * ST, smem + cur * ST + AS);
-    cur = cur + 1 == NS ? 0 : cur + 1;
-    nxt = nxt + 1 == NS ? 0 : nxt + 1;
-  }
-  lds_barrier();  // the stages are free for a following loop
-}
 
 // The operand fragments of one MFMA sub-step (K = M::K) of a stage.
 template <class C>
