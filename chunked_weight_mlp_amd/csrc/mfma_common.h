@@ -649,7 +649,8 @@ __device__ __forceinline__ void kloop_dma_pl(__bf16 *smem, const LA &la, const L
 // boundaries, so a tile's first stages land during the previous tile's last
 // steps, and epi(t) (tile t's epilogue, from the accumulators) runs between
 // tile t's last MFMAs and tile t + 1's first, with t + 1's first fragments
-// already in registers; its stores drain under the next tile's MFMAs.
+// already in registers; its stores stay in flight over t + 1's first MFMA
+// sub-step (the next vmcnt wait covers them).
 // next(t) points the loaders at tile t (called before tile t's first copy);
 // koff(s, ka, kb) gives step s's offsets within a tile.
 template <class C, int NS, bool IL, int ND, class LA, class LB, class Ldf, class Koff, class Next,
