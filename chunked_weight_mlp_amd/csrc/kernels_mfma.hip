@@ -35,6 +35,7 @@
 //   k_conv     depthwise conv of E, vector loads, sliding window.
 
 #include <algorithm>
+#include <atomic>
 
 #include "mfma_common.h"
 
@@ -649,18 +650,19 @@ __global__ __launch_bounds__(256) void k_conv(Slab s, const __bf16 *__restrict__
 }
 
 // ---- launchers (templated on the block configuration) ---------------------
-// Compute units of the current device (cached per device).
+// Compute units of the current device, cached per device (relaxed atomics:
+// handles may launch from several threads; every writer stores the same value).
 inline int device_cus() {
-  static int cus[64] = {0};
+  static std::atomic<int> cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cus[dev]) {
-    int n = 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n < 1) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
       n = 256;
-    cus[dev] = n;
+    cus[dev].store(n, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return n;
 }
 
 // persistent kernels run one block per CU (their stages fill most of a CU's LDS)
