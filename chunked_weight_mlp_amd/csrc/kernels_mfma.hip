@@ -250,7 +250,7 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
 // d_ff), plus, when pt is given, the updates of the group's earlier chunks as
 // P (eta V), P^T read from the Gram buffer. The MSE rule (G = 1) also writes
 // Rt = eta (V - O)^T.
-template <class C>
+template <class C, bool IL = false>
 __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC))) void k_apply(
     Slab s, int q0, int nq, const __bf16 *__restrict__ zt, const __bf16 *__restrict__ snap,
     int64_t snap_seq_stride, int64_t snap_group_stride, const __bf16 *__restrict__ pt,
@@ -305,7 +305,10 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
     const int n = n0 + r0 + C::RPP * i;
     lb.ptr[i] = ss + (int64_t)(n < s.d ? n : 0) * s.F;
   }
-  kloop_t<C>(smem, la, lb, s.F / C::BK, tid, wm * C::WTM, brow, acc);
+  if constexpr (IL)
+    kloop_t_il<C>(smem, la, lb, s.F / C::BK, tid, wm * C::WTM, brow, acc);
+  else
+    kloop_t<C>(smem, la, lb, s.F / C::BK, tid, wm * C::WTM, brow, acc);
 
   if (pts && cs_last > 0) {
     la.ld = RG;
@@ -694,27 +697,28 @@ inline int slab_groups(const Slab &s) { return (s.nc + s.G - 1) / s.G; }
 
 // Apply with every operand explicit: snapshot q0 + i at snap + n * snap_seq +
 // i * snap_group; residual (MSE) to rt + n * rt_seq + c * rt_ld + row.
-template <class C>
+// IL: the interleaved loop for blocks of two waves per SIMD (eight-wave blocks)
+template <class C, bool IL = (C::WM * C::WN >= 8)>
 hipError_t launch_apply_x(const Slab &s, int q0, int nq, const __bf16 *zt, const __bf16 *snap,
                           int64_t snap_seq, int64_t snap_group, const __bf16 *pt, float *o,
                           const __bf16 *vt, __bf16 *rt, int64_t rt_seq, int64_t rt_ld,
                           hipStream_t st) {
   const int64_t RG = (int64_t)s.G * s.Bp;
   const int64_t nb = ((RG + C::BM - 1) / C::BM) * ((s.d + C::BN - 1) / C::BN) * nq * s.n_seq;
-  hipLaunchKernelGGL(k_apply<C>, dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, q0, nq, zt, snap,
+  hipLaunchKernelGGL((k_apply<C, IL>), dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, q0, nq, zt, snap,
                      snap_seq, snap_group, pt, (int64_t)s.ng_cap * RG * RG, o, vt, rt, rt_seq,
                      rt_ld);
   return hipGetLastError();
 }
 
-template <class C>
+template <class C, bool IL = (C::WM * C::WN >= 8)>
 hipError_t launch_apply(const Slab &s, int q0, int nq, const WsPtrs &ws, float *o,
                         hipStream_t st) {
   const int64_t dF = (int64_t)s.d * s.F;
   const int64_t snap_seq = s.mse ? dF : (int64_t)s.ng_cap * dF;
   const int64_t snap_group = s.mse ? 0 : dF;
   const __bf16 *snap = (const __bf16 *)ws.s + (s.mse ? 0 : (int64_t)q0 * dF);
-  return launch_apply_x<C>(s, q0, nq, (const __bf16 *)ws.zt, snap, snap_seq, snap_group,
+  return launch_apply_x<C, IL>(s, q0, nq, (const __bf16 *)ws.zt, snap, snap_seq, snap_group,
                            s.G > 1 ? (const __bf16 *)ws.p : nullptr, o, (const __bf16 *)ws.vt,
                            s.mse ? (__bf16 *)ws.rt : nullptr, (int64_t)s.d * s.Bp, s.Bp, st);
 }
