@@ -110,7 +110,10 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
         for (int i = 0; i < C::B_PIECES; ++i)
           lb.ptr[i] = pb + min((int64_t)n0 + r0 + C::RPP * i, Bo.lim - 1) * Bo.ld;
       }
-      kloop_g<C, TA, TB>(smem, la, lb, g.ph[ph].K / C::BK, tid, wm * C::WTM, brow, acc);
+      if constexpr (C::WM * C::WN >= 8)  // two waves per SIMD: interleaved loop
+        kloop_g_il<C, TA, TB>(smem, la, lb, g.ph[ph].K / C::BK, tid, wm * C::WTM, brow, acc);
+      else
+        kloop_g<C, TA, TB>(smem, la, lb, g.ph[ph].K / C::BK, tid, wm * C::WTM, brow, acc);
     }
   }
 #pragma unroll

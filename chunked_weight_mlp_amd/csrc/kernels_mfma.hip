@@ -306,7 +306,7 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
     lb.ptr[i] = ss + (int64_t)(n < s.d ? n : 0) * s.F;
   }
   if constexpr (IL)
-    kloop_t_il<C>(smem, la, lb, s.F / C::BK, tid, wm * C::WTM, brow, acc);
+    kloop_g_il<C, true, false>(smem, la, lb, s.F / C::BK, tid, wm * C::WTM, brow, acc);
   else
     kloop_t<C>(smem, la, lb, s.F / C::BK, tid, wm * C::WTM, brow, acc);
 
@@ -320,7 +320,10 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
       const int n = n0 + r0 + C::RPP * i;
       lb.ptr[i] = vts + (int64_t)(n < s.d ? n : 0) * s.Lp + row0;
     }
-    kloop_t<C>(smem, la, lb, cs_last / C::BK, tid, wm * C::WTM, brow, acc);
+    if constexpr (IL)
+      kloop_g_il<C, true, false>(smem, la, lb, cs_last / C::BK, tid, wm * C::WTM, brow, acc);
+    else
+      kloop_t<C>(smem, la, lb, cs_last / C::BK, tid, wm * C::WTM, brow, acc);
   }
 
   float *os = o ? o + n_seq * s.x_seq_stride : nullptr;  // nullptr: residual only
@@ -401,7 +404,10 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
   for (int jj = 0; jj < C::NJ; ++jj) brow[jj] = wn * C::WTN + C::FM * jj;
   typename C::acc_t acc[C::MI][C::NJ];
   zero_acc<C>(acc);
-  kloop_tt<C>(smem, la, lb, s.F / C::BK, tid, wm * C::WTM, brow, acc);
+  if constexpr (C::WM * C::WN >= 8)  // two waves per SIMD: interleaved loop
+    kloop_g_il<C, true, true>(smem, la, lb, s.F / C::BK, tid, wm * C::WTM, brow, acc);
+  else
+    kloop_tt<C>(smem, la, lb, s.F / C::BK, tid, wm * C::WTM, brow, acc);
 
   __bf16 *pts = pt + n_seq * pt_seq_stride + (int64_t)q * RG * RG;
 #pragma unroll

@@ -319,64 +319,6 @@ __device__ __forceinline__ void kloop_t(__bf16 *smem, LoaderT<C, C::BM> &la,
   }
 }
 
-// kloop_t with the step's memory work spread among its MFMAs: the next step's
-// global loads between the first sub-steps' MFMAs, its LDS writes between the
-// last sub-step's MFMAs (all waves leave each barrier together, so bursts of
-// memory instructions before or after the MFMAs leave the SIMDs idle). The
-// last step (no next stage) is peeled so each main-loop step is one block.
-template <class C>
-__device__ __forceinline__ void kloop_t_il(__bf16 *smem, LoaderT<C, C::BM> &la,
-                                           Loader<C, C::B_PIECES> &lb, int nk, int tid, int arow0,
-                                           const int (&brow)[C::NJ],
-                                           typename C::acc_t (&acc)[C::MI][C::NJ]) {
-  constexpr int NU = C::BK / C::M::K;
-  static_assert(NU >= 2, "two or more MFMA sub-steps per stage");
-  constexpr int NV = LoaderT<C, C::BM>::NP + C::B_PIECES;  // loads (and LDS writes) per step
-  constexpr int NMF = C::MI * C::NJ;
-  static_assert(NV <= NMF, "more memory instructions than MFMAs to hide them");
-  __bf16 *const Bbase = smem + 2 * C::AT_STAGE;
-  const int lane = tid & 63, r0 = tid / C::KP, q = tid % C::KP;
-  la.fetch(0);
-  lb.fetch(0, q);
-  la.stash(smem, tid);
-  lb.stash(Bbase, r0, q);
-  __syncthreads();
-  const auto step = [&](int s, auto more) __attribute__((always_inline)) {
-    constexpr bool MORE = decltype(more)::value;
-    const int cur = s & 1;
-    if constexpr (MORE) {
-      la.fetch((s + 1) * C::BK);
-      lb.fetch((s + 1) * C::BK, q);
-    }
-    mma_stage_t<C, false, 0, NU - 1>(smem + cur * C::AT_STAGE, Bbase + cur * C::B_STAGE, arow0,
-                                     brow, lane, acc);
-    if constexpr (MORE) {
-#pragma unroll
-      for (int k = 0; k < NV; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    mma_stage_t<C, false, NU - 1>(smem + cur * C::AT_STAGE, Bbase + cur * C::B_STAGE, arow0, brow,
-                                  lane, acc);
-    if constexpr (MORE) {
-      la.stash(smem + (cur ^ 1) * C::AT_STAGE, tid);
-      lb.stash(Bbase + (cur ^ 1) * C::B_STAGE, r0, q);
-#pragma unroll
-      for (int k = 0; k < NV; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
-  };
-  int s = 0;
-  for (; s + 1 < nk; ++s) step(s, std::true_type());
-  if (s < nk) step(s, std::false_type());
-}
-
 // Both operands K-major in memory (the Gram product of Zt with itself).
 template <class C>
 __device__ __forceinline__ void kloop_tt(__bf16 *smem, LoaderT<C, C::BM> &la,
@@ -495,6 +437,67 @@ __device__ __forceinline__ void kloop_g(__bf16 *smem, typename GLoaders<C, TA, T
                                           brow, lane, acc);
     __syncthreads();
   }
+}
+
+// kloop_g with each step's memory work spread among its MFMAs, for blocks of
+// two waves per SIMD: the next step's global loads between the first
+// sub-steps' MFMAs, its LDS writes between the last sub-step's MFMAs (all
+// waves leave each barrier together, so bursts of memory instructions before
+// or after the MFMAs leave the SIMDs idle). The last step (no next stage) is
+// peeled, so each main-loop step is one block. Same arithmetic as kloop_g.
+template <class C, bool TA, bool TB>
+__device__ __forceinline__ void kloop_g_il(__bf16 *smem, typename GLoaders<C, TA, TB>::LA &la,
+                                           typename GLoaders<C, TA, TB>::LB &lb, int nk, int tid,
+                                           int arow0, const int (&brow)[C::NJ],
+                                           typename C::acc_t (&acc)[C::MI][C::NJ]) {
+  using GL = GLoaders<C, TA, TB>;
+  constexpr int NU = C::BK / C::M::K;
+  static_assert(NU >= 2, "two or more MFMA sub-steps per stage");
+  constexpr int NVA = TA ? LoaderT<C, C::BM>::NP : C::A_PIECES;
+  constexpr int NVB = TB ? LoaderT<C, C::BN>::NP : C::B_PIECES;
+  constexpr int NV = NVA + NVB;  // global loads (and LDS writes) per step
+  static_assert(NV <= C::MI * C::NJ, "more memory instructions than MFMAs to hide them");
+  __bf16 *const Bbase = smem + 2 * GL::A_ST;
+  const int lane = tid & 63, r0 = tid / C::KP, q = tid % C::KP;
+  gfetch(la, 0, q);
+  gfetch(lb, 0, q);
+  gstash(la, smem, tid, r0, q);
+  gstash(lb, Bbase, tid, r0, q);
+  __syncthreads();
+  const auto step = [&](int s, auto more) __attribute__((always_inline)) {
+    constexpr bool MORE = decltype(more)::value;
+    const int cur = s & 1;
+    if constexpr (MORE) {
+      gfetch(la, (s + 1) * C::BK, q);
+      gfetch(lb, (s + 1) * C::BK, q);
+    }
+    mma_stage_g<C, TA, TB, 0, NU - 1>(smem + cur * GL::A_ST, Bbase + cur * GL::B_ST, arow0, brow,
+                                      lane, acc);
+    if constexpr (MORE) {
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    mma_stage_g<C, TA, TB, NU - 1>(smem + cur * GL::A_ST, Bbase + cur * GL::B_ST, arow0, brow,
+                                   lane, acc);
+    if constexpr (MORE) {
+      gstash(la, smem + (cur ^ 1) * GL::A_ST, tid, r0, q);
+      gstash(lb, Bbase + (cur ^ 1) * GL::B_ST, tid, r0, q);
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+  };
+  int s = 0;
+  for (; s + 1 < nk; ++s) step(s, std::true_type());
+  if (s < nk) step(s, std::false_type());
 }
 
 // ---- direct global -> LDS loads (K-contiguous operands, swizzled rows) -------
