@@ -123,6 +123,14 @@ def test_bf16_small_shapes(flags, update, L, Bc):
     check_against_oracle(w, flags=flags, seq_len=L)
 
 
+def test_bf16_persistent_uneven_tiles():
+    """Persistent gate/up and proj blocks with tile counts that do not split
+    evenly over the 8 XCDs: d_ff 4224 and 4224 slab rows give 17 x 33 = 561
+    gate/up tiles (2-3 per block, one XCD with a tile more), proj 17 x 2 = 34."""
+    w = BF16_SMALL.replace(d=512, d_ff=4224, chunk=128)
+    check_against_oracle(w, n_seq=1, seq_len=33 * 128)
+
+
 def test_bf16_multi_slab():
     """A workspace for 3 chunks forces several passes over a 9-chunk sequence."""
     check_against_oracle(BF16_SMALL.replace(chunk=64), seq_len=9 * 64 - 5, slab_chunks=3)
