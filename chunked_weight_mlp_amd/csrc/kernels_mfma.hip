@@ -539,12 +539,27 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
     if (f < s.F && c < s.d) *(uint2 *)(sdst + (int64_t)c * s.F + f) = sbuf[q];
   };
   auto slot_piece = [](int k, int e) { return ((k / C::NJ) * PPS + e) * C::NJ + k % C::NJ; };
+  // Pieces q0, q1 of row tiles i and i + 1 of one column tile: lane l holds 4
+  // values (d_ff 4 (l / 16) ..) of each; swapping between lane groups
+  // l / 16 = 0 <-> 1 and 2 <-> 3 leaves every lane 8 consecutive values of its
+  // row, one 16-byte store (64 contiguous bytes per row per instruction).
+  auto store_pair = [&](int q0, int q1) __attribute__((always_inline)) {
+    const int i = q0 / (C::NJ * M::NG), jj = q0 / M::NG % C::NJ;
+    const auto x = __builtin_amdgcn_permlane16_swap(sbuf[q0].x, sbuf[q1].x, false, false);
+    const auto y = __builtin_amdgcn_permlane16_swap(sbuf[q0].y, sbuf[q1].y, false, false);
+    const uint4 v{x[0], y[0], x[1], y[1]};
+    const int gq = lane >> 4;
+    const int f = f0 + wm * C::WTM + C::FM * i + 8 * (gq >> 1) + C::FM * (gq & 1);
+    const int c = cl + C::FM * jj;
+    if (f < s.F && c < s.d) *(uint4 *)(sdst + (int64_t)c * s.F + f) = v;
+  };
+  static_assert(PPS % 2 == 0 && C::FM == 16, "slots store pairs of 16-row tiles");
   auto store_slot = [&](int slot) __attribute__((always_inline)) {
 #pragma unroll
     for (int k = 0; k < NSLOT; ++k)
       if (slot == k)
 #pragma unroll
-        for (int e = 0; e < PPS; ++e) store_piece(slot_piece(k, e));
+        for (int e = 0; e < PPS; e += 2) store_pair(slot_piece(k, e), slot_piece(k, e + 1));
   };
   int gr = 0, gq = 0;            // K step within the group, group (walk order)
   int nslot = NSLOT, nstep = 0;  // next slot to store and the group step it is due at

@@ -131,6 +131,16 @@ def test_bf16_persistent_uneven_tiles():
     check_against_oracle(w, n_seq=1, seq_len=33 * 128)
 
 
+@pytest.mark.parametrize("update", ["linear", "mse"])
+def test_bf16_partial_tiles(update):
+    """d 320 and d_ff 576 (multiples of 64, not of 128 or 256): the last row and
+    column tiles of gate/up, proj, the update scan and the apply are partial, so
+    their bounds checks (loads clamped to a valid row, stores skipped) run."""
+    w = BF16_SMALL.replace(d=320, d_ff=576, update=update,
+                           eta=1e-2 if update == "linear" else 2e-3)
+    check_against_oracle(w, n_seq=2, seq_len=700)
+
+
 def test_bf16_multi_slab():
     """A workspace for 3 chunks forces several passes over a 9-chunk sequence."""
     check_against_oracle(BF16_SMALL.replace(chunk=64), seq_len=9 * 64 - 5, slab_chunks=3)
