@@ -142,43 +142,66 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
     int n_seq, m0, f0;
     tile(id, n_seq, m0, f0);
     __bf16 *zts = zt + (int64_t)n_seq * s.F * s.Lp;
+    // Row tiles i and i + 1 together: lane l holds rows (tokens) 4 (l / 16) ..
+    // + 3 of each at its column f; swapping between lane groups l / 16 = 0 <-> 1
+    // and 2 <-> 3 leaves every lane 8 consecutive tokens of its column, one
+    // 16-byte store (Bp and P are multiples of 64, so an 8-row group is wholly
+    // inside or outside the slab).
+    static_assert(M::NG == 1 && C::MI % 2 == 0, "pairs of 16-row tiles");
+    const int gq = lane >> 4;
+    const auto swap8 = [](bf16x4 a, bf16x4 b) __attribute__((always_inline)) {
+      const uint2 ua = __builtin_bit_cast(uint2, a), ub = __builtin_bit_cast(uint2, b);
+      const auto x = __builtin_amdgcn_permlane16_swap(ua.x, ub.x, false, false);
+      const auto y = __builtin_amdgcn_permlane16_swap(ua.y, ub.y, false, false);
+      return uint4{x[0], y[0], x[1], y[1]};
+    };
 #pragma unroll
-    for (int i = 0; i < C::MI; ++i)
+    for (int i = 0; i < C::MI; i += 2) {
+      // rows p .. p + 3 of each tile lie in one chunk (Bp is a multiple of 4);
+      // chunk-padding rows and tokens past the sequence end are exact zeros
+      bool real[2][4];
 #pragma unroll
-      for (int g = 0; g < M::NG; ++g) {
-        // rows p .. p + 3 lie in one chunk (Bp is a multiple of 4); chunk-padding
-        // rows and tokens past the sequence end are written as exact zeros
-        const int p = m0 + wm * C::WTM + C::FM * i + M::rrow(lane, g);
+      for (int h = 0; h < 2; ++h) {
+        const int p = m0 + wm * C::WTM + C::FM * (i + h) + M::rrow(lane, 0);
         const int jc = p / s.Bp, ic = p - jc * s.Bp;
         const int64_t t0 = s.tok0 + (int64_t)jc * s.B + ic;
-        bool real[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) real[r] = jc < s.nc && ic + r < s.B && t0 + r < s.L;
-        if (p >= P) continue;
+        for (int r = 0; r < 4; ++r) real[h][r] = jc < s.nc && ic + r < s.B && t0 + r < s.L;
+      }
+      const int pl = m0 + wm * C::WTM + C::FM * i + 8 * (gq >> 1) + C::FM * (gq & 1);
 #pragma unroll
-        for (int j = 0; j < HJ; ++j) {
-          const int f = f0 + wn * WF + C::FM * j + M::rcol(lane);
-          if (f < s.F) {
-            const f32x4 gv = get4(acc[i][j], g), uv = get4(acc[i][j + HJ], g);
-            bf16x4 v;
+      for (int j = 0; j < HJ; ++j) {
+        const int f = f0 + wn * WF + C::FM * j + M::rcol(lane);
+        bf16x4 v[2];
 #pragma unroll
-            for (int r = 0; r < 4; ++r)  // SiLU(a) = a sigmoid(a)
-              v[r] = (__bf16)(real[r] ? gv[r] * fast_sigmoid(gv[r]) * uv[r] : 0.f);
-            *(bf16x4 *)(zts + (int64_t)f * s.Lp + p) = v;
-            if (at) {  // pre-activations, for the backward
-              bf16x4 va, vu;
+        for (int h = 0; h < 2; ++h) {
+          const f32x4 gv = get4(acc[i + h][j], 0), uv = get4(acc[i + h][j + HJ], 0);
 #pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                va[r] = (__bf16)(real[r] ? gv[r] : 0.f);
-                vu[r] = (__bf16)(real[r] ? uv[r] : 0.f);
-              }
-              const int64_t off = (int64_t)n_seq * s.F * s.Lp + (int64_t)f * s.Lp + p;
-              *(bf16x4 *)(at + off) = va;
-              *(bf16x4 *)(ut + off) = vu;
+          for (int r = 0; r < 4; ++r)  // SiLU(a) = a sigmoid(a)
+            v[h][r] = (__bf16)(real[h][r] ? gv[r] * fast_sigmoid(gv[r]) * uv[r] : 0.f);
+        }
+        const uint4 z = swap8(v[0], v[1]);
+        if (pl < P && f < s.F) *(uint4 *)(zts + (int64_t)f * s.Lp + pl) = z;
+        if (at) {  // pre-activations, for the backward
+          bf16x4 va[2], vu[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const f32x4 gv = get4(acc[i + h][j], 0), uv = get4(acc[i + h][j + HJ], 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              va[h][r] = (__bf16)(real[h][r] ? gv[r] : 0.f);
+              vu[h][r] = (__bf16)(real[h][r] ? uv[r] : 0.f);
             }
+          }
+          const uint4 za = swap8(va[0], va[1]), zu = swap8(vu[0], vu[1]);
+          const int64_t off = (int64_t)n_seq * s.F * s.Lp + (int64_t)f * s.Lp + pl;
+          if (pl < P && f < s.F) {
+            *(uint4 *)(at + off) = za;
+            *(uint4 *)(ut + off) = zu;
           }
         }
       }
+    }
   };
 
   run_tiles<C, PERS>(smem, la, lb, per_seq * s.n_seq, s.d / C::BK, wave, lane, wm * C::WTM, brow,
