@@ -119,6 +119,22 @@ def test_backward_mse_small_shapes(Bc, L, N, with_dwf):
     compare(to_pages(g), oracle_backward(w, weights, x, e, d_o, d_wf), f"mse B={Bc}")
 
 
+@pytest.mark.parametrize("update", ["linear", "mse"])
+def test_backward_partial_tiles(update):
+    """d 320 and d_ff 576 (multiples of 64, not of 128 or 256): the last row and
+    column tiles of every backward GEMM, transpose and scan are partial."""
+    w = SMALL.replace(d=320, d_ff=576, chunk=128, seq_len=600, n_seq=2, update=update,
+                      eta=1e-2 if update == "linear" else 2e-3)
+    weights = wl.make_weights(w)
+    x, e = wl.make_inputs(w)
+    d_o, d_wf = wl.make_upstream(w)
+    say(f"[backward] partial tiles {update} d={w.d} F={w.d_ff} B=128 L=600 N=2")
+    layer = make_layer(w, weights, 2)
+    g = layer.backward(x.to(DEV), e.to(DEV), d_o.to(DEV), d_wf.to(DEV))
+    torch.cuda.synchronize()
+    compare(to_pages(g), oracle_backward(w, weights, x, e, d_o, d_wf), f"partial {update}")
+
+
 def test_backward_mse_1p5b_shape():
     """The 1.5B pretraining layer (d 2048, d_ff 8192, MSE rule): two sequences of
     three chunks of 512 and a tail."""
