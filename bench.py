@@ -346,7 +346,7 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the library runs on one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
     if not torch.cuda.is_available():
