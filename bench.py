@@ -96,8 +96,9 @@ HBM_PEAK = 8000.0                       # GB/s
 def achievable_peaks() -> dict:
     """The chip's achievable rates, measured here by the library's micro-benchmarks
     (ipttt_probe): bf16 MFMA issue at two waves per SIMD for each MFMA shape, with
-    no memory traffic, and a streaming read of 4 GiB (more than the caches hold).
-    Best of a few launches, HIP events on the launch stream."""
+    no memory traffic, a streaming read of 4 GiB (more than the caches hold),
+    conflict-free LDS reads and direct copies from L2 into LDS. Best of a few
+    launches, HIP events on the launch stream."""
     from chunked_weight_mlp_amd import ipttt
     dev = "cuda:0"
     stream = torch.cuda.current_stream()
@@ -121,9 +122,12 @@ def achievable_peaks() -> dict:
     m16 = best(ipttt.IPTTT_PROBE_MFMA16, 20000, None) / 1e12
     m32 = best(ipttt.IPTTT_PROBE_MFMA32, 20000, None) / 1e12
     rd = best(ipttt.IPTTT_PROBE_READ, nbytes, ctypes.c_void_p(src.data_ptr())) / 1e9
+    lds = best(ipttt.IPTTT_PROBE_LDS, 20000, None) / 1e12
+    cp = best(ipttt.IPTTT_PROBE_COPY, 4000, ctypes.c_void_p(src.data_ptr())) / 1e12
     del src
     return {"mfma16_bf16_tflops": round(m16, 1), "mfma32_bf16_tflops": round(m32, 1),
             "mfma_bf16_tflops": round(max(m16, m32), 1), "hbm_read_gbps": round(rd, 1),
+            "lds_read_tbps": round(lds, 2), "l2_to_lds_copy_tbps": round(cp, 2),
             "source": "ipttt_probe micro-benchmarks on this GPU"}
 
 

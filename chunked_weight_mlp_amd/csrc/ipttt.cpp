@@ -277,10 +277,14 @@ ipttt_status ipttt_profile_end(ipttt_layer *h, int32_t *launches, double *ms) {
 
 ipttt_status ipttt_probe(int32_t kind, int64_t n, const void *src, void *dst, size_t dst_bytes,
                          double *work, void *hip_stream) {
-  if (kind != IPTTT_PROBE_MFMA16 && kind != IPTTT_PROBE_MFMA32 && kind != IPTTT_PROBE_READ)
+  if (kind != IPTTT_PROBE_MFMA16 && kind != IPTTT_PROBE_MFMA32 && kind != IPTTT_PROBE_READ &&
+      kind != IPTTT_PROBE_LDS && kind != IPTTT_PROBE_COPY)
     return fail(IPTTT_E_INVALID, "unknown probe kind %d", kind);
   if (!dst || !work || n < 1) return fail(IPTTT_E_INVALID, "dst and work must be non-NULL, n >= 1");
-  if (kind == IPTTT_PROBE_READ && !src) return fail(IPTTT_E_INVALID, "read probe needs src");
+  if ((kind == IPTTT_PROBE_READ || kind == IPTTT_PROBE_COPY) && !src)
+    return fail(IPTTT_E_INVALID, "read and copy probes need src");
+  if (kind == IPTTT_PROBE_COPY && ((uintptr_t)src & 15))
+    return fail(IPTTT_E_INVALID, "copy probe src must be 16-byte aligned");
   const hipError_t e =
       ipttt::probe_launch(kind, n, src, dst, dst_bytes, work, (hipStream_t)hip_stream);
   if (e == hipErrorInvalidValue) return fail(IPTTT_E_INVALID, "probe buffers do not fit");

@@ -1,6 +1,7 @@
 // Measurement-only micro-benchmarks of the chip's achievable rates, against
 // which the layer's kernels are reported: MFMA issue with no memory traffic
-// (two waves per SIMD, independent accumulators) and a streaming read.
+// (two waves per SIMD, independent accumulators), a streaming read, LDS reads
+// and direct copies from L2 into LDS.
 #include "internal.h"
 
 namespace ipttt {
@@ -86,6 +87,56 @@ __global__ __launch_bounds__(kProbeThreads) void k_probe_read(const uint4 *__res
   out[(int64_t)blockIdx.x * kProbeThreads + threadIdx.x] = acc;
 }
 
+// LDS reads: two 256-thread blocks per CU (two waves per SIMD) each fill 32 KB
+// of LDS, then read it n times over in 16-byte pieces (four per thread per
+// iteration, a wave's 64 pieces contiguous, so no bank conflicts), folded into
+// one value per thread (stored so the reads are kept)
+constexpr int kProbeLdsBytes = 32 * 1024;
+__global__ __launch_bounds__(kProbeThreads) void k_probe_lds(unsigned *__restrict__ out,
+                                                             int64_t iters) {
+  __shared__ uint4 buf[kProbeLdsBytes / 16];
+  constexpr int N = kProbeLdsBytes / 16;
+  for (int i = threadIdx.x; i < N; i += kProbeThreads)
+    buf[i] = uint4{(unsigned)i, (unsigned)i * 3u, (unsigned)i * 5u, (unsigned)i * 7u};
+  __syncthreads();
+  unsigned acc = 0;
+  for (int64_t it = 0; it < iters; ++it) {
+    const int base = (int)((it * 4 * kProbeThreads) % N);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint4 v = buf[(base + k * kProbeThreads + threadIdx.x) % N];
+      acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    asm volatile("" ::: "memory");  // each iteration's reads stay in it
+  }
+  out[(int64_t)blockIdx.x * kProbeThreads + threadIdx.x] = acc;
+}
+// Direct global -> LDS copies from L2: four-wave blocks, two per CU, each copy
+// 8 KB per wave and iteration (eight 1 KB global_load_lds_dwordx4) from a
+// 64 KB window of src into a two-half 32 KB LDS ring, with two iterations in
+// flight; the 64 windows (4 MiB) stay in L2 after the first pass.
+typedef __attribute__((address_space(3))) void probe_lds_t;
+typedef __attribute__((address_space(1))) const void probe_gbl_t;
+__global__ __launch_bounds__(kProbeThreads) void k_probe_copy(const char *__restrict__ src,
+                                                              int64_t iters) {
+  __shared__ __attribute__((aligned(1024))) char ring[32768];
+  constexpr int NW = kProbeThreads / 64;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const char *win = src + (int64_t)(blockIdx.x % 64) * 65536;
+  for (int64_t it = 0; it < iters; ++it) {
+    char *half = ring + (it & 1) * 16384;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t off = ((it * 8 + i) * 1024 + wave * 8192) % 65536;
+      __builtin_amdgcn_global_load_lds((probe_gbl_t *)(win + off + lane * 16),
+                                       (probe_lds_t *)(half + ((i * NW + wave) % 16) * 1024), 16,
+                                       0, 0);
+    }
+    // the previous iteration's copies landed (this one's 8 may still fly)
+    asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
 }  // namespace
 
 hipError_t probe_launch(int kind, int64_t n, const void *src, void *dst, size_t dst_bytes,
@@ -107,6 +158,21 @@ hipError_t probe_launch(int kind, int64_t n, const void *src, void *dst, size_t 
                          (float *)dst, n, 1e-3f);
       *work = (double)n * 4 * (2.0 * 32 * 32 * 16) * waves;
     }
+    return hipGetLastError();
+  }
+  if (kind == IPTTT_PROBE_COPY) {
+    const int64_t blocks = 2 * (int64_t)cus;
+    hipLaunchKernelGGL(k_probe_copy, dim3((unsigned)blocks), dim3(kProbeThreads), 0, st,
+                       (const char *)src, n);
+    *work = (double)n * 8 * 1024 * (kProbeThreads / 64) * blocks;
+    return hipGetLastError();
+  }
+  if (kind == IPTTT_PROBE_LDS) {
+    const int64_t blocks = 2 * (int64_t)cus;
+    if (dst_bytes < (size_t)(blocks * kProbeThreads * sizeof(unsigned))) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_probe_lds, dim3((unsigned)blocks), dim3(kProbeThreads), 0, st,
+                       (unsigned *)dst, n);
+    *work = (double)n * 4 * 16 * kProbeThreads * blocks;
     return hipGetLastError();
   }
   // read: n bytes from src, one 32-bit value per thread to dst

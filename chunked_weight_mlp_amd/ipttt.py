@@ -36,6 +36,8 @@ EXPORTS = (
 IPTTT_PROBE_MFMA16 = 0
 IPTTT_PROBE_MFMA32 = 1
 IPTTT_PROBE_READ = 2
+IPTTT_PROBE_LDS = 3
+IPTTT_PROBE_COPY = 4
 
 KERNELS = ("gateup", "conv", "proj", "update", "apply", "snapshot", "gram",  # ipttt_kernel order
            "bw_scan", "bw_dz", "bw_dv", "bw_dx", "bw_dw", "bw_small", "bw_misc")

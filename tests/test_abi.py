@@ -333,6 +333,10 @@ def test_probe_errors_before_device_work(lib):
                                        (B.IPTTT_PROBE_MFMA16, 0, None, buf, True),   # n < 1
                                        (B.IPTTT_PROBE_MFMA32, 10, None, None, True),  # no dst
                                        (B.IPTTT_PROBE_READ, 16, None, buf, True),    # read without src
+                                       (B.IPTTT_PROBE_LDS, 0, None, buf, True),      # n < 1
+                                       (B.IPTTT_PROBE_LDS, 10, None, None, True),    # no dst
+                                       (B.IPTTT_PROBE_COPY, 10, None, buf, True),    # copy without src
+                                       (B.IPTTT_PROBE_COPY, 10, buf + 8, buf, True),  # misaligned src
                                        (B.IPTTT_PROBE_MFMA16, 10, None, buf, False)):  # no work
         work = ctypes.byref(ctypes.c_double()) if work_ok else None
         assert lib.ipttt_probe(kind, n, src, dst, 1 << 20, work, None) == B.IPTTT_E_INVALID
