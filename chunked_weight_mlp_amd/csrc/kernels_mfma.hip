@@ -467,8 +467,11 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
     const __bf16 *__restrict__ bsrc, int64_t b_ld, int64_t b_seq_stride, int64_t b_chunk_stride,
     float *__restrict__ w, __bf16 *__restrict__ snap, int64_t snap_seq_stride,
     int64_t snap_group_stride, int snap_each_group, int snap_after, int reverse) {
-  static_assert(C::SMEM_ELEMS * 2 <= 160 * 1024, "LDS overflow");
-  __shared__ __attribute__((aligned(1024))) __bf16 smem[C::SMEM_ELEMS];
+  // three copy stages of the 128 x 256 tile (144 KB, one block per CU): each
+  // stage's copies are issued two K steps ahead of its fragment reads
+  constexpr int NSU = 3;
+  static_assert(C::SMEM_ELEMS / 2 * NSU * 2 <= 160 * 1024, "LDS overflow");
+  __shared__ __attribute__((aligned(1024))) __bf16 smem[C::SMEM_ELEMS / 2 * NSU];
   using M = typename C::M;
   const int nm = (s.F + C::BM - 1) / C::BM, nn = (s.d + C::BN - 1) / C::BN;
   const int per_seq = nm * nn;
@@ -623,7 +626,7 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
     }
   };
   const int nk = n_chunks * spc;
-  kloop_dma_pl<C, 2, false>(smem, la, lb, nk, wave, lane, wm * C::WTM, brow, acc, koff, pre, post);
+  kloop_dma_pl<C, NSU, true>(smem, la, lb, nk, wave, lane, wm * C::WTM, brow, acc, koff, pre, post);
 #pragma unroll
   for (int k = 0; k < NSLOT; ++k)
     if (k >= nslot)
@@ -835,7 +838,7 @@ using ProjCfg = Cfg<2, 4, 64, 16, 0, 8, 1, 8>;     // direct LDS copies, swizzle
 // bank (a pad of 8 leaves every such read 2-way conflicted).
 using ApplyCfg = Cfg<2, 4, 64, 16, 16, 16>;
 using ApplySmallCfg = Cfg<1, 2, 64, 16, 16, 16>;  // when ApplyCfg would leave most CUs idle
-using UpdateCfg = Cfg<1, 2, 64, 16, 0, 8, 1, 16>;  // direct copies, pipelined fragments
+using UpdateCfg = Cfg<1, 4, 64, 16, 0, 8, 1, 16>;  // direct copies, pipelined, interleaved fragments
 using GramCfg = Cfg<2, 4, 64, 16, 16, 16>;
 static_assert(kChunkAlign % UpdateCfg::BK == 0, "chunk pitch must be whole update K steps");
 // The Gram computes, per m tile, the columns the apply's m tiles read: its m
