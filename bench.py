@@ -99,7 +99,7 @@ def achievable_peaks() -> dict:
     no memory traffic, a streaming read of 4 GiB (more than the caches hold),
     conflict-free LDS reads and direct copies from L2 into LDS. Best of a few
     launches, HIP events on the launch stream."""
-    from chunked_weight_mlp_amd import ipttt
+    from chunked_weight_mlp_amd import probe
     dev = "cuda:0"
     stream = torch.cuda.current_stream()
     sp = ctypes.c_void_p(stream.cuda_stream)
@@ -112,18 +112,18 @@ def achievable_peaks() -> dict:
         for _ in range(reps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            work = ipttt.ipttt_probe(kind, n, a, ctypes.c_void_p(out_buf.data_ptr()),
-                                     out_buf.numel() * 4, sp)
+            work = probe.ipttt_probe(kind, n, a, nbytes if a is not None else 0,
+                                     ctypes.c_void_p(out_buf.data_ptr()), out_buf.numel() * 4, sp)
             e1.record(stream)
             e1.synchronize()
             rates.append(work / (e0.elapsed_time(e1) * 1e-3))
         return max(rates)
 
-    m16 = best(ipttt.IPTTT_PROBE_MFMA16, 20000, None) / 1e12
-    m32 = best(ipttt.IPTTT_PROBE_MFMA32, 20000, None) / 1e12
-    rd = best(ipttt.IPTTT_PROBE_READ, nbytes, ctypes.c_void_p(src.data_ptr())) / 1e9
-    lds = best(ipttt.IPTTT_PROBE_LDS, 20000, None) / 1e12
-    cp = best(ipttt.IPTTT_PROBE_COPY, 4000, ctypes.c_void_p(src.data_ptr())) / 1e12
+    m16 = best(probe.IPTTT_PROBE_MFMA16, 20000, None) / 1e12
+    m32 = best(probe.IPTTT_PROBE_MFMA32, 20000, None) / 1e12
+    rd = best(probe.IPTTT_PROBE_READ, nbytes, ctypes.c_void_p(src.data_ptr())) / 1e9
+    lds = best(probe.IPTTT_PROBE_LDS, 20000, None) / 1e12
+    cp = best(probe.IPTTT_PROBE_COPY, 4000, ctypes.c_void_p(src.data_ptr())) / 1e12
     del src
     return {"mfma16_bf16_tflops": round(m16, 1), "mfma32_bf16_tflops": round(m32, 1),
             "mfma_bf16_tflops": round(max(m16, m32), 1), "hbm_read_gbps": round(rd, 1),
@@ -246,8 +246,31 @@ def backward_work(w: wl.Workload, tokens: int):
     }
 
 
+def host_info() -> dict:
+    """The host the oracle runs on: logical CPUs, CPU model, the BLAS numpy
+    calls (vendor, version, threads) and the thread variables in effect."""
+    from threadpoolctl import threadpool_info
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = [dict(api=p.get("internal_api"), version=p.get("version"), threads=p.get("num_threads"),
+                 arch=p.get("architecture")) for p in threadpool_info() if p.get("user_api") == "blas"]
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
+    return {"os_cpu_count": os.cpu_count(), "cpus_in_affinity": affinity, "cpu_model": model,
+            "blas": blas, "env": {k: os.environ.get(k) for k in
+                                  ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")
+                                  if os.environ.get(k) is not None}}
+
+
 def cpu_baseline(w: wl.Workload, x, e, weights, n_chunks: int):
-    import numpy as np  # noqa: F401
     from threadpoolctl import threadpool_info
 
     import oracle
@@ -266,8 +289,11 @@ def cpu_baseline(w: wl.Workload, x, e, weights, n_chunks: int):
         "unit": "tokens/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"first {tokens} tokens ({tokens // w.chunk} chunks) of sequence 0, float64 numpy, "
-                  f"{dt:.1f} s",
+        "sample": f"the oracle's chunk scan (float64 numpy) over the first {tokens} tokens "
+                  f"({-(-tokens // w.chunk)} chunks) of sequence 0 of this workload, {dt:.1f} s; "
+                  f"value = those tokens / that time (the scan's cost per chunk does not depend "
+                  f"on the chunk's position)",
+        "host": host_info(),
     }
 
 
@@ -481,8 +507,9 @@ def cpu_baseline_backward(w: wl.Workload, x, e, weights, d_o, n_chunks: int):
     dt = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"backward over the first {tokens} tokens ({tokens // w.chunk} chunks) of "
-                      f"sequence 0, float64 numpy, {dt:.1f} s"}
+            "sample": f"the oracle's backward (float64 numpy) over the first {tokens} tokens "
+                      f"({-(-tokens // w.chunk)} chunks) of sequence 0, {dt:.1f} s",
+            "host": host_info()}
 
 
 def bench_backward(args, w: wl.Workload):
@@ -654,7 +681,7 @@ def bench_decode(args, w: wl.Workload):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
         out["cpu_baseline"] = {"value": Bc / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
                                "sample": f"decode_steps over one chunk of {Bc} tokens of one sequence, "
-                                         f"float64 numpy, {dt:.1f} s"}
+                                         f"float64 numpy, {dt:.1f} s", "host": host_info()}
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

@@ -176,8 +176,5 @@ hipError_t bw_conv(const Slab &s, const BwBufs &b, const __bf16 *e, const void *
 hipError_t bw_sum_seq(const float *in, int n, int64_t len, float *out, hipStream_t st);
 hipError_t bw_fill(float *p, int64_t n, float v, hipStream_t st);
 
-// micro-benchmark launches behind ipttt_probe (probe.hip)
-hipError_t probe_launch(int kind, int64_t n, const void *src, void *dst, size_t dst_bytes,
-                        double *work, hipStream_t st);
 
 }  // namespace ipttt

@@ -137,11 +137,11 @@ struct ProfScope {
     if (!h->prof) return;
     a = take(h);
     b = take(h);
-    if (a && b) hipEventRecord(a, st);
+    if (a && b) (void)hipEventRecord(a, st);  // best effort: a failed record shows as a zero time
   }
   ~ProfScope() {
     if (!h->prof || !a || !b) return;
-    hipEventRecord(b, st);
+    (void)hipEventRecord(b, st);
     h->recs.push_back({kind, a, b});
   }
 };
@@ -236,7 +236,7 @@ ipttt_status ipttt_init(const ipttt_layer_desc *desc, ipttt_layer **out) {
 
 void ipttt_destroy(ipttt_layer *h) {
   if (!h) return;
-  for (hipEvent_t e : h->all_events) hipEventDestroy(e);
+  for (hipEvent_t e : h->all_events) (void)hipEventDestroy(e);
   delete h;
 }
 
@@ -275,22 +275,6 @@ ipttt_status ipttt_profile_end(ipttt_layer *h, int32_t *launches, double *ms) {
   return st;
 }
 
-ipttt_status ipttt_probe(int32_t kind, int64_t n, const void *src, void *dst, size_t dst_bytes,
-                         double *work, void *hip_stream) {
-  if (kind != IPTTT_PROBE_MFMA16 && kind != IPTTT_PROBE_MFMA32 && kind != IPTTT_PROBE_READ &&
-      kind != IPTTT_PROBE_LDS && kind != IPTTT_PROBE_COPY)
-    return fail(IPTTT_E_INVALID, "unknown probe kind %d", kind);
-  if (!dst || !work || n < 1) return fail(IPTTT_E_INVALID, "dst and work must be non-NULL, n >= 1");
-  if ((kind == IPTTT_PROBE_READ || kind == IPTTT_PROBE_COPY) && !src)
-    return fail(IPTTT_E_INVALID, "read and copy probes need src");
-  if (kind == IPTTT_PROBE_COPY && ((uintptr_t)src & 15))
-    return fail(IPTTT_E_INVALID, "copy probe src must be 16-byte aligned");
-  const hipError_t e =
-      ipttt::probe_launch(kind, n, src, dst, dst_bytes, work, (hipStream_t)hip_stream);
-  if (e == hipErrorInvalidValue) return fail(IPTTT_E_INVALID, "probe buffers do not fit");
-  return hip_status(e, "probe launch");
-}
-
 ipttt_status ipttt_reset_fast_weights(ipttt_layer *h, int32_t first_seq, int32_t n_seq,
                                       void *hip_stream) {
   if (!h) return fail(IPTTT_E_INVALID, "handle is NULL");
@@ -318,7 +302,8 @@ namespace {
 // outputs of those tokens were produced elsewhere, e.g. token by token).
 template <typename T>
 ipttt_status run_scan(ipttt_layer *h, const T *x, const T *e, float *o, int slot0, int n_seq,
-                      int64_t L, int64_t seq_stride, hipStream_t st) {
+                      int64_t L, int64_t seq_stride, void *ws_base, size_t ws_bytes,
+                      hipStream_t st) {
   using namespace ipttt;
   const ipttt_layer_desc &d = h->desc;
   const int elem = (int)sizeof(T);
@@ -334,12 +319,12 @@ ipttt_status run_scan(ipttt_layer *h, const T *x, const T *e, float *o, int slot
   };
   // slab rows are indexed in 32 bits on the device
   int64_t lo = 1, hi = std::min<int64_t>(K, ((int64_t)1 << 30) / Bp);
-  if (layout(1).total > d.workspace_bytes)
-    return fail(IPTTT_E_WORKSPACE, "workspace_bytes=%zu cannot hold one chunk of %d sequences (%zu)",
-                d.workspace_bytes, n_seq, layout(1).total);
+  if (layout(1).total > ws_bytes)
+    return fail(IPTTT_E_WORKSPACE, "workspace of %zu bytes cannot hold one chunk of %d sequences (%zu)",
+                ws_bytes, n_seq, layout(1).total);
   while (lo < hi) {
     const int64_t mid = (lo + hi + 1) / 2;
-    if (layout(mid).total <= d.workspace_bytes)
+    if (layout(mid).total <= ws_bytes)
       lo = mid;
     else
       hi = mid - 1;
@@ -348,7 +333,7 @@ ipttt_status run_scan(ipttt_layer *h, const T *x, const T *e, float *o, int slot
   // slabs of whole groups unless one slab covers the call
   const int nc_cap = (int)(lo < K ? lo / G * G : lo);
   const WsLayout lay = ws_layout(elem, n_seq, d.d, d.d_ff, Bp, nc_cap, G, mse, !h->mfma);
-  char *base = (char *)d.workspace;
+  char *base = (char *)ws_base;
   WsPtrs ws{base + lay.z,  base + lay.zt, base + lay.c, base + lay.vt,
             base + lay.s,  base + lay.rt, base + lay.p};
   Weights w{d.w_gate, d.w_up, d.proj, d.conv_w};
@@ -431,12 +416,36 @@ ipttt_status check_call(ipttt_layer *h, const void *x, const void *e, const floa
   return IPTTT_OK;
 }
 
+// ws_base == nullptr: the descriptor's workspace
 ipttt_status dispatch(ipttt_layer *h, const void *x, const void *e, float *o, int slot0, int n_seq,
-                      int64_t L, int64_t seq_stride, hipStream_t st) {
+                      int64_t L, int64_t seq_stride, hipStream_t st, void *ws_base = nullptr,
+                      size_t ws_bytes = 0) {
+  if (!ws_base) {
+    ws_base = h->desc.workspace;
+    ws_bytes = h->desc.workspace_bytes;
+  }
   if (h->desc.in_dtype == IPTTT_BF16)
     return run_scan<__bf16>(h, (const __bf16 *)x, (const __bf16 *)e, o, slot0, n_seq, L, seq_stride,
-                            st);
-  return run_scan<float>(h, (const float *)x, (const float *)e, o, slot0, n_seq, L, seq_stride, st);
+                            ws_base, ws_bytes, st);
+  return run_scan<float>(h, (const float *)x, (const float *)e, o, slot0, n_seq, L, seq_stride,
+                         ws_base, ws_bytes, st);
+}
+
+// The checks every prefill entry point makes before any device work.
+ipttt_status check_prefill(ipttt_layer *h, const void *x, const void *e, const float *o,
+                           int32_t batch, int64_t seq_len) {
+  if (!h) return fail(IPTTT_E_INVALID, "handle is NULL");
+  if (batch < 0 || seq_len < 0)
+    return fail(IPTTT_E_INVALID, "batch=%d seq_len=%lld must be >= 0", batch, (long long)seq_len);
+  if (batch > h->desc.max_batch)
+    return fail(IPTTT_E_INVALID, "batch=%d exceeds max_batch=%d", batch, h->desc.max_batch);
+  if (batch == 0 || seq_len == 0) return IPTTT_OK;
+  ipttt_status s = check_call(h, x, e, o);
+  if (s != IPTTT_OK) return s;
+  if (seq_len > ((int64_t)1 << 40) / h->desc.d) return fail(IPTTT_E_UNSUPPORTED, "seq_len too large");
+  for (int32_t i = 0; i < batch; ++i)
+    if (!h->was_reset[(size_t)i]) return fail(IPTTT_E_STATE, "sequence %d was never reset", i);
+  return IPTTT_OK;
 }
 
 // ---- backward ---------------------------------------------------------------
@@ -490,16 +499,8 @@ extern "C" {
 
 ipttt_status ipttt_prefill_layer(ipttt_layer *h, const void *x, const void *e, float *o,
                                  int32_t batch, int64_t seq_len, void *hip_stream) {
-  if (!h) return fail(IPTTT_E_INVALID, "handle is NULL");
-  if (batch < 0 || seq_len < 0) return fail(IPTTT_E_INVALID, "batch=%d seq_len=%lld must be >= 0", batch, (long long)seq_len);
-  if (batch > h->desc.max_batch)
-    return fail(IPTTT_E_INVALID, "batch=%d exceeds max_batch=%d", batch, h->desc.max_batch);
-  if (batch == 0 || seq_len == 0) return IPTTT_OK;
-  ipttt_status s = check_call(h, x, e, o);
-  if (s != IPTTT_OK) return s;
-  if (seq_len > ((int64_t)1 << 40) / h->desc.d) return fail(IPTTT_E_UNSUPPORTED, "seq_len too large");
-  for (int32_t i = 0; i < batch; ++i)
-    if (!h->was_reset[(size_t)i]) return fail(IPTTT_E_STATE, "sequence %d was never reset", i);
+  ipttt_status s = check_prefill(h, x, e, o, batch, seq_len);
+  if (s != IPTTT_OK || batch == 0 || seq_len == 0) return s;
   return dispatch(h, x, e, o, 0, batch, seq_len, seq_len * h->desc.d, (hipStream_t)hip_stream);
 }
 

@@ -1,8 +1,11 @@
 // Measurement-only micro-benchmarks of the chip's achievable rates, against
 // which the layer's kernels are reported: MFMA issue with no memory traffic
 // (two waves per SIMD, independent accumulators), a streaming read, LDS reads
-// and direct copies from L2 into LDS.
-#include "internal.h"
+// and direct copies from L2 into LDS. Built into its own library
+// (libipttt_probe.so, include/ipttt_probe.h), apart from the layer library.
+#include <hip/hip_runtime.h>
+
+#include "../../include/ipttt_probe.h"
 
 namespace ipttt {
 namespace {
@@ -139,51 +142,55 @@ __global__ __launch_bounds__(kProbeThreads) void k_probe_copy(const char *__rest
 }
 }  // namespace
 
-hipError_t probe_launch(int kind, int64_t n, const void *src, void *dst, size_t dst_bytes,
-                        double *work, hipStream_t st) {
+constexpr size_t kCopyWindowBytes = (size_t)64 * 65536;  // 64 windows of 64 KB
+
+}  // namespace ipttt
+
+extern "C" int ipttt_probe(int32_t kind, int64_t n, const void *src, size_t src_bytes, void *dst,
+                           size_t dst_bytes, double *work, void *hip_stream) {
+  using namespace ipttt;
+  constexpr int kOk = 0, kInvalid = -1, kHip = -3;
+  if (kind < IPTTT_PROBE_MFMA16 || kind > IPTTT_PROBE_COPY || n < 1 || !dst || !work ||
+      ((uintptr_t)dst & 15))
+    return kInvalid;
+  const bool needs_src = kind == IPTTT_PROBE_READ || kind == IPTTT_PROBE_COPY;
+  if (needs_src && (!src || ((uintptr_t)src & 15))) return kInvalid;
+  if (kind == IPTTT_PROBE_READ && (n % 16 || (size_t)n > src_bytes)) return kInvalid;
+  if (kind == IPTTT_PROBE_COPY && src_bytes < kCopyWindowBytes) return kInvalid;
   int dev = 0, cus = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) return e;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    return kHip;
+  hipStream_t st = (hipStream_t)hip_stream;
+  const int64_t blocks2 = 2 * (int64_t)cus;  // 8 waves per CU: two per SIMD
+  const size_t out2 = (size_t)blocks2 * kProbeThreads * 4;
   if (kind == IPTTT_PROBE_MFMA16 || kind == IPTTT_PROBE_MFMA32) {
-    const int64_t blocks = 2 * (int64_t)cus;  // 8 waves per CU: two per SIMD
-    if (dst_bytes < (size_t)(blocks * kProbeThreads * sizeof(float))) return hipErrorInvalidValue;
-    const int64_t waves = blocks * (kProbeThreads / 64);
+    if (dst_bytes < out2) return kInvalid;
+    const int64_t waves = blocks2 * (kProbeThreads / 64);
     if (kind == IPTTT_PROBE_MFMA16) {
-      hipLaunchKernelGGL(k_probe_mfma16, dim3((unsigned)blocks), dim3(kProbeThreads), 0, st,
+      hipLaunchKernelGGL(k_probe_mfma16, dim3((unsigned)blocks2), dim3(kProbeThreads), 0, st,
                          (float *)dst, n, 1e-3f);
       *work = (double)n * 8 * (2.0 * 16 * 16 * 32) * waves;
     } else {
-      hipLaunchKernelGGL(k_probe_mfma32, dim3((unsigned)blocks), dim3(kProbeThreads), 0, st,
+      hipLaunchKernelGGL(k_probe_mfma32, dim3((unsigned)blocks2), dim3(kProbeThreads), 0, st,
                          (float *)dst, n, 1e-3f);
       *work = (double)n * 4 * (2.0 * 32 * 32 * 16) * waves;
     }
-    return hipGetLastError();
-  }
-  if (kind == IPTTT_PROBE_COPY) {
-    const int64_t blocks = 2 * (int64_t)cus;
-    hipLaunchKernelGGL(k_probe_copy, dim3((unsigned)blocks), dim3(kProbeThreads), 0, st,
+  } else if (kind == IPTTT_PROBE_COPY) {
+    hipLaunchKernelGGL(k_probe_copy, dim3((unsigned)blocks2), dim3(kProbeThreads), 0, st,
                        (const char *)src, n);
-    *work = (double)n * 8 * 1024 * (kProbeThreads / 64) * blocks;
-    return hipGetLastError();
-  }
-  if (kind == IPTTT_PROBE_LDS) {
-    const int64_t blocks = 2 * (int64_t)cus;
-    if (dst_bytes < (size_t)(blocks * kProbeThreads * sizeof(unsigned))) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_probe_lds, dim3((unsigned)blocks), dim3(kProbeThreads), 0, st,
+    *work = (double)n * 8 * 1024 * (kProbeThreads / 64) * blocks2;
+  } else if (kind == IPTTT_PROBE_LDS) {
+    if (dst_bytes < out2) return kInvalid;
+    hipLaunchKernelGGL(k_probe_lds, dim3((unsigned)blocks2), dim3(kProbeThreads), 0, st,
                        (unsigned *)dst, n);
-    *work = (double)n * 4 * 16 * kProbeThreads * blocks;
-    return hipGetLastError();
+    *work = (double)n * 4 * 16 * kProbeThreads * blocks2;
+  } else {  // read: n bytes from src, one 32-bit value per thread to dst
+    const int64_t blocks = 8 * (int64_t)cus;
+    if (dst_bytes < (size_t)blocks * kProbeThreads * 4) return kInvalid;
+    hipLaunchKernelGGL(k_probe_read, dim3((unsigned)blocks), dim3(kProbeThreads), 0, st,
+                       (const uint4 *)src, (unsigned *)dst, n / 16);
+    *work = (double)n;
   }
-  // read: n bytes from src, one 32-bit value per thread to dst
-  const int64_t blocks = 8 * (int64_t)cus;
-  if (n % 16 || ((uintptr_t)src & 15) ||
-      dst_bytes < (size_t)(blocks * kProbeThreads * sizeof(unsigned)))
-    return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_probe_read, dim3((unsigned)blocks), dim3(kProbeThreads), 0, st,
-                     (const uint4 *)src, (unsigned *)dst, n / 16);
-  *work = (double)n;
-  return hipGetLastError();
+  return hipGetLastError() == hipSuccess ? kOk : kHip;
 }
-
-}  // namespace ipttt

@@ -237,41 +237,6 @@ ipttt_status ipttt_profile_begin(ipttt_layer *h);
  * ms[IPTTT_K_COUNT] (host arrays), and stops recording. */
 ipttt_status ipttt_profile_end(ipttt_layer *h, int32_t *launches, double *ms);
 
-/* Measurement only, not part of the layer: micro-benchmarks of the chip's
- * achievable rates, enqueued on hip_stream for the caller to time (the layer's
- * kernel rates are reported against them).
- *   IPTTT_PROBE_MFMA16: two waves per SIMD on every CU issue back-to-back
- *     independent v_mfma_f32_16x16x32_bf16, n iterations of 8 per wave, no
- *     memory traffic; dst (device, at least 2 x CUs x 256 floats) receives
- *     per-thread sums so the loop is kept; src is unused.
- *   IPTTT_PROBE_MFMA32: the same with v_mfma_f32_32x32x16_bf16, n iterations
- *     of 4 per wave.
- *   IPTTT_PROBE_READ: streams n bytes of src (device, 16-byte aligned, n a
- *     multiple of 16) through the CUs; dst (device, at least 8 x CUs x 256
- *     32-bit values) receives one folded value per thread.
- *   IPTTT_PROBE_LDS: two 256-thread blocks per CU read 32 KB of their LDS n
- *     times over in conflict-free 16-byte pieces; dst (device, at least
- *     2 x CUs x 256 32-bit values) receives one folded value per thread; src
- *     is unused.
- *   IPTTT_PROBE_COPY: two four-wave blocks per CU copy 8 KB per wave and
- *     iteration from a 64 KB window of src (device, 16-byte aligned, at least
- *     4 MiB: 64 windows, L2-resident after the first pass) into LDS with
- *     direct global-to-LDS copies, two iterations in flight, n iterations;
- *     dst must be non-NULL (nothing is written to it).
- * *work receives the launch's FLOPs (MFMA probes) or bytes read or copied. Returns
- * IPTTT_E_INVALID for an unknown kind, a NULL buffer or work, n < 1, or
- * buffers that do not fit; IPTTT_E_HIP if the launch fails. */
-typedef enum {
-  IPTTT_PROBE_MFMA16 = 0,
-  IPTTT_PROBE_MFMA32 = 1,
-  IPTTT_PROBE_READ = 2,
-  IPTTT_PROBE_LDS = 3,
-  IPTTT_PROBE_COPY = 4
-} ipttt_probe_kind;
-
-ipttt_status ipttt_probe(int32_t kind, int64_t n, const void *src, void *dst, size_t dst_bytes,
-                         double *work, void *hip_stream);
-
 /* Frees the handle (host memory only). NULL is ignored. */
 void ipttt_destroy(ipttt_layer *h);
 

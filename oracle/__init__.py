@@ -14,6 +14,7 @@ from .ipttt_oracle import (  # noqa: F401
     initial_weight_grad_entries,
     prefill,
     prefill_prefix_form,
+    prefill_prefix_form_stream,
     prefill_with_resets,
     silu,
     silu_grad,

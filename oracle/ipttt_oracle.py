@@ -77,6 +77,7 @@ __all__ = [
     "chunk_ranges",
     "prefill",
     "prefill_prefix_form",
+    "prefill_prefix_form_stream",
     "prefill_with_resets",
     "final_weight_entries",
     "decode_steps",
@@ -207,6 +208,26 @@ def prefill_prefix_form(X, E, W_g, W_u, conv_w, Proj, W_start, eta, B):
             prefix = prefix + S[k]
         W_final[n] = W0 + eta * prefix
     return O, W_final
+
+
+def prefill_prefix_form_stream(X, E, W_g, W_u, conv_w, Proj, W_start, eta, B, on_chunk):
+    """Linear update only: the prefix-sum form of ONE sequence, chunk by chunk.
+
+    The same function as prefill_prefix_form (W_k = W_0 + eta * P_k with
+    P_k = sum_{j<k} Z_j^T V_j, [explainer] §2.3 associativity), evaluated with
+    one running P instead of every chunk's S_j at once, so that a long
+    sequence fits in memory: O_k = Z_k W_0 + eta * (Z_k P_k), then
+    P_{k+1} = P_k + Z_k^T V_k. X, E: [L, d]; W_start: [F, d]. Calls
+    on_chunk(s, e, O_k) for each chunk in order and returns W_final [F, d].
+    """
+    X, E, W0 = _f64(X), _f64(E), _f64(W_start)
+    P = np.zeros(W0.shape, dtype=np.float64)
+    for s, e in chunk_ranges(X.shape[0], B):
+        Z = gate_up(X[s:e], W_g, W_u)
+        V = target_chunk(E[s:e], conv_w, Proj)
+        on_chunk(s, e, Z @ W0 + eta * (Z @ P))
+        P += Z.T @ V
+    return W0 + eta * P
 
 
 def prefill_with_resets(X, E, W_g, W_u, conv_w, Proj, W_0, eta, B, doc_starts, update="linear",

@@ -325,18 +325,34 @@ def test_backward_errors_before_device_work(lib):
         B.IPTTT_E_INVALID
 
 
-def test_probe_errors_before_device_work(lib):
-    """The measurement probes reject bad arguments before touching the device."""
+def test_probe_library_errors_before_device_work():
+    """The measurement library (its own ABI, include/ipttt_probe.h) rejects bad
+    arguments, including sources shorter than a probe reads, before touching
+    the device."""
+    from chunked_weight_mlp_amd import probe as P
+    if not os.path.exists(P.LIB_PATH):
+        pytest.fail("libipttt_probe.so is not built: run __graft_entry__.build()")
+    lib = P.load()
+    hdr = open(os.path.join(ROOT, "include", "ipttt_probe.h")).read()
+    assert sorted(set(re.findall(r"\b(ipttt_[a-z_]+)\s*\(", re.sub(r"/\*.*?\*/", "", hdr,
+                                                                     flags=re.S)))) == list(P.EXPORTS)
     mem = FakeMem()
     buf = mem.ptr()
-    for kind, n, src, dst, work_ok in ((7, 10, None, buf, True),     # unknown kind
-                                       (B.IPTTT_PROBE_MFMA16, 0, None, buf, True),   # n < 1
-                                       (B.IPTTT_PROBE_MFMA32, 10, None, None, True),  # no dst
-                                       (B.IPTTT_PROBE_READ, 16, None, buf, True),    # read without src
-                                       (B.IPTTT_PROBE_LDS, 0, None, buf, True),      # n < 1
-                                       (B.IPTTT_PROBE_LDS, 10, None, None, True),    # no dst
-                                       (B.IPTTT_PROBE_COPY, 10, None, buf, True),    # copy without src
-                                       (B.IPTTT_PROBE_COPY, 10, buf + 8, buf, True),  # misaligned src
-                                       (B.IPTTT_PROBE_MFMA16, 10, None, buf, False)):  # no work
+    big = 1 << 20
+    for kind, n, src, src_bytes, dst, work_ok in (
+            (7, 10, None, 0, buf, True),                          # unknown kind
+            (P.IPTTT_PROBE_MFMA16, 0, None, 0, buf, True),        # n < 1
+            (P.IPTTT_PROBE_MFMA32, 10, None, 0, None, True),      # no dst
+            (P.IPTTT_PROBE_MFMA32, 10, None, 0, buf + 8, True),   # misaligned dst
+            (P.IPTTT_PROBE_READ, 16, None, big, buf, True),       # read without src
+            (P.IPTTT_PROBE_READ, 32, buf, 16, buf, True),         # reads past src
+            (P.IPTTT_PROBE_READ, 24, buf, big, buf, True),        # n not a multiple of 16
+            (P.IPTTT_PROBE_LDS, 0, None, 0, buf, True),           # n < 1
+            (P.IPTTT_PROBE_LDS, 10, None, 0, None, True),         # no dst
+            (P.IPTTT_PROBE_COPY, 10, None, 4 << 20, buf, True),   # copy without src
+            (P.IPTTT_PROBE_COPY, 10, buf + 8, 4 << 20, buf, True),  # misaligned src
+            (P.IPTTT_PROBE_COPY, 10, buf, (4 << 20) - 16, buf, True),  # src below 4 MiB
+            (P.IPTTT_PROBE_MFMA16, 10, None, 0, buf, False)):     # no work
         work = ctypes.byref(ctypes.c_double()) if work_ok else None
-        assert lib.ipttt_probe(kind, n, src, dst, 1 << 20, work, None) == B.IPTTT_E_INVALID
+        assert lib.ipttt_probe(kind, n, src, src_bytes, dst, 1 << 20, work, None) == \
+            B.IPTTT_E_INVALID, (kind, n, src_bytes)

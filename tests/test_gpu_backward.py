@@ -99,6 +99,26 @@ def test_backward_small_shapes(Bc, L, N, with_dwf):
     compare(to_pages(g), oracle_backward(w, weights, x, e, d_o, d_wf), f"B={Bc}")
 
 
+@pytest.mark.parametrize("Kc,Bc,L,update", [
+    (1, 64, 194, "linear"),   # one tap: no window at all
+    (3, 2, 41, "linear"),     # chunks of 2 tokens, shorter than the filter
+    (8, 5, 67, "mse"),        # 8 taps over 5-token chunks, 2-token tail
+    (8, 64, 130, "linear"),   # 2-token tail
+])
+def test_backward_conv_taps(Kc, Bc, L, update):
+    """Conv adjoint with 1, 3 and 8 taps, including chunks shorter than the filter."""
+    w = SMALL.replace(chunk=Bc, seq_len=L, n_seq=1, conv_k=Kc, update=update,
+                      eta=1e-2 if update == "linear" else 2e-3)
+    weights = wl.make_weights(w)
+    x, e = wl.make_inputs(w)
+    d_o, d_wf = wl.make_upstream(w)
+    say(f"[backward] taps={Kc} B={Bc} L={L} {update}")
+    layer = make_layer(w, weights, 1)
+    g = layer.backward(x.to(DEV), e.to(DEV), d_o.to(DEV), d_wf.to(DEV))
+    torch.cuda.synchronize()
+    compare(to_pages(g), oracle_backward(w, weights, x, e, d_o, d_wf), f"taps={Kc} B={Bc}")
+
+
 @pytest.mark.parametrize("Bc,L,N,with_dwf", [
     (128, 700, 2, True),     # ragged last chunk, two sequences
     (96, 500, 1, False),     # padding rows in every chunk

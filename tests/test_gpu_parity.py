@@ -16,6 +16,7 @@ import torch
 import oracle
 import workloads as wl
 from chunked_weight_mlp_amd import ipttt as B
+from parity_check import ChunkErrors, check_chunks, check_weights
 
 pytestmark = pytest.mark.gpu
 
@@ -81,11 +82,9 @@ def check_against_oracle(w, flags=0, n_seq=None, seq_len=None, slab_chunks=None,
     o = gpu_run(layer, x, e).to("cpu", torch.float64).numpy()
     Wg = w_pages(layer, N)
     O_ref, W_ref = oracle_run(w, x, e, weights)
-    eo, ew = rel_fro(o, O_ref), rel_fro(Wg, W_ref)
-    say(f"[parity]   rel_fro O={eo:.3e} W={ew:.3e} (tol {TOL[w.dtype]:.0e})")
     assert np.isfinite(o).all()
-    assert eo <= TOL[w.dtype], eo
-    assert ew <= TOL[w.dtype], ew
+    eo = check_chunks(o, O_ref, w.chunk, TOL[w.dtype], "parity")
+    ew = check_weights(Wg, W_ref, TOL[w.dtype], "parity")
     return eo, ew
 
 
@@ -139,6 +138,22 @@ def test_bf16_partial_tiles(update):
     w = BF16_SMALL.replace(d=320, d_ff=576, update=update,
                            eta=1e-2 if update == "linear" else 2e-3)
     check_against_oracle(w, n_seq=2, seq_len=700)
+
+
+@pytest.mark.parametrize("Kc,Bc,L,update", [
+    (1, 64, 194, "linear"),   # one tap
+    (3, 2, 41, "linear"),     # chunks of 2 tokens, shorter than the filter
+    (3, 128, 257, "mse"),     # 1-token tail
+    (8, 5, 67, "linear"),     # 8 taps over 5-token chunks, 2-token tail
+    (8, 64, 130, "mse"),      # 2-token tail
+])
+def test_bf16_conv_taps(Kc, Bc, L, update):
+    """The conv with 1, 3 and 8 taps per channel (each a kernel instance of its
+    own), including chunks and ragged tails shorter than the filter, whose taps
+    past the chunk's end read the zero pad."""
+    w = BF16_SMALL.replace(chunk=Bc, conv_k=Kc, update=update,
+                           eta=1e-2 if update == "linear" else 2e-3)
+    check_against_oracle(w, n_seq=1, seq_len=L)
 
 
 def test_bf16_multi_slab():
@@ -204,9 +219,8 @@ def test_chunk_sweep_vs_prefix_form(Bc):
     ow = wl.to_oracle(weights)
     O_ref, W_ref = oracle.prefill_prefix_form(x.double().numpy(), e.double().numpy(), ow["W_g"],
                                               ow["W_u"], ow["conv_w"], ow["Proj"], ow["W_0"], w.eta, Bc)
-    eo, ew = rel_fro(o, O_ref), rel_fro(w_pages(layer, 1), W_ref)
-    say(f"[sweep]   rel_fro O={eo:.3e} W={ew:.3e}")
-    assert eo <= TOL["bf16"] and ew <= TOL["bf16"]
+    check_chunks(o, O_ref, Bc, TOL["bf16"], f"sweep B={Bc}")
+    check_weights(w_pages(layer, 1), W_ref, TOL["bf16"], f"sweep B={Bc}")
 
 
 def _bitwise_pair(layer_a, layer_b, x, e):
@@ -293,10 +307,16 @@ def test_packed_documents():
     O_ref, W_ref = oracle.prefill_with_resets(x[0].double().numpy(), e[0].double().numpy(), ow["W_g"],
                                               ow["W_u"], ow["conv_w"], ow["Proj"], ow["W_0"], w.eta,
                                               w.chunk, starts)
-    eo = rel_fro(o.double().cpu().numpy(), O_ref)
-    ew = rel_fro(w_pages(layer, 1)[0], W_ref)
-    say(f"[packed] rel_fro O={eo:.3e} W={ew:.3e}")
-    assert eo <= TOL["bf16"] and ew <= TOL["bf16"]
+    # chunks restart at every document start
+    ce = ChunkErrors("packed")
+    og = o.double().cpu().numpy()
+    bounds = [0, *starts, w.seq_len]
+    for i in range(len(bounds) - 1):
+        a, b = bounds[i], bounds[i + 1]
+        for k, (s, t) in enumerate(oracle.chunk_ranges(b - a, w.chunk)):
+            ce.add(i, k, a + s, og[a + s:a + t], O_ref[a + s:a + t])
+    ce.check(TOL["bf16"])
+    check_weights(w_pages(layer, 1), W_ref[None], TOL["bf16"], "packed")
 
 
 def test_profile_records_every_kernel():
@@ -343,10 +363,10 @@ def test_decode_token_by_token(dtype, update):
     for n in range(2):
         O_ref, W_after = oracle.decode_steps(X[n], E[n], ow["W_g"], ow["W_u"], ow["conv_w"], ow["Proj"],
                                              ow["W_0"], w.eta, Bc, update=update)
-        eo = rel_fro(o_dec[n], O_ref[64:])
-        ep = rel_fro(o_pre[n].double().cpu().numpy(), O_ref[:64])
-        say(f"[decode] {dtype} {update} seq {n}: rel_fro O(decode)={eo:.3e} O(prefill)={ep:.3e}")
-        assert eo <= tol and ep <= tol
+        # the decoded tokens start on a chunk boundary (position 64)
+        check_chunks(o_dec[n][None], O_ref[None, 64:], Bc, tol, f"decode {dtype} {update} seq {n}")
+        check_chunks(o_pre[n].double().cpu().numpy()[None], O_ref[None, :64], Bc, tol,
+                     f"decode prefill {dtype} {update} seq {n}")
         W_ref.append(W_after)
     ew = rel_fro(w_pages(layer, 2), np.stack(W_ref))
     say(f"[decode] {dtype} {update}: rel_fro W={ew:.3e}")

@@ -186,6 +186,27 @@ def pin_prefix_form(orc):
         np.testing.assert_allclose(Wf, Wp, rtol=1e-11, atol=1e-12)
 
 
+def pin_prefix_form_stream(orc):
+    """The chunk-by-chunk prefix form against the all-at-once one (itself pinned
+    against the scan above and the masked dual form below), with tails."""
+    for B, L in ((1, 9), (5, 23), (8, 40), (40, 40), (64, 40)):
+        c = case(17, N=1, L=L)
+        Op, Wp = orc.prefill_prefix_form(c["X"], c["E"], c["W_g"], c["W_u"], c["conv_w"],
+                                         c["Proj"], c["W_0"], 0.03, B)
+        got = np.full_like(Op[0], np.nan)
+        seen = []
+
+        def put(s, e, Ok):
+            seen.append((s, e))
+            got[s:e] = Ok
+
+        Wf = orc.prefill_prefix_form_stream(c["X"][0], c["E"][0], c["W_g"], c["W_u"], c["conv_w"],
+                                            c["Proj"], c["W_0"], 0.03, B, put)
+        assert seen == orc.chunk_ranges(L, B)
+        np.testing.assert_allclose(got, Op[0], rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(Wf, Wp[0], rtol=1e-11, atol=1e-12)
+
+
 def pin_dual_form(orc):
     """Linear: O = Z W_0 + eta (M * Z Z^T) V with M[t, s] = [chunk(s) < chunk(t)],
     Z and V from library routines (V chunk by chunk)."""
@@ -488,7 +509,7 @@ def pin_initial_weight_grad_entries(orc):
 
 PINS = [
     pin_gate_up_library, pin_conv_library, pin_next_token_target, pin_eta0_textbook,
-    pin_single_chunk, pin_library_model, pin_prefix_form, pin_dual_form, pin_final_state,
+    pin_single_chunk, pin_library_model, pin_prefix_form, pin_prefix_form_stream, pin_dual_form, pin_final_state,
     pin_causality, pin_brute_force, pin_continuation, pin_batch_independence,
     pin_update_direction, pin_resets, pin_decode_steps, pin_backward_autograd,
     pin_backward_finite_differences, pin_backward_eta0, pin_backward_linear_in_upstream,
@@ -526,6 +547,9 @@ MUTANTS = {
                         "return [(s, min(s + B - 1, L)) for s in range(0, L, B)]"),
     "prefix form inclusive": ("O[n, s:e] = Zs[k] @ (W0 + eta * prefix)\n            prefix = prefix + S[k]",
                               "prefix = prefix + S[k]\n            O[n, s:e] = Zs[k] @ (W0 + eta * prefix)"),
+    "streamed prefix form inclusive": ("on_chunk(s, e, Z @ W0 + eta * (Z @ P))\n        P += Z.T @ V",
+                                       "P += Z.T @ V\n        on_chunk(s, e, Z @ W0 + eta * (Z @ P))"),
+    "streamed prefix form drops eta": ("return W0 + eta * P", "return W0 + P"),
     "reset keeps state": ("            W = _f64(W_0).copy()\n", "            pass\n"),
     # backward
     "backward drops the update path of dZ": ("dZ = dOk @ Wk.T + eta * (V @ G.T)", "dZ = dOk @ Wk.T"),
