@@ -16,7 +16,7 @@ LIB = os.path.join(HERE, "libipttt.so")
 PROBE_LIB = os.path.join(HERE, "libipttt_probe.so")
 OBJDIR = os.path.join(HERE, "_build")
 SOURCES = ["ipttt.cpp", "kernels_generic.hip", "kernels_mfma.hip", "kernels_decode.hip",
-           "kernels_backward.hip"]
+           "kernels_backward.hip", "scratch.hip"]
 PROBE_SOURCES = ["probe.hip"]
 ARCH = "gfx950"
 FLAGS = [

@@ -42,6 +42,13 @@ struct WsLayout {
 // Largest rows per chunk group (G * Bp) of the chunk-parallel scan.
 constexpr int kMaxGroupRows = 4096;
 
+// Size of the fixed per-device scratch area that ipttt_prefill_layer_noalloc
+// uses as its workspace (scratch.hip).
+constexpr size_t kScratchBytes = IPTTT_NOALLOC_SCRATCH_BYTES;
+// Device address of the current device's scratch area (looked up on the first
+// call per device, then cached); *out = nullptr on failure.
+hipError_t scratch_setup(void **out);
+
 // need_z: the token-major copy of Z (read by the generic apply only).
 // G: chunks per snapshot group (linear rule; 1 for MSE and the generic path).
 WsLayout ws_layout(int elem, int n_seq, int d, int F, int Bp, int nc_cap, int G, int mse,

@@ -30,8 +30,10 @@ struct ipttt_layer {
   ipttt_layer_desc desc;
   std::vector<uint8_t> was_reset;
   bool mfma;
-  // per-kernel timing (ipttt_profile_begin / _end)
+  // per-kernel timing (ipttt_profile_begin / _end); no_events: the current call
+  // must not create or record events (the allocation-free entry point)
   bool prof = false;
+  bool no_events = false;
   struct Rec {
     int kind;
     hipEvent_t a, b;
@@ -134,13 +136,13 @@ struct ProfScope {
     return e;
   }
   ProfScope(ipttt_layer *h_, int kind_, hipStream_t st_) : h(h_), kind(kind_), st(st_) {
-    if (!h->prof) return;
+    if (!h->prof || h->no_events) return;
     a = take(h);
     b = take(h);
     if (a && b) (void)hipEventRecord(a, st);  // best effort: a failed record shows as a zero time
   }
   ~ProfScope() {
-    if (!h->prof || !a || !b) return;
+    if (!h->prof || h->no_events || !a || !b) return;
     (void)hipEventRecord(b, st);
     h->recs.push_back({kind, a, b});
   }
@@ -230,6 +232,10 @@ ipttt_status ipttt_init(const ipttt_layer_desc *desc, ipttt_layer **out) {
   h->desc = *desc;
   h->was_reset.assign((size_t)desc->max_batch, 0);
   h->mfma = use_mfma(desc);
+  // set-up of the allocation-free prefill's scratch area on the current device;
+  // a failure here (no device yet) is retried, and reported, by that entry point
+  void *scr = nullptr;
+  (void)ipttt::scratch_setup(&scr);
   *out = h;
   return IPTTT_OK;
 }
@@ -502,6 +508,29 @@ ipttt_status ipttt_prefill_layer(ipttt_layer *h, const void *x, const void *e, f
   ipttt_status s = check_prefill(h, x, e, o, batch, seq_len);
   if (s != IPTTT_OK || batch == 0 || seq_len == 0) return s;
   return dispatch(h, x, e, o, 0, batch, seq_len, seq_len * h->desc.d, (hipStream_t)hip_stream);
+}
+
+ipttt_status ipttt_prefill_layer_noalloc(ipttt_layer *h, const void *x, const void *e, float *o,
+                                         int32_t batch, int64_t seq_len, void *hip_stream) {
+  ipttt_status s = check_prefill(h, x, e, o, batch, seq_len);
+  if (s != IPTTT_OK || batch == 0 || seq_len == 0) return s;
+  const ipttt_layer_desc &d = h->desc;
+  const int mse = d.update == IPTTT_UPDATE_MSE;
+  const size_t one = ipttt::ws_layout(elem_size(d.in_dtype), batch, d.d, d.d_ff,
+                                      chunk_pitch(d.chunk), 1, 1, mse, !h->mfma)
+                         .total;
+  if (one > ipttt::kScratchBytes)
+    return fail(IPTTT_E_WORKSPACE,
+                "one chunk of %d sequences needs %zu bytes of workspace, above the fixed %zu-byte "
+                "scratch area of the allocation-free prefill",
+                batch, one, ipttt::kScratchBytes);
+  void *scr = nullptr;
+  TRY_HIP(ipttt::scratch_setup(&scr), "scratch area lookup");
+  h->no_events = true;
+  s = dispatch(h, x, e, o, 0, batch, seq_len, seq_len * d.d, (hipStream_t)hip_stream, scr,
+               ipttt::kScratchBytes);
+  h->no_events = false;
+  return s;
 }
 
 ipttt_status ipttt_decode_step(ipttt_layer *h, const void *x, const void *e, int64_t seq_stride,

@@ -27,8 +27,10 @@ IPTTT_UPDATE_LINEAR = 0
 IPTTT_UPDATE_MSE = 1
 IPTTT_FLAG_GENERIC_KERNELS = 1
 
+IPTTT_NOALLOC_SCRATCH_BYTES = 256 << 20
+
 EXPORTS = (
-    "ipttt_workspace_bytes", "ipttt_init", "ipttt_prefill_layer",
+    "ipttt_workspace_bytes", "ipttt_init", "ipttt_prefill_layer", "ipttt_prefill_layer_noalloc",
     "ipttt_prefill_packed", "ipttt_decode_step", "ipttt_backward_workspace_bytes",
     "ipttt_backward_layer", "ipttt_reset_fast_weights", "ipttt_profile_begin",
     "ipttt_profile_end", "ipttt_destroy", "ipttt_status_str", "ipttt_last_error",
@@ -92,6 +94,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ipttt_init.restype = ctypes.c_int
     lib.ipttt_prefill_layer.argtypes = [vp, vp, vp, vp, i32, i64, vp]
     lib.ipttt_prefill_layer.restype = ctypes.c_int
+    lib.ipttt_prefill_layer_noalloc.argtypes = [vp, vp, vp, vp, i32, i64, vp]
+    lib.ipttt_prefill_layer_noalloc.restype = ctypes.c_int
     lib.ipttt_prefill_packed.argtypes = [vp, vp, vp, vp, i32, i64, ctypes.POINTER(i64), i32, vp]
     lib.ipttt_prefill_packed.restype = ctypes.c_int
     lib.ipttt_decode_step.argtypes = [vp, vp, vp, i64, i32, vp, i32, vp]
@@ -160,6 +164,11 @@ def ipttt_init(desc: LayerDesc) -> ctypes.c_void_p:
 
 def ipttt_prefill_layer(h, x, e, o, batch: int, seq_len: int, stream=None) -> None:
     _check(load().ipttt_prefill_layer(h, _ptr(x), _ptr(e), _ptr(o), batch, seq_len, _stream(stream)))
+
+
+def ipttt_prefill_layer_noalloc(h, x, e, o, batch: int, seq_len: int, stream=None) -> None:
+    _check(load().ipttt_prefill_layer_noalloc(h, _ptr(x), _ptr(e), _ptr(o), batch, seq_len,
+                                              _stream(stream)))
 
 
 def ipttt_prefill_packed(h, x, e, o, slot: int, seq_len: int, doc_starts, stream=None) -> None:

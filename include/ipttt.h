@@ -125,7 +125,9 @@ size_t ipttt_workspace_bytes(const ipttt_layer_desc *desc, int32_t batch, int32_
 
 /* Validates the descriptor (sizes, dtypes, non-null and 16-byte aligned device
  * pointers, workspace pointer and size) and returns a handle in *out. No
- * device work. Every sequence starts "never reset": reset it before prefill. */
+ * device work (it looks up, on the current device, the address of the scratch
+ * area of ipttt_prefill_layer_noalloc). Every sequence starts "never reset":
+ * reset it before prefill. */
 ipttt_status ipttt_init(const ipttt_layer_desc *desc, ipttt_layer **out);
 
 /* Prefill of sequences 0..batch-1 (state slots 0..batch-1), seq_len tokens
@@ -137,6 +139,27 @@ ipttt_status ipttt_init(const ipttt_layer_desc *desc, ipttt_layer **out);
  * aligned on the bf16 MFMA path, element-aligned otherwise; o 4-byte). */
 ipttt_status ipttt_prefill_layer(ipttt_layer *h, const void *x, const void *e, float *o,
                                  int32_t batch, int64_t seq_len, void *hip_stream);
+
+/* Allocation-free prefill, for callers that cannot allocate device memory
+ * (code under HIP stream capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation as ipttt_prefill_layer, with its workspace
+ * in a fixed scratch area of IPTTT_NOALLOC_SCRATCH_BYTES bytes that the library
+ * holds on every device it runs on (a static device array, alive until the
+ * process ends) instead of the descriptor's workspace. It calls no hipMalloc,
+ * hipFree or other allocating routine and records no profiling events; the
+ * caller still passes x, e, o and the handle's w_state. Longer sequences run
+ * in several passes over the scratch area (W stays exact between them, as with
+ * a small workspace); a call whose single chunk of `batch` sequences needs more
+ * than the scratch area returns IPTTT_E_WORKSPACE. Every call on one device
+ * shares that device's scratch area, which keeps the last call's contents
+ * (nothing in it needs to start at zero): calls that overlap on one device,
+ * from any handle, stream or thread, race and must be ordered by the caller.
+ * The scratch address is looked up with the current device current, at
+ * ipttt_init and, for another device, at the first call there. Same validation
+ * and error codes as ipttt_prefill_layer, plus IPTTT_E_HIP if the lookup fails. */
+#define IPTTT_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+ipttt_status ipttt_prefill_layer_noalloc(ipttt_layer *h, const void *x, const void *e, float *o,
+                                         int32_t batch, int64_t seq_len, void *hip_stream);
 
 /* Prefill of ONE sequence holding several packed documents (state slot
  * `slot`). The fast weight goes back to w0 at every document start (explainer

@@ -97,6 +97,10 @@ int main(void) {
   EXPECT(ipttt_prefill_layer(h, (char *)x + 2, e, o, 1, 128, NULL) == IPTTT_E_INVALID);
   EXPECT(ipttt_prefill_layer(h, x, e, o, 0, 128, NULL) == IPTTT_OK);
   EXPECT(ipttt_prefill_layer(h, x, e, o, 1, 0, NULL) == IPTTT_OK);
+  EXPECT(ipttt_prefill_layer_noalloc(h, x, e, o, 3, 128, NULL) == IPTTT_E_INVALID);
+  EXPECT(ipttt_prefill_layer_noalloc(h, x, e, o, 1, 128, NULL) == IPTTT_E_STATE);
+  EXPECT(ipttt_prefill_layer_noalloc(h, x, e, o, -1, 128, NULL) == IPTTT_E_INVALID);
+  EXPECT(ipttt_prefill_layer_noalloc(h, x, e, o, 0, 128, NULL) == IPTTT_OK);
   {
     int64_t starts[2] = {9, 3};
     EXPECT(ipttt_prefill_packed(h, x, e, o, 0, 128, starts, 2, NULL) == IPTTT_E_INVALID);
@@ -129,6 +133,7 @@ int main(void) {
   ipttt_destroy(h);
   ipttt_destroy(NULL);
   EXPECT(ipttt_prefill_layer(NULL, x, e, o, 1, 1, NULL) == IPTTT_E_INVALID);
+  EXPECT(ipttt_prefill_layer_noalloc(NULL, x, e, o, 1, 1, NULL) == IPTTT_E_INVALID);
 
   if (failures) {
     fprintf(stderr, "%d expectation(s) failed\n", failures);

@@ -230,6 +230,7 @@ def test_prefill_errors_before_device_work(lib):
 
 def test_null_handle(lib):
     assert lib.ipttt_prefill_layer(None, None, None, None, 1, 1, None) == B.IPTTT_E_INVALID
+    assert lib.ipttt_prefill_layer_noalloc(None, None, None, None, 1, 1, None) == B.IPTTT_E_INVALID
     assert lib.ipttt_reset_fast_weights(None, 0, 1, None) == B.IPTTT_E_INVALID
     assert lib.ipttt_prefill_packed(None, None, None, None, 0, 1, None, 0, None) == B.IPTTT_E_INVALID
 
