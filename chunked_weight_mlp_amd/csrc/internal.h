@@ -110,16 +110,25 @@ hipError_t mf_conv(const Slab &s, const __bf16 *e, const Weights &w, const WsPtr
 hipError_t mf_proj(const Slab &s, const Weights &w, const WsPtrs &ws, hipStream_t st);
 // Linear rule: for each group q of G chunks of the slab, write snapshot
 // S[q] = bf16(W) then W += sum over the group's tokens of z_t^T (eta v_t); W
-// stays in registers across the slab.
-hipError_t mf_update_scan(const Slab &s, const WsPtrs &ws, float *w_state, hipStream_t st);
+// stays in registers across the slab. blocked: S in the layout of mf_snapshot
+// (what mf_apply reads), else row-major [d][F] (what the backward reads).
+hipError_t mf_update_scan(const Slab &s, const WsPtrs &ws, float *w_state, bool blocked,
+                          hipStream_t st);
 // G > 1: masked Gram of every group of the slab, P^T[s][m] = z_m . z_s when
 // token s lies in an earlier chunk of the group than token m, else 0.
 hipError_t mf_gram(const Slab &s, const WsPtrs &ws, hipStream_t st);
-// MSE rule, one chunk j: W += Rt Zt_j^T-contract, snapshot S = bf16(new W).
+// S = bf16(W) in the blocked layout the MFMA apply reads (element (c, f) at
+// ((f / 8) d + c) 8 + f % 8), every sequence of the slab: the MSE rule's first
+// copy of a call.
+hipError_t mf_snapshot(const Slab &s, const float *w_state, __bf16 *snap, int64_t snap_seq_stride,
+                       hipStream_t st);
+// MSE rule, one chunk j: W += Rt Zt_j^T-contract, snapshot S = bf16(new W) in
+// the layout of mf_snapshot.
 hipError_t mf_update_one(const Slab &s, int j, const WsPtrs &ws, float *w_state,
                          hipStream_t st);
-// O rows of groups [q0, q0 + nq) (G = 1: chunks): O = Z S_q, plus P (eta V)
-// when G > 1; the MSE rule (G = 1, nq = 1) also writes Rt.
+// O rows of groups [q0, q0 + nq) (G = 1: chunks): O = Z S_q (S in the layout
+// of mf_snapshot), plus P (eta V) when G > 1; the MSE rule (G = 1, nq = 1)
+// also writes Rt.
 hipError_t mf_apply(const Slab &s, int q0, int nq, const WsPtrs &ws, float *o,
                     hipStream_t st);
 

@@ -370,13 +370,15 @@ ipttt_status run_scan(ipttt_layer *h, const T *x, const T *e, float *o, int slot
       LAUNCH(IPTTT_K_CONV, mf_conv(s, (const __bf16 *)e, w, ws, st), "conv launch");
       LAUNCH(IPTTT_K_PROJ, mf_proj(s, w, ws, st), "proj launch");
       if (!mse) {
-        LAUNCH(IPTTT_K_UPDATE, mf_update_scan(s, ws, wst, st), "update scan launch");
+        LAUNCH(IPTTT_K_UPDATE, mf_update_scan(s, ws, wst, true, st), "update scan launch");
         if (o) {
           if (G > 1) LAUNCH(IPTTT_K_GRAM, mf_gram(s, ws, st), "Gram launch");
           LAUNCH(IPTTT_K_APPLY, mf_apply(s, 0, (s.nc + G - 1) / G, ws, o, st), "apply launch");
         }
       } else {
-        if (k0 == 0) LAUNCH(IPTTT_K_SNAPSHOT, gen_snapshot<T>(s, wst, (T *)ws.s, snap_seq_stride, st), "snapshot launch");
+        if (k0 == 0)
+          LAUNCH(IPTTT_K_SNAPSHOT, mf_snapshot(s, wst, (__bf16 *)ws.s, snap_seq_stride, st),
+                 "snapshot launch");
         for (int j = 0; j < s.nc; ++j) {
           LAUNCH(IPTTT_K_APPLY, mf_apply(s, j, 1, ws, o, st), "apply launch");
           LAUNCH(IPTTT_K_UPDATE, mf_update_one(s, j, ws, wst, st), "update launch");
@@ -681,7 +683,7 @@ ipttt_status ipttt_backward_layer(ipttt_layer *h, const void *x, const void *e, 
   __bf16 *rt = (__bf16 *)(base + lay.rt);
   const int64_t tstride = (int64_t)d.d * sl.Lp;  // [n][d][Lp] pitch between sequences
   if (!mse) {
-    LAUNCH(IPTTT_K_UPDATE, mf_update_scan(sl, ws, wscr, st), "update scan launch");
+    LAUNCH(IPTTT_K_UPDATE, mf_update_scan(sl, ws, wscr, false, st), "update scan launch");
   } else {
     // chunk by chunk: W_j kept per chunk, residual eta (V - O_j) kept per chunk
     LAUNCH(IPTTT_K_SNAPSHOT, gen_snapshot<__bf16>(sl, wscr, snap_w, sseq, st), "snapshot launch");

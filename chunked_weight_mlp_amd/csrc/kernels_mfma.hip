@@ -268,12 +268,63 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
 }
 
 // ---------------------------------------------------------------------------
+// Layout of the forward's bf16 copies S of the fast weight (BLK): blocks of 8
+// consecutive d_ff values, element (c, f) at ((f / 8) d + c) 8 + f % 8. The
+// update writes S from the accumulators, where 16 consecutive lanes hold 8
+// consecutive f each for 16 consecutive columns c: one 256-byte run here,
+// against 16 separate 16-byte pieces (half cache lines) in the row-major
+// [d][F] layout, whose partial-line writes completed slowly enough to hold
+// up the update's later waits. The apply's snapshot loads stay whole lines
+// (8 consecutive c of one block of f). Otherwise row-major.
+template <bool BLK>
+__device__ __forceinline__ int64_t snap_offset(const Slab &s, int c, int f) {
+  if constexpr (BLK)
+    return ((int64_t)(f >> 3) * s.d + c) * 8 + (f & 7);
+  else
+    return (int64_t)c * s.F + f;
+}
+// S = bf16(W) in the blocked layout, for every sequence of the slab (the MSE
+// rule's first copy; the update writes the later ones). A block converts 16
+// rows c x 256 columns f through LDS: rows read whole, blocks of f written as
+// 256-byte runs of 16 consecutive c.
+__global__ __launch_bounds__(256) void k_snapshot_blk(Slab s, const float *__restrict__ w,
+                                                      __bf16 *__restrict__ snap,
+                                                      int64_t snap_seq_stride) {
+  constexpr int TC = 16, TF = 256;
+  __shared__ __attribute__((aligned(16))) __bf16 tile[TC][TF + 8];
+  const int c0 = blockIdx.x * TC, f0 = blockIdx.y * TF, n_seq = blockIdx.z;
+  const int t = threadIdx.x;
+  const float *ws = w + (int64_t)n_seq * s.d * s.F;
+  {  // thread t: row c0 + t / 16, 16 columns from f0 + 16 (t % 16)
+    const int c = c0 + t / 16, f = f0 + 16 * (t % 16);
+#pragma unroll
+    for (int k = 0; k < 16; k += 4) {
+      f32x4 v = (c < s.d && f + k < s.F) ? *(const f32x4 *)(ws + (int64_t)c * s.F + f + k)
+                                         : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) tile[t / 16][16 * (t % 16) + k + r] = (__bf16)v[r];
+    }
+  }
+  __syncthreads();
+  __bf16 *ss = snap + n_seq * snap_seq_stride;
+#pragma unroll
+  for (int k = 0; k < TC * TF / 8 / 256; ++k) {  // piece p: column c0 + p % 16, block p / 16
+    const int p = t + 256 * k;
+    const int c = c0 + p % TC, f = f0 + 8 * (p / TC);
+    if (c < s.d && f < s.F)
+      *(bf16x8 *)(ss + snap_offset<true>(s, c, f)) = *(const bf16x8 *)&tile[p % TC][8 * (p / TC)];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // O rows of chunk groups [q0, q0 + nq) of every sequence (G = 1: one chunk per
 // group): O = Z S_q over the group's rows (S_q stored output-major, d rows of
 // d_ff), plus, when pt is given, the updates of the group's earlier chunks as
 // P (eta V), P^T read from the Gram buffer. The MSE rule (G = 1) also writes
 // Rt = eta (V - O)^T.
-template <class C, bool IL = false>
+// BLK: the snapshots are in the blocked layout of snap_offset (the forward's),
+// else row-major [d][F] (the backward's).
+template <class C, bool IL, bool BLK>
 __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC))) void k_apply(
     Slab s, int q0, int nq, const __bf16 *__restrict__ zt, const __bf16 *__restrict__ snap,
     int64_t snap_seq_stride, int64_t snap_group_stride, const __bf16 *__restrict__ pt,
@@ -318,22 +369,36 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
   // the group's slab rows. Columns past the workspace rows are clamped in
   // bounds; the rows they feed are past the group and are dropped.
   LA la;
-  Loader<C, C::B_PIECES> lb;
   la.ld = s.Lp;
 #pragma unroll
   for (int i = 0; i < LA::NP; ++i)
     la.ptr[i] = zts + (int64_t)LA::krow(tid, i) * s.Lp + min(row0 + m0 + LA::col(tid, i), s.Lp - 8);
+  {
+    using LS = typename std::conditional<BLK, BlockLoader<C, C::B_PIECES>,
+                                         Loader<C, C::B_PIECES>>::type;
+    LS lb;
+    int lr0 = r0;
+    if constexpr (BLK) {
+      lb.assign(tid);
+      lr0 = lb.r0;
+      lb.blk = (int64_t)8 * s.d;
+    }
 #pragma unroll
-  for (int i = 0; i < C::B_PIECES; ++i) {
-    const int n = n0 + r0 + C::RPP * i;
-    lb.ptr[i] = ss + (int64_t)(n < s.d ? n : 0) * s.F;
+    for (int i = 0; i < C::B_PIECES; ++i) {
+      const int n = n0 + lr0 + C::RPP * i;
+      if constexpr (BLK)
+        lb.ptr[i] = ss + (int64_t)(n < s.d ? n : 0) * 8;
+      else
+        lb.ptr[i] = ss + (int64_t)(n < s.d ? n : 0) * s.F;
+    }
+    if constexpr (IL)
+      kloop_g_il<C, true, false>(smem, la, lb, s.F / C::BK, tid, wm * C::WTM, brow, acc);
+    else
+      kloop_t<C>(smem, la, lb, s.F / C::BK, tid, wm * C::WTM, brow, acc);
   }
-  if constexpr (IL)
-    kloop_g_il<C, true, false>(smem, la, lb, s.F / C::BK, tid, wm * C::WTM, brow, acc);
-  else
-    kloop_t<C>(smem, la, lb, s.F / C::BK, tid, wm * C::WTM, brow, acc);
 
   if (pts && cs_last > 0) {
+    Loader<C, C::B_PIECES> lb;
     la.ld = RG;
 #pragma unroll
     for (int i = 0; i < LA::NP; ++i)
@@ -460,8 +525,9 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
 // snap_each_group: write S[g] = bf16(W) before group g's accumulation;
 // snap_after: write S = bf16(W) after the last chunk. reverse (G = 1): walk
 // the chunks last to first, snapshot S[j] before chunk j (the backward's
-// G_{j+1}).
-template <class C>
+// G_{j+1}). BLK: snapshots in the blocked layout snap_offset describes (the
+// forward's, read by the apply), else row-major [d][F] (the backward's).
+template <class C, bool BLK>
 __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC))) void k_update(
     Slab s, int j_first, int n_chunks, int G, const __bf16 *__restrict__ zt,
     const __bf16 *__restrict__ bsrc, int64_t b_ld, int64_t b_seq_stride, int64_t b_chunk_stride,
@@ -514,7 +580,7 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
             bf16x4 v;
 #pragma unroll
             for (int r = 0; r < 4; ++r) v[r] = (__bf16)a4[r];
-            *(bf16x4 *)(dst + (int64_t)c * s.F + f) = v;
+            *(bf16x4 *)(dst + snap_offset<BLK>(s, c, f)) = v;
           }
         }
   };
@@ -557,13 +623,7 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
                 "snapshot slots must be whole column tiles of PPS row tiles");
   uint2 sbuf[NSP];
   __bf16 *sdst = snap + n_seq * snap_seq_stride;  // the pending snapshot
-  const int fl = f0 + wm * C::WTM + M::rrow(lane, 0), cl = c0 + wn * C::WTN + M::rcol(lane);
-  auto store_piece = [&](int q) __attribute__((always_inline)) {
-    const int i = q / (C::NJ * M::NG), jj = q / M::NG % C::NJ, g = q % M::NG;
-    const int f = fl + C::FM * i + M::rrow(lane, g) - M::rrow(lane, 0);
-    const int c = cl + C::FM * jj;
-    if (f < s.F && c < s.d) *(uint2 *)(sdst + (int64_t)c * s.F + f) = sbuf[q];
-  };
+  const int cl = c0 + wn * C::WTN + M::rcol(lane);
   auto slot_piece = [](int k, int e) { return ((k / C::NJ) * PPS + e) * C::NJ + k % C::NJ; };
   // Pieces q0, q1 of row tiles i and i + 1 of one column tile: lane l holds 4
   // values (d_ff 4 (l / 16) ..) of each; swapping between lane groups
@@ -577,7 +637,7 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
     const int gq = lane >> 4;
     const int f = f0 + wm * C::WTM + C::FM * i + 8 * (gq >> 1) + C::FM * (gq & 1);
     const int c = cl + C::FM * jj;
-    if (f < s.F && c < s.d) *(uint4 *)(sdst + (int64_t)c * s.F + f) = v;
+    if (f < s.F && c < s.d) *(uint4 *)(sdst + snap_offset<BLK>(s, c, f)) = v;
   };
   static_assert(PPS % 2 == 0 && C::FM == 16, "slots store pairs of 16-row tiles");
   auto store_slot = [&](int slot) __attribute__((always_inline)) {
@@ -610,7 +670,7 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
       nstep = 0;
     } else {
 #pragma unroll
-      for (int q = 0; q < NSP; ++q) store_piece(q);
+      for (int k = 0; k < NSLOT; ++k) store_slot(k);
     }
   };
   auto post = [&](int) __attribute__((always_inline)) {
@@ -629,9 +689,7 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
   kloop_dma_pl<C, NSU, true>(smem, la, lb, nk, wave, lane, wm * C::WTM, brow, acc, koff, pre, post);
 #pragma unroll
   for (int k = 0; k < NSLOT; ++k)
-    if (k >= nslot)
-#pragma unroll
-      for (int e = 0; e < PPS; ++e) store_piece(slot_piece(k, e));
+    if (k >= nslot) store_slot(k);
   if (snap_after) write_snap(snap + n_seq * snap_seq_stride);
 #pragma unroll
   for (int i = 0; i < C::MI; ++i)
@@ -745,27 +803,27 @@ inline int slab_groups(const Slab &s) { return (s.nc + s.G - 1) / s.G; }
 // Apply with every operand explicit: snapshot q0 + i at snap + n * snap_seq +
 // i * snap_group; residual (MSE) to rt + n * rt_seq + c * rt_ld + row.
 // IL: the interleaved loop for blocks of two waves per SIMD (eight-wave blocks)
-template <class C, bool IL = (C::WM * C::WN >= 8)>
+template <class C, bool BLK, bool IL = (C::WM * C::WN >= 8)>
 hipError_t launch_apply_x(const Slab &s, int q0, int nq, const __bf16 *zt, const __bf16 *snap,
                           int64_t snap_seq, int64_t snap_group, const __bf16 *pt, float *o,
                           const __bf16 *vt, __bf16 *rt, int64_t rt_seq, int64_t rt_ld,
                           hipStream_t st) {
   const int64_t RG = (int64_t)s.G * s.Bp;
   const int64_t nb = ((RG + C::BM - 1) / C::BM) * ((s.d + C::BN - 1) / C::BN) * nq * s.n_seq;
-  hipLaunchKernelGGL((k_apply<C, IL>), dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, q0, nq, zt, snap,
+  hipLaunchKernelGGL((k_apply<C, IL, BLK>), dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, q0, nq, zt, snap,
                      snap_seq, snap_group, pt, (int64_t)s.ng_cap * RG * RG, o, vt, rt, rt_seq,
                      rt_ld);
   return hipGetLastError();
 }
 
-template <class C, bool IL = (C::WM * C::WN >= 8)>
+template <class C>
 hipError_t launch_apply(const Slab &s, int q0, int nq, const WsPtrs &ws, float *o,
                         hipStream_t st) {
   const int64_t dF = (int64_t)s.d * s.F;
   const int64_t snap_seq = s.mse ? dF : (int64_t)s.ng_cap * dF;
   const int64_t snap_group = s.mse ? 0 : dF;
   const __bf16 *snap = (const __bf16 *)ws.s + (s.mse ? 0 : (int64_t)q0 * dF);
-  return launch_apply_x<C, IL>(s, q0, nq, (const __bf16 *)ws.zt, snap, snap_seq, snap_group,
+  return launch_apply_x<C, true>(s, q0, nq, (const __bf16 *)ws.zt, snap, snap_seq, snap_group,
                            s.G > 1 ? (const __bf16 *)ws.p : nullptr, o, (const __bf16 *)ws.vt,
                            s.mse ? (__bf16 *)ws.rt : nullptr, (int64_t)s.d * s.Bp, s.Bp, st);
 }
@@ -780,12 +838,12 @@ hipError_t launch_gram(const Slab &s, const WsPtrs &ws, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <class C>
+template <class C, bool BLK>
 hipError_t launch_update_scan(const Slab &s, const WsPtrs &ws, float *w_state, hipStream_t st) {
   const int64_t dF = (int64_t)s.d * s.F;
   const int64_t nb = ((s.F + C::BM - 1) / C::BM) * ((s.d + C::BN - 1) / C::BN) * s.n_seq;
   // B operand: Vt rows c; chunk jc starts jc * Bp tokens along the row
-  hipLaunchKernelGGL(k_update<C>, dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, 0, s.nc, s.G,
+  hipLaunchKernelGGL((k_update<C, BLK>), dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, 0, s.nc, s.G,
                      (const __bf16 *)ws.zt, (const __bf16 *)ws.vt, s.Lp, (int64_t)s.d * s.Lp,
                      (int64_t)s.Bp, w_state, (__bf16 *)ws.s, (int64_t)s.ng_cap * dF, dF, 1, 0, 0);
   return hipGetLastError();
@@ -799,7 +857,7 @@ hipError_t launch_update_reverse(const Slab &s, const __bf16 *zt, const __bf16 *
                                  __bf16 *snap, hipStream_t st) {
   const int64_t dF = (int64_t)s.d * s.F;
   const int64_t nb = ((s.F + C::BM - 1) / C::BM) * ((s.d + C::BN - 1) / C::BN) * s.n_seq;
-  hipLaunchKernelGGL(k_update<C>, dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, 0, s.nc, 1, zt, bt,
+  hipLaunchKernelGGL((k_update<C, false>), dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, 0, s.nc, 1, zt, bt,
                      s.Lp, (int64_t)s.d * s.Lp, (int64_t)s.Bp, g, snap, (int64_t)s.nc_cap * dF, dF,
                      1, 0, 1);
   return hipGetLastError();
@@ -811,7 +869,7 @@ hipError_t launch_update_one(const Slab &s, int j, const WsPtrs &ws, float *w_st
   const int64_t dF = (int64_t)s.d * s.F;
   const int64_t nb = ((s.F + C::BM - 1) / C::BM) * ((s.d + C::BN - 1) / C::BN) * s.n_seq;
   // B operand: Rt [n][d][Bp] of chunk j
-  hipLaunchKernelGGL(k_update<C>, dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, j, 1, 1,
+  hipLaunchKernelGGL((k_update<C, true>), dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, j, 1, 1,
                      (const __bf16 *)ws.zt, (const __bf16 *)ws.rt, (int64_t)s.Bp,
                      (int64_t)s.d * s.Bp, (int64_t)0, w_state, (__bf16 *)ws.s, dF, (int64_t)0, 0,
                      1, 0);
@@ -884,26 +942,35 @@ hipError_t mf_apply_mse_chunk(const Slab &s, int j, const __bf16 *zt, const __bf
   using C = mfma::ApplyCfg;
   const int64_t big_blocks = ((s.Bp + C::BM - 1) / C::BM) * ((s.d + C::BN - 1) / C::BN) * s.n_seq;
   if (big_blocks < 512)
-    return mfma::launch_apply_x<mfma::ApplySmallCfg>(s, j, 1, zt, snap, snap_seq, 0, nullptr,
-                                                     nullptr, vt, rt, rt_seq, rt_ld, st);
-  return mfma::launch_apply_x<C>(s, j, 1, zt, snap, snap_seq, 0, nullptr, nullptr, vt, rt, rt_seq,
-                                 rt_ld, st);
+    return mfma::launch_apply_x<mfma::ApplySmallCfg, false>(s, j, 1, zt, snap, snap_seq, 0, nullptr,
+                                                            nullptr, vt, rt, rt_seq, rt_ld, st);
+  return mfma::launch_apply_x<C, false>(s, j, 1, zt, snap, snap_seq, 0, nullptr, nullptr, vt, rt,
+                                        rt_seq, rt_ld, st);
 }
 hipError_t mf_update_chunk(const Slab &s, int j, const __bf16 *zt, const __bf16 *bsrc,
                            int64_t b_ld, int64_t b_seq, float *w, __bf16 *snap_after,
                            int64_t snap_seq, hipStream_t st) {
   using C = mfma::UpdateCfg;
   const int64_t nb = ((s.F + C::BM - 1) / C::BM) * ((s.d + C::BN - 1) / C::BN) * s.n_seq;
-  hipLaunchKernelGGL(mfma::k_update<C>, dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, j, 1, 1, zt,
+  hipLaunchKernelGGL((mfma::k_update<C, false>), dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, j, 1, 1, zt,
                      bsrc, b_ld, b_seq, (int64_t)0, w, snap_after, snap_seq, (int64_t)0, 0,
                      snap_after ? 1 : 0, 0);
+  return hipGetLastError();
+}
+hipError_t mf_snapshot(const Slab &s, const float *w_state, __bf16 *snap, int64_t snap_seq_stride,
+                       hipStream_t st) {
+  hipLaunchKernelGGL(mfma::k_snapshot_blk, dim3((unsigned)(s.d / 16), (unsigned)((s.F + 255) / 256),
+                                                (unsigned)s.n_seq),
+                     dim3(256), 0, st, s, w_state, snap, snap_seq_stride);
   return hipGetLastError();
 }
 hipError_t mf_gram(const Slab &s, const WsPtrs &ws, hipStream_t st) {
   return mfma::launch_gram<mfma::GramCfg>(s, ws, st);
 }
-hipError_t mf_update_scan(const Slab &s, const WsPtrs &ws, float *w_state, hipStream_t st) {
-  return mfma::launch_update_scan<mfma::UpdateCfg>(s, ws, w_state, st);
+hipError_t mf_update_scan(const Slab &s, const WsPtrs &ws, float *w_state, bool blocked,
+                          hipStream_t st) {
+  if (blocked) return mfma::launch_update_scan<mfma::UpdateCfg, true>(s, ws, w_state, st);
+  return mfma::launch_update_scan<mfma::UpdateCfg, false>(s, ws, w_state, st);
 }
 hipError_t mf_update_one(const Slab &s, int j, const WsPtrs &ws, float *w_state, hipStream_t st) {
   return mfma::launch_update_one<mfma::UpdateCfg>(s, j, ws, w_state, st);

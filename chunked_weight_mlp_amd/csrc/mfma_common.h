@@ -181,6 +181,40 @@ struct Loader {
   }
 };
 
+// Per-thread loader of a K-contiguous operand stored in blocks of 8 K values
+// (element (n, k) at ((k / 8) * rows + n) * 8 + k % 8, the layout of the
+// forward's fast-weight copies): piece q of the K step at k0 of row n is the
+// 16 bytes of block k0 / 8 + q. It fills the same LDS tile as Loader, but a
+// thread's (row, piece) is its own (r0, q below, not the ones the K loop
+// passes): each 16 lanes take rows r .. r + 7 of pieces q, q + 1, two whole
+// 128-byte lines of the blocked layout, and each 8 lanes take 4 rows of both
+// pieces, which land on distinct LDS banks at a 160-byte row pitch.
+template <class C, int NP>
+struct BlockLoader {
+  static_assert(C::KP % 2 == 0 && C::RPP % 8 == 0 && C::NTHR % (8 * C::KP) == 0,
+                "BlockLoader lane map");
+  const __bf16 *ptr[NP];  // row r0 + RPP i of block 0: base + 8 (r0 + RPP i)
+  int64_t blk;            // elements between consecutive blocks (8 x rows)
+  int r0, q;
+  uint4 v[NP];
+  __device__ __forceinline__ void assign(int tid) {
+    const int l16 = tid % 16, g = tid / 16;
+    q = 2 * (g % (C::KP / 2)) + (l16 / 4) % 2;
+    r0 = 8 * (g / (C::KP / 2)) + l16 % 4 + 4 * (l16 / 8);
+  }
+  __device__ __forceinline__ void fetch(int k0, int) {
+#pragma unroll
+    for (int i = 0; i < NP; ++i) v[i] = ld16(ptr[i] + (int64_t)(k0 / 8 + q) * blk);
+  }
+  __device__ __forceinline__ void stash(__bf16 *stage, int, int) const {
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int row = r0 + C::RPP * i;
+      *(uint4 *)(stage + row * C::PITCH + kslot<C>(row, 8 * q)) = v[i];
+    }
+  }
+};
+
 // MFMA sub-steps [U0, U1) of one LDS stage (all of them by default).
 template <class C, int U0 = 0, int U1 = C::BK / C::M::K>
 __device__ __forceinline__ void mma_stage(const __bf16 *As, const __bf16 *Bs, int arow0,
@@ -289,9 +323,9 @@ constexpr int mid_step() {
 // arithmetically from the __shared__ base so the compiler keeps them in the
 // LDS address space (ds_read / ds_write, not flat).
 // A K-major (transposed) operand and a K-contiguous B operand (the apply):
-template <class C>
-__device__ __forceinline__ void kloop_t(__bf16 *smem, LoaderT<C, C::BM> &la,
-                                        Loader<C, C::B_PIECES> &lb, int nk, int tid, int arow0,
+template <class C, class LB>
+__device__ __forceinline__ void kloop_t(__bf16 *smem, LoaderT<C, C::BM> &la, LB &lb, int nk,
+                                        int tid, int arow0,
                                         const int (&brow)[C::NJ],
                                         typename C::acc_t (&acc)[C::MI][C::NJ]) {
   __bf16 *const Bbase = smem + 2 * C::AT_STAGE;
@@ -376,6 +410,13 @@ template <class C, int NP>
 __device__ __forceinline__ void gstash(const Loader<C, NP> &l, __bf16 *st, int, int r0, int q) {
   l.stash(st, r0, q);
 }
+template <class C, int NP>
+__device__ __forceinline__ void gfetch(BlockLoader<C, NP> &l, int k0, int q) { l.fetch(k0, q); }
+template <class C, int NP>
+__device__ __forceinline__ void gstash(const BlockLoader<C, NP> &l, __bf16 *st, int, int r0,
+                                       int q) {
+  l.stash(st, r0, q);
+}
 template <class C, int COLS>
 __device__ __forceinline__ void gstash(const LoaderT<C, COLS> &l, __bf16 *st, int tid, int, int) {
   l.stash(st, tid);
@@ -445,9 +486,8 @@ __device__ __forceinline__ void kloop_g(__bf16 *smem, typename GLoaders<C, TA, T
 // waves leave each barrier together, so bursts of memory instructions before
 // or after the MFMAs leave the SIMDs idle). The last step (no next stage) is
 // peeled, so each main-loop step is one block. Same arithmetic as kloop_g.
-template <class C, bool TA, bool TB>
-__device__ __forceinline__ void kloop_g_il(__bf16 *smem, typename GLoaders<C, TA, TB>::LA &la,
-                                           typename GLoaders<C, TA, TB>::LB &lb, int nk, int tid,
+template <class C, bool TA, bool TB, class LA, class LB>
+__device__ __forceinline__ void kloop_g_il(__bf16 *smem, LA &la, LB &lb, int nk, int tid,
                                            int arow0, const int (&brow)[C::NJ],
                                            typename C::acc_t (&acc)[C::MI][C::NJ]) {
   using GL = GLoaders<C, TA, TB>;
