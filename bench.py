@@ -144,11 +144,13 @@ def achievable_fracs(ach: dict, roof: dict, n3_tflops=None) -> dict:
 
 
 def group_chunks(w: wl.Workload, requested: int, generic: bool) -> int:
-    """Chunks per W snapshot, as the library picks them: groups of about 1024
-    chunk-padded rows on the bf16 MFMA path with the linear rule, else 1."""
-    if w.update != "linear" or w.dtype != "bf16" or generic:
+    """Chunks per group, as the library picks them on the bf16 MFMA path:
+    about 1024 chunk-padded rows with the linear rule, 2048 with the MSE rule;
+    1 on the generic kernels."""
+    if w.dtype != "bf16" or generic:
         return 1
-    return requested or max(1, 1024 // (-(-w.chunk // 64) * 64))
+    rows = 2048 if w.update == "mse" else 1024
+    return requested or max(1, rows // (-(-w.chunk // 64) * 64))
 
 
 def kernel_work(w: wl.Workload, tokens: int, G: int = 1):
@@ -156,10 +158,11 @@ def kernel_work(w: wl.Workload, tokens: int, G: int = 1):
     tokens (all sequences of one pass), with one W snapshot per G chunks. Bytes
     count each operand once per use the method makes of it: the linear scan
     reads and writes each sequence's fp32 W once per pass and writes one bf16
-    copy per group; the MSE rule reads and writes W and its copy every chunk.
+    copy per group; the MSE rule reads and writes W and its copy every group.
     The apply counts the method's product Z W only; the Gram kernel's work (and
-    the apply's use of it) is what the chunk-parallel form spends to skip
-    snapshots, reported for its own rate."""
+    the apply's use of it, and the MSE rule's per-chunk corrections) is what
+    the chunk-parallel form spends to skip snapshots, reported for its own
+    rate."""
     d, F, Kc, n = w.d, w.d_ff, w.conv_k, w.n_seq
     el = 2 if w.dtype == "bf16" else 4
     chunks = -(-(tokens // n) // w.chunk)   # per sequence
@@ -167,8 +170,8 @@ def kernel_work(w: wl.Workload, tokens: int, G: int = 1):
     rows = G * (-(-w.chunk // 64) * 64)
     W32, Wb = 4 * F * d, el * F * d         # one sequence's fp32 W and its copy
     if w.update == "mse":
-        upd = el * tokens * (F + d) + n * chunks * (2 * W32 + Wb)
-        app = el * tokens * (F + d) + n * chunks * Wb + 4 * tokens * d
+        upd = el * tokens * (F + d) + n * groups * (2 * W32 + Wb)
+        app = el * tokens * (F + d) + n * groups * Wb + 4 * tokens * d
     else:
         upd = el * tokens * (F + d) + n * (2 * W32 + groups * Wb)
         app = el * tokens * F + n * groups * Wb + 4 * tokens * d
@@ -181,6 +184,14 @@ def kernel_work(w: wl.Workload, tokens: int, G: int = 1):
     }
     if G > 1:  # block-causal Z Z^T: about half of each group's rows x rows x F
         work["gram"] = (rows * F * tokens, el * tokens * F + el * tokens * rows // 2)
+    if G > 1 and w.update == "mse":
+        # chunk jl of a group: O += P R over the jl Bp earlier rows, all chunks but
+        # the first; P and R blocks read, O read and written, V read, Rt written
+        Bp = rows // G
+        pairs = n * groups * G * (G - 1) // 2
+        later = tokens * (G - 1) // G
+        work["mse_fix"] = (2 * pairs * Bp * Bp * d,
+                           el * pairs * Bp * (Bp + d) + later * d * (8 + 2 * el))
     return work
 
 
@@ -455,7 +466,8 @@ def main():
     roof["traffic"] = None if args.generic else load_traffic(w.name, dom)
     # the fast-weight step on its own (apply + update, and the Gram product of
     # chunk groups): algorithmic 4 d d_ff FLOPs per token
-    n3_ms = sum(prof[k][1] for k in ("update", "apply", "gram", "snapshot") if prof[k][0]) / args.steps
+    n3_ms = sum(prof[k][1] for k in ("update", "apply", "gram", "snapshot", "mse_fix")
+                if prof[k][0]) / args.steps
     n3_fl = 4 * w.d * w.d_ff * tokens
     n3 = {"ms_per_step": round(n3_ms, 4), "tflops": round(n3_fl / (n3_ms * 1e-3) / 1e12, 2),
           "frac_of_peak": round(n3_fl / (n3_ms * 1e-3) / 1e12 / PEAK[w.dtype], 4)}

@@ -50,7 +50,7 @@ constexpr size_t kScratchBytes = IPTTT_NOALLOC_SCRATCH_BYTES;
 hipError_t scratch_setup(void **out);
 
 // need_z: the token-major copy of Z (read by the generic apply only).
-// G: chunks per snapshot group (linear rule; 1 for MSE and the generic path).
+// G: chunks per group (bf16 MFMA path; 1 on the generic path).
 WsLayout ws_layout(int elem, int n_seq, int d, int F, int Bp, int nc_cap, int G, int mse,
                    int need_z);
 
@@ -126,6 +126,15 @@ hipError_t mf_snapshot(const Slab &s, const float *w_state, __bf16 *snap, int64_
 // the layout of mf_snapshot.
 hipError_t mf_update_one(const Slab &s, int j, const WsPtrs &ws, float *w_state,
                          hipStream_t st);
+// MSE rule over chunk groups (G > 1), group q: O = Z S for the group's rows (S:
+// W at its first chunk) and Rt = eta (V - O)^T ([n][d][G Bp]) from them; then
+// mf_mse_fix for its chunks jl = 1 .. in order (O += the Gram term over the
+// earlier chunks' residuals, Rt of the chunk's rows), then mf_update_group
+// (W += Zt Rt over the group's chunks, S = bf16(W)).
+hipError_t mf_apply_mse_group(const Slab &s, int q, const WsPtrs &ws, float *o, hipStream_t st);
+hipError_t mf_mse_fix(const Slab &s, int q, int jl, const WsPtrs &ws, float *o, hipStream_t st);
+hipError_t mf_update_group(const Slab &s, int q, const WsPtrs &ws, float *w_state,
+                           hipStream_t st);
 // O rows of groups [q0, q0 + nq) (G = 1: chunks): O = Z S_q (S in the layout
 // of mf_snapshot), plus P (eta V) when G > 1; the MSE rule (G = 1, nq = 1)
 // also writes Rt.

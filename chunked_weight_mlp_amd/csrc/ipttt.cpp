@@ -99,12 +99,17 @@ bool use_mfma(const ipttt_layer_desc *d) {
 // to one per 1024 rows.
 constexpr int kDefaultGroupRows = 1024;
 
-// Chunks per group of the chunk-parallel scan (bf16 MFMA path, linear rule);
-// 1 elsewhere. A slab of n chunks uses min(G, n).
+// The MSE rule's default: its groups trade the Gram term (a cost growing with
+// the group) against streaming W through HBM once per group.
+constexpr int kDefaultMseGroupRows = 2048;
+
+// Chunks per group of the chunk-parallel scan (bf16 MFMA path); 1 elsewhere.
+// A slab of n chunks uses min(G, n).
 int group_chunks(const ipttt_layer_desc *d) {
-  if (!use_mfma(d) || d->update != IPTTT_UPDATE_LINEAR) return 1;
+  if (!use_mfma(d)) return 1;
   if (d->group_chunks > 0) return d->group_chunks;
-  return std::max(1, kDefaultGroupRows / chunk_pitch(d->chunk));
+  const int rows = d->update == IPTTT_UPDATE_MSE ? kDefaultMseGroupRows : kDefaultGroupRows;
+  return std::max(1, rows / chunk_pitch(d->chunk));
 }
 
 ipttt_status hip_status(hipError_t e, const char *what) {
@@ -174,7 +179,7 @@ WsLayout ws_layout(int elem, int n_seq, int d, int F, int Bp, int nc_cap, int G,
   w.c = take((size_t)n_seq * Lp * d * elem);
   w.vt = take((size_t)n_seq * d * Lp * elem);
   w.s = take((size_t)n_seq * (mse ? 1 : ng) * d * F * elem);
-  w.rt = mse ? take((size_t)n_seq * d * Bp * elem) : off;
+  w.rt = mse ? take((size_t)n_seq * d * RG * elem) : off;
   w.p = G > 1 ? take((size_t)n_seq * ng * RG * RG * elem) : off;
   w.total = off;
   return w;
@@ -379,9 +384,24 @@ ipttt_status run_scan(ipttt_layer *h, const T *x, const T *e, float *o, int slot
         if (k0 == 0)
           LAUNCH(IPTTT_K_SNAPSHOT, mf_snapshot(s, wst, (__bf16 *)ws.s, snap_seq_stride, st),
                  "snapshot launch");
-        for (int j = 0; j < s.nc; ++j) {
-          LAUNCH(IPTTT_K_APPLY, mf_apply(s, j, 1, ws, o, st), "apply launch");
-          LAUNCH(IPTTT_K_UPDATE, mf_update_one(s, j, ws, wst, st), "update launch");
+        if (G > 1 && o) {
+          // chunk groups: one apply, the chunks' Gram corrections in order, one update
+          LAUNCH(IPTTT_K_GRAM, mf_gram(s, ws, st), "Gram launch");
+          for (int q = 0; q * G < s.nc; ++q) {
+            LAUNCH(IPTTT_K_APPLY, mf_apply_mse_group(s, q, ws, o, st), "apply launch");
+            for (int jl = 1; jl < G && q * G + jl < s.nc; ++jl)
+              LAUNCH(IPTTT_K_MSE_FIX, mf_mse_fix(s, q, jl, ws, o, st), "MSE correction launch");
+            LAUNCH(IPTTT_K_UPDATE, mf_update_group(s, q, ws, wst, st), "update launch");
+          }
+        } else {
+          // chunk by chunk (also when only the updates are wanted: the groups'
+          // corrections need the outputs)
+          s.G = 1;
+          s.ng_cap = nc_cap;
+          for (int j = 0; j < s.nc; ++j) {
+            LAUNCH(IPTTT_K_APPLY, mf_apply(s, j, 1, ws, o, st), "apply launch");
+            LAUNCH(IPTTT_K_UPDATE, mf_update_one(s, j, ws, wst, st), "update launch");
+          }
         }
       }
     } else {

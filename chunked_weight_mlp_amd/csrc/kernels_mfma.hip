@@ -447,6 +447,102 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
 }
 
 // ---------------------------------------------------------------------------
+// MSE rule over chunk groups (G > 1), chunk jl >= 1 of group q of every
+// sequence. The apply wrote the group's rows O = Z S_q (S_q: W at the group's
+// first chunk) and Rt = eta (V - O)^T from them, which is final for chunk 0.
+// Chunk jl adds what the group's earlier chunks changed in W: with R_i their
+// final residuals, W_jl = W_q + sum over i < jl of Z_i^T R_i, so
+//   O_jl = Z_jl S_q + sum over group rows s of earlier chunks of (z_m . z_s) R_s,
+// the Gram term read from P^T (block-causal, as the linear rule's). Then
+// Rt = eta (V - O)^T for the chunk's rows, which chunks after it read.
+// A = P^T (rows s, K-major), B = Rt rows c (token-contiguous, pitch G Bp).
+template <class C, bool IL>
+__global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC))) void k_mse_fix(
+    Slab s, int q, int jl, const __bf16 *__restrict__ pt, int64_t pt_seq_stride,
+    const __bf16 *__restrict__ vt, __bf16 *__restrict__ rt, int64_t rt_seq_stride,
+    float *__restrict__ o) {
+  static_assert(C::SMEM_T_ELEMS * 2 <= 160 * 1024, "LDS overflow");
+  static_assert(kChunkAlign % C::BK == 0, "chunk starts must be whole K steps");
+  __shared__ __bf16 smem[C::SMEM_T_ELEMS];
+  using M = typename C::M;
+  using LA = LoaderT<C, C::BM>;
+  const int RG = s.G * s.Bp;  // rows of a full group
+  const int nm = (s.Bp + C::BM - 1) / C::BM, nn = (s.d + C::BN - 1) / C::BN;
+  const int per_seq = nm * nn;
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  const int n_seq = id / per_seq;
+  int tm, tn;
+  tile_of<C::GM>(id % per_seq, nm, nn, tm, tn);
+  const int cs = jl * s.Bp;           // the chunk's first group row = rows of earlier chunks
+  const int m0 = cs + tm * C::BM, n0 = tn * C::BN;
+  const int mend = cs + s.Bp;         // rows past the chunk belong to the next one
+  const int j_first = q * s.G;
+  const int64_t row0 = (int64_t)j_first * s.Bp;  // the group's first slab row
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int r0 = tid / C::KP;
+  int brow[C::NJ];
+#pragma unroll
+  for (int jj = 0; jj < C::NJ; ++jj) brow[jj] = wn * C::WTN + C::FM * jj;
+  typename C::acc_t acc[C::MI][C::NJ];
+  zero_acc<C>(acc);
+  const __bf16 *pts = pt + n_seq * pt_seq_stride + (int64_t)q * RG * RG;
+  __bf16 *rts = rt + n_seq * rt_seq_stride;
+  const __bf16 *vts = vt + (int64_t)n_seq * s.d * s.Lp;
+  {
+    LA la;
+    la.ld = RG;
+#pragma unroll
+    for (int i = 0; i < LA::NP; ++i)
+      la.ptr[i] = pts + (int64_t)LA::krow(tid, i) * RG + min(m0 + LA::col(tid, i), RG - 8);
+    Loader<C, C::B_PIECES> lb;
+#pragma unroll
+    for (int i = 0; i < C::B_PIECES; ++i) {
+      const int n = n0 + r0 + C::RPP * i;
+      lb.ptr[i] = rts + (int64_t)(n < s.d ? n : 0) * RG;
+    }
+    if constexpr (IL)
+      kloop_g_il<C, true, false>(smem, la, lb, cs / C::BK, tid, wm * C::WTM, brow, acc);
+    else
+      kloop_t<C>(smem, la, lb, cs / C::BK, tid, wm * C::WTM, brow, acc);
+  }
+
+  float *os = o + n_seq * s.x_seq_stride;
+#pragma unroll
+  for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+    for (int g = 0; g < M::NG; ++g) {
+      // rows m .. m + 3 share one chunk (Bp is a multiple of 4)
+      const int m = m0 + wm * C::WTM + C::FM * i + M::rrow(lane, g);
+      if (m >= mend) continue;
+      const int ic = m - cs;
+      const int64_t t0 = s.tok0 + (int64_t)(j_first + jl) * s.B + ic;
+      bool valid[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) valid[r] = ic + r < s.B && t0 + r < s.L;
+#pragma unroll
+      for (int jj = 0; jj < C::NJ; ++jj) {
+        const int n = n0 + wn * C::WTN + C::FM * jj + M::rcol(lane);
+        if (n >= s.d) continue;
+        const f32x4 a4 = get4(acc[i][jj], g);
+        const bf16x4 v = *(const bf16x4 *)(vts + (int64_t)n * s.Lp + row0 + m);
+        bf16x4 rv;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float ov = 0.f;
+          if (valid[r]) {
+            ov = os[(t0 + r) * s.d + n] + a4[r];
+            os[(t0 + r) * s.d + n] = ov;
+          }
+          rv[r] = (__bf16)(valid[r] ? s.eta * ((float)v[r] - ov) : 0.f);
+        }
+        *(bf16x4 *)(rts + (int64_t)n * RG + m) = rv;
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Block-causal Gram of chunk groups [0, ng) of the slab: P^T[s][m] = z_m . z_s
 // (a sum over d_ff) when group row s lies in an earlier chunk than group row
 // m, else 0. A = Zt columns m, B = Zt columns s, both K-major (rows of d_ff)
@@ -849,6 +945,20 @@ hipError_t launch_update_scan(const Slab &s, const WsPtrs &ws, float *w_state, h
   return hipGetLastError();
 }
 
+// MSE rule over chunk groups: W += sum over the chunks of group q of
+// Zt_j . Rt_j (Rt [n][d][G Bp], the group's rows), then S = bf16(W).
+template <class C>
+hipError_t launch_update_group(const Slab &s, int q, const WsPtrs &ws, float *w_state,
+                               hipStream_t st) {
+  const int64_t dF = (int64_t)s.d * s.F, RG = (int64_t)s.G * s.Bp;
+  const int j_first = q * s.G, n_chunks = std::min(s.G, s.nc - j_first);
+  const int64_t nb = ((s.F + C::BM - 1) / C::BM) * ((s.d + C::BN - 1) / C::BN) * s.n_seq;
+  hipLaunchKernelGGL((k_update<C, true>), dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, j_first,
+                     n_chunks, 1, (const __bf16 *)ws.zt, (const __bf16 *)ws.rt, RG, s.d * RG,
+                     (int64_t)s.Bp, w_state, (__bf16 *)ws.s, dF, (int64_t)0, 0, 1, 0);
+  return hipGetLastError();
+}
+
 // Backward scan: G (fp32, [n][d][F] like W) += Zt_j . Bt_j over the chunks in
 // reverse, writing snap[n][j] = bf16(G) before chunk j. Bt rows c are
 // token-contiguous with the slab's row layout (pitch Lp).
@@ -935,6 +1045,41 @@ hipError_t mf_apply(const Slab &s, int q0, int nq, const WsPtrs &ws, float *o, h
                              ((s.d + C::BN - 1) / C::BN) * (int64_t)nq * s.n_seq;
   if (big_blocks < 512) return mfma::launch_apply<mfma::ApplySmallCfg>(s, q0, nq, ws, o, st);
   return mfma::launch_apply<C>(s, q0, nq, ws, o, st);
+}
+hipError_t mf_apply_mse_group(const Slab &s, int q, const WsPtrs &ws, float *o, hipStream_t st) {
+  using C = mfma::ApplyCfg;
+  const int64_t RG = (int64_t)s.G * s.Bp, dF = (int64_t)s.d * s.F;
+  const int64_t big_blocks = ((RG + C::BM - 1) / C::BM) * ((s.d + C::BN - 1) / C::BN) * s.n_seq;
+  const __bf16 *zt = (const __bf16 *)ws.zt, *snap = (const __bf16 *)ws.s,
+               *vt = (const __bf16 *)ws.vt;
+  __bf16 *rt = (__bf16 *)ws.rt;
+  if (big_blocks < 512)
+    return mfma::launch_apply_x<mfma::ApplySmallCfg, true>(s, q, 1, zt, snap, dF, 0, nullptr, o, vt,
+                                                           rt, s.d * RG, RG, st);
+  return mfma::launch_apply_x<C, true>(s, q, 1, zt, snap, dF, 0, nullptr, o, vt, rt, s.d * RG, RG,
+                                       st);
+}
+hipError_t mf_mse_fix(const Slab &s, int q, int jl, const WsPtrs &ws, float *o, hipStream_t st) {
+  using C = mfma::ApplyCfg;
+  using CS = mfma::ApplySmallCfg;
+  const int64_t RG = (int64_t)s.G * s.Bp;
+  const int64_t big_blocks = ((s.Bp + C::BM - 1) / C::BM) * ((s.d + C::BN - 1) / C::BN) * s.n_seq;
+  const __bf16 *pt = (const __bf16 *)ws.p, *vt = (const __bf16 *)ws.vt;
+  __bf16 *rt = (__bf16 *)ws.rt;
+  const int64_t pseq = (int64_t)s.ng_cap * RG * RG;
+  if (big_blocks < 512) {
+    const int64_t nb = ((s.Bp + CS::BM - 1) / CS::BM) * ((s.d + CS::BN - 1) / CS::BN) * s.n_seq;
+    hipLaunchKernelGGL((mfma::k_mse_fix<CS, (CS::WM * CS::WN >= 8)>), dim3((unsigned)nb),
+                       dim3(CS::NTHR), 0, st, s, q, jl, pt, pseq, vt, rt, s.d * RG, o);
+  } else {
+    hipLaunchKernelGGL((mfma::k_mse_fix<C, (C::WM * C::WN >= 8)>), dim3((unsigned)big_blocks),
+                       dim3(C::NTHR), 0, st, s, q, jl, pt, pseq, vt, rt, s.d * RG, o);
+  }
+  return hipGetLastError();
+}
+hipError_t mf_update_group(const Slab &s, int q, const WsPtrs &ws, float *w_state,
+                           hipStream_t st) {
+  return mfma::launch_update_group<mfma::UpdateCfg>(s, q, ws, w_state, st);
 }
 hipError_t mf_apply_mse_chunk(const Slab &s, int j, const __bf16 *zt, const __bf16 *snap,
                               int64_t snap_seq, const __bf16 *vt, __bf16 *rt, int64_t rt_seq,

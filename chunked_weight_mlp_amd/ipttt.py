@@ -37,7 +37,8 @@ EXPORTS = (
 )
 
 KERNELS = ("gateup", "conv", "proj", "update", "apply", "snapshot", "gram",  # ipttt_kernel order
-           "bw_scan", "bw_dz", "bw_dv", "bw_dx", "bw_dw", "bw_small", "bw_misc")
+           "bw_scan", "bw_dz", "bw_dv", "bw_dx", "bw_dw", "bw_small", "bw_misc",
+           "mse_fix")
 
 
 class LayerDesc(ctypes.Structure):

@@ -250,7 +250,8 @@ typedef enum {
   IPTTT_K_BW_DW = 11,   /* backward: dW_gate, dW_up                  */
   IPTTT_K_BW_SMALL = 12,/* backward: dC, dProj, conv adjoint, dW_0   */
   IPTTT_K_BW_MISC = 13, /* backward: transposes, fills, copies       */
-  IPTTT_K_COUNT = 14
+  IPTTT_K_MSE_FIX = 14, /* MSE rule, chunk groups: Gram correction   */
+  IPTTT_K_COUNT = 15
 } ipttt_kernel;
 
 ipttt_status ipttt_profile_begin(ipttt_layer *h);

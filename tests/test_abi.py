@@ -115,7 +115,8 @@ def test_workspace_bytes(lib):
 
 
 def test_workspace_bytes_of_chunk_groups(lib):
-    """Groups of G chunks share one W snapshot and add a (G Bp)^2 Gram buffer."""
+    """Groups of G chunks share one W snapshot and add a (G Bp)^2 Gram buffer
+    (linear rule); the MSE rule's groups add the Gram buffer and residual rows."""
     mem = FakeMem()
     d, F, Bc = 64, 256, 64
     el = 2
@@ -131,10 +132,18 @@ def test_workspace_bytes_of_chunk_groups(lib):
     auto = B.ipttt_workspace_bytes(make_desc(mem, chunk=Bc, group_chunks=0), 1, 32)
     g16 = B.ipttt_workspace_bytes(make_desc(mem, chunk=Bc, group_chunks=16), 1, 32)
     assert auto == g16
-    # the rule, the generic kernels and fp32 layers keep one snapshot per chunk
-    for kw in (dict(update=1), dict(flags=B.IPTTT_FLAG_GENERIC_KERNELS), dict(in_dtype=0)):
+    # the generic kernels and fp32 layers keep one snapshot per chunk
+    for kw in (dict(flags=B.IPTTT_FLAG_GENERIC_KERNELS), dict(in_dtype=0)):
         assert (B.ipttt_workspace_bytes(make_desc(mem, chunk=Bc, group_chunks=4, **kw), 1, 8) ==
                 B.ipttt_workspace_bytes(make_desc(mem, chunk=Bc, group_chunks=1, **kw), 1, 8))
+    # the MSE rule keeps one copy of W either way; its groups hold the residuals
+    # of all their rows (d x G Bp) and the Gram buffer
+    mse1 = B.ipttt_workspace_bytes(make_desc(mem, chunk=Bc, group_chunks=1, update=1), 1, 8)
+    mse4 = B.ipttt_workspace_bytes(make_desc(mem, chunk=Bc, group_chunks=4, update=1), 1, 8)
+    assert mse4 - mse1 == 3 * d * Bc * el + 2 * (4 * Bc) ** 2 * el
+    # default: about 2048 padded rows per group (32 chunks of 64)
+    assert (B.ipttt_workspace_bytes(make_desc(mem, chunk=Bc, group_chunks=0, update=1), 1, 64) ==
+            B.ipttt_workspace_bytes(make_desc(mem, chunk=Bc, group_chunks=32, update=1), 1, 64))
 
 
 @pytest.mark.parametrize("kw,status", [
