@@ -521,21 +521,29 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
       bool valid[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) valid[r] = ic + r < s.B && t0 + r < s.L;
+      // every load of the row tile before its stores, so one wait covers them
+      f32x4 ob[C::NJ];
+      bf16x4 vb[C::NJ];
+#pragma unroll
+      for (int jj = 0; jj < C::NJ; ++jj) {
+        // clamped in bounds and loaded unconditionally; rows and columns out of
+        // range are never stored
+        const int n = min(n0 + wn * C::WTN + C::FM * jj + M::rcol(lane), s.d - 1);
+        vb[jj] = *(const bf16x4 *)(vts + (int64_t)n * s.Lp + row0 + m);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ob[jj][r] = os[min(t0 + r, s.L - 1) * s.d + n];
+      }
 #pragma unroll
       for (int jj = 0; jj < C::NJ; ++jj) {
         const int n = n0 + wn * C::WTN + C::FM * jj + M::rcol(lane);
         if (n >= s.d) continue;
         const f32x4 a4 = get4(acc[i][jj], g);
-        const bf16x4 v = *(const bf16x4 *)(vts + (int64_t)n * s.Lp + row0 + m);
         bf16x4 rv;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float ov = 0.f;
-          if (valid[r]) {
-            ov = os[(t0 + r) * s.d + n] + a4[r];
-            os[(t0 + r) * s.d + n] = ov;
-          }
-          rv[r] = (__bf16)(valid[r] ? s.eta * ((float)v[r] - ov) : 0.f);
+          const float ov = ob[jj][r] + a4[r];
+          if (valid[r]) os[(t0 + r) * s.d + n] = ov;
+          rv[r] = (__bf16)(valid[r] ? s.eta * ((float)vb[jj][r] - ov) : 0.f);
         }
         *(bf16x4 *)(rts + (int64_t)n * RG + m) = rv;
       }
