@@ -27,7 +27,8 @@ METRIC = "fast-weight prefill tokens/s per MLP layer at L=128k,B=1024; % MFMA/HB
 KERNEL_SRCS = [os.path.join(ROOT, "chunked_weight_mlp_amd", "csrc", f)
                for f in ("kernels_mfma.hip", "mfma_common.h")]
 KERNEL_TAGS = {"gateup": "k_gateup", "conv": "k_conv", "proj": "k_proj", "update": "k_update",
-               "apply": "k_apply", "gram": "k_gram", "copy": "copyBuffer"}
+               "apply": "k_apply", "gram": "k_gram", "snapshot": "k_snapshot",
+               "mse_fix": "k_mse_fix", "copy": "copyBuffer"}
 
 
 def kernel_source_hash() -> str:
@@ -47,7 +48,9 @@ def summarize_traffic(workload: str, fetch_csv: str, write_csv: str) -> dict:
     """HBM bytes per launch of each kernel from two rocprofv3 --pmc runs of this
     benchmark (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each scaled by
     what the same counter reads for the reset's plain device copy of W_0
-    (d * d_ff * 4 bytes read and written) in the same run."""
+    (d * d_ff * 4 bytes read and written, one per sequence) in the same run:
+    the median over those copies, so a stray small copy of the runtime's does
+    not skew it."""
     import csv
     w = wl.WORKLOADS[workload]
     copy_bytes = w.d * w.d_ff * 4
@@ -60,7 +63,11 @@ def summarize_traffic(workload: str, fetch_csv: str, write_csv: str) -> dict:
             for k, tag in KERNEL_TAGS.items():
                 if tag in r["Kernel_Name"]:
                     vals.setdefault(k, []).append(float(r["Counter_Value"]) * 1024.0)
-        return {k: sum(v) / len(v) for k, v in vals.items()}
+        out = {k: sum(v) / len(v) for k, v in vals.items()}
+        if "copy" in vals:
+            c = sorted(vals["copy"])
+            out["copy"] = c[len(c) // 2]
+        return out
 
     fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
     f_fetch, f_write = copy_bytes / fetch["copy"], copy_bytes / write["copy"]
