@@ -295,14 +295,22 @@ __global__ __launch_bounds__(256) void k_snapshot_blk(Slab s, const float *__res
   const int c0 = blockIdx.x * TC, f0 = blockIdx.y * TF, n_seq = blockIdx.z;
   const int t = threadIdx.x;
   const float *ws = w + (int64_t)n_seq * s.d * s.F;
-  {  // thread t: row c0 + t / 16, 16 columns from f0 + 16 (t % 16)
-    const int c = c0 + t / 16, f = f0 + 16 * (t % 16);
+  {  // thread t: rows c0 + t / 64 + 4 i, 4 columns from f0 + 4 (t % 64): each wave
+     // reads 1 KB of one row per load, all four loads in flight together
+    const int f = f0 + 4 * (t % 64);
+    f32x4 v[4];
 #pragma unroll
-    for (int k = 0; k < 16; k += 4) {
-      f32x4 v = (c < s.d && f + k < s.F) ? *(const f32x4 *)(ws + (int64_t)c * s.F + f + k)
-                                         : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 4; ++i) {
+      const int c = c0 + t / 64 + 4 * i;
+      v[i] = (c < s.d && f < s.F) ? *(const f32x4 *)(ws + (int64_t)c * s.F + f)
+                                  : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) tile[t / 16][16 * (t % 16) + k + r] = (__bf16)v[r];
+    for (int i = 0; i < 4; ++i) {
+      bf16x4 b;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) b[r] = (__bf16)v[i][r];
+      *(bf16x4 *)&tile[t / 64 + 4 * i][4 * (t % 64)] = b;
     }
   }
   __syncthreads();

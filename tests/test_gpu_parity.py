@@ -315,11 +315,15 @@ def test_batch_independence_bitwise():
     assert torch.equal(o2[1], o[1])
 
 
-def test_packed_documents():
-    w = BF16_SMALL.replace(n_seq=1, seq_len=900, chunk=128)
+@pytest.mark.parametrize("update,Bc,L,starts", [
+    ("linear", 128, 900, [200, 333, 700]),
+    ("mse", 64, 1500, [200, 333, 1100]),   # documents of 3-12 chunks: MSE chunk groups per document
+])
+def test_packed_documents(update, Bc, L, starts):
+    w = BF16_SMALL.replace(n_seq=1, seq_len=L, chunk=Bc, update=update,
+                           eta=1e-2 if update == "linear" else 2e-3)
     weights = wl.make_weights(w)
     x, e = wl.make_inputs(w)
-    starts = [200, 333, 700]
     layer = make_layer(w, weights)
     layer.reset()
     o = layer.prefill_packed(x[0].to(DEV), e[0].to(DEV), starts)
@@ -327,7 +331,7 @@ def test_packed_documents():
     ow = wl.to_oracle(weights)
     O_ref, W_ref = oracle.prefill_with_resets(x[0].double().numpy(), e[0].double().numpy(), ow["W_g"],
                                               ow["W_u"], ow["conv_w"], ow["Proj"], ow["W_0"], w.eta,
-                                              w.chunk, starts)
+                                              w.chunk, starts, update=update)
     # chunks restart at every document start
     ce = ChunkErrors("packed")
     og = o.double().cpu().numpy()
