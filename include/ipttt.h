@@ -82,18 +82,23 @@ typedef enum { IPTTT_UPDATE_LINEAR = 0, IPTTT_UPDATE_MSE = 1 } ipttt_update;
  * order); fp32 layers always use them. */
 #define IPTTT_FLAG_GENERIC_KERNELS 1u
 
-/* Chunk-parallel linear scan (bf16 MFMA path, linear rule). The linear update
- * is associative, a plain sum of per-chunk terms (explainer page §2.3), so a
- * group of G consecutive chunks can share one copy of W: with W_q the fast
- * weight at the group's first chunk,
+/* Chunk groups (bf16 MFMA path). The linear update is associative, a plain
+ * sum of per-chunk terms (explainer page §2.3), so a group of G consecutive
+ * chunks can share one copy of W: with W_q the fast weight at the group's
+ * first chunk,
  *   O_t = z_t W_q + sum over earlier-chunk tokens s of the group of
  *         (z_t . z_s) eta v_s,
  * which is O_k = Z_k W_k for every chunk k of the group. The scan then keeps
  * one bf16 copy of W per group instead of per chunk, and the apply adds the
- * block-causal Gram term. group_chunks sets G (1 gives the plain chunk scan;
- * G * round_up(chunk, 64) must not exceed 4096); 0 lets the library choose,
- * about 1024 chunk-padded rows per group. Results agree with the plain scan
- * up to bf16 rounding. Other paths ignore the field. */
+ * block-causal Gram term. The MSE rule (analysis page, 第二板斧) groups the
+ * same way with the residuals r_s = eta (v_s - o_s) of the earlier chunks in
+ * place of eta v_s; those are final only once their own chunk is, so the
+ * chunks of a group are corrected in order, and W is updated once per group.
+ * group_chunks sets G (1 gives the plain chunk scan; G * round_up(chunk, 64)
+ * must not exceed 4096); 0 lets the library choose, about 1024 chunk-padded
+ * rows per group for the linear rule and 2048 for the MSE rule. Results agree
+ * with the plain scan up to bf16 rounding. The generic kernels ignore the
+ * field. */
 typedef struct {
   int32_t d;           /* model width (columns of X, E, O)                       */
   int32_t d_ff;        /* MLP width F (rows of the fast weight's input side)     */
@@ -104,8 +109,8 @@ typedef struct {
   ipttt_update update; /* linear or MSE rule                                     */
   ipttt_dtype in_dtype;/* dtype of x, e, w_gate, w_up, proj, conv_w              */
   uint32_t flags;      /* IPTTT_FLAG_*                                           */
-  int32_t group_chunks;/* chunks per group of the chunk-parallel linear scan, see
-                          below; 0 = library choice, 1 = plain chunk scan       */
+  int32_t group_chunks;/* chunks per group of the chunk-parallel scan (the
+                          note above); 0 = library choice, 1 = chunk by chunk */
   const void *w_gate;  /* [d_ff][d]                                              */
   const void *w_up;    /* [d_ff][d]                                              */
   const void *proj;    /* [d][d]                                                 */
