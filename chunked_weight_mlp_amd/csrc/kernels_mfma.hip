@@ -23,15 +23,18 @@
 //   k_apply    O = Z_q S_q (+ P_q (eta V_q))  M = rows of a group of G
 //              chunks, N = d, K = d_ff (then the group's earlier tokens),
 //              batched over (sequence, group); A comes from Zt (then P^T)
-//              through LDS transpose reads. The MSE rule (G = 1) also writes
-//              Rt = eta (V - O)^T.
+//              through LDS transpose reads, B from the blocked copy S_q. The
+//              MSE rule also writes Rt = eta (V - O)^T of the group's rows.
+//   k_mse_fix  MSE rule, chunk jl of a group: O += P R over the group's
+//              earlier chunks' final residuals, then Rt of the chunk.
 //   k_gram     P^T = block-causal Z_q Z_q^T of each group (G > 1), both
 //              operands read transposed; only the tiles the apply reads.
 //   k_update   W^T tile (BM d_ff rows x BN d columns, fp32) held in the
 //              accumulators across the chunks of a slab, one K loop over all
 //              of them: per group of G chunks, optionally the bf16 snapshot
-//              S_q (streamed out over the group's K steps), then Zt . Vt
-//              over the group's tokens.
+//              S_q (streamed out over the group's K steps, blocked layout),
+//              then Zt . Vt over the group's tokens.
+//   k_snapshot_blk  bf16 blocked copy of W (the MSE rule's first group).
 //   k_conv     depthwise conv of E, vector loads, sliding window.
 
 #include <algorithm>
@@ -328,7 +331,7 @@ __global__ __launch_bounds__(256) void k_snapshot_blk(Slab s, const float *__res
 // O rows of chunk groups [q0, q0 + nq) of every sequence (G = 1: one chunk per
 // group): O = Z S_q over the group's rows (S_q stored output-major, d rows of
 // d_ff), plus, when pt is given, the updates of the group's earlier chunks as
-// P (eta V), P^T read from the Gram buffer. The MSE rule (G = 1) also writes
+// P (eta V), P^T read from the Gram buffer. The MSE rule (pt null) also writes
 // Rt = eta (V - O)^T.
 // BLK: the snapshots are in the blocked layout of snap_offset (the forward's),
 // else row-major [d][F] (the backward's).
