@@ -166,10 +166,16 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int p = m0 + wm * C::WTM + C::FM * (i + h) + M::rrow(lane, 0);
-        const int jc = p / s.Bp, ic = p - jc * s.Bp;
-        const int64_t t0 = s.tok0 + (int64_t)jc * s.B + ic;
+        if (s.B == s.Bp) {  // no padding rows: slab row p is token tok0 + p
+          const int64_t t0 = s.tok0 + p;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) real[h][r] = jc < s.nc && ic + r < s.B && t0 + r < s.L;
+          for (int r = 0; r < 4; ++r) real[h][r] = p < P && t0 + r < s.L;
+        } else {
+          const int jc = p / s.Bp, ic = p - jc * s.Bp;
+          const int64_t t0 = s.tok0 + (int64_t)jc * s.B + ic;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) real[h][r] = jc < s.nc && ic + r < s.B && t0 + r < s.L;
+        }
       }
       const int pl = m0 + wm * C::WTM + C::FM * i + 8 * (gq >> 1) + C::FM * (gq & 1);
 #pragma unroll

@@ -856,6 +856,10 @@ __device__ __forceinline__ void kloop_dma_pl(__bf16 *smem, const DmaLoader<C, C:
 
 // Token of slab row p (slab rows fit in 32 bits), or -1 for a padding row.
 __device__ __forceinline__ int64_t slab_row_token(const Slab &s, int p) {
+  if (s.B == s.Bp) {  // no padding rows: no divide
+    const int64_t t = s.tok0 + p;
+    return p < s.nc * s.Bp && t < s.L ? t : -1;
+  }
   const int j = p / s.Bp, i = p - j * s.Bp;
   if (i >= s.B || j >= s.nc) return -1;
   const int64_t t = s.tok0 + (int64_t)j * s.B + i;
