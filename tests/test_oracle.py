@@ -600,3 +600,59 @@ def test_empty_sequence():
     O, Wf = run(oracle, c, 0.1, 4)
     assert O.shape == (1, 0, 6)
     np.testing.assert_array_equal(Wf[0], c["W_0"])
+
+
+# ----------------------------------------------------------------------------
+# worked example (tests/golden): numbers stored by a script that calls only the
+# oracle, checked here against the scalar loops above and per-step formulas
+# ----------------------------------------------------------------------------
+
+def _worked_example():
+    import json
+    import pathlib
+    path = pathlib.Path(__file__).parent / "golden" / "worked_example_d2_F3.json"
+    return json.loads(path.read_text(encoding="utf-8"))
+
+
+@pytest.mark.parametrize("update", ["linear", "mse"])
+def test_worked_example_scalar(update):
+    """Every stored chunk of the worked example against scalar arithmetic:
+    Z from the gated-MLP formula, V from the forward conv with its zero pad
+    and Proj, O and the fast weight after each chunk from the scalar scan
+    (brute) run on the prefix that ends with that chunk."""
+    g = _worked_example()
+    inp, eta, B = g["inputs"], g["eta"], g["chunk"]
+    X, E, W_g, W_u = inp["X"], inp["E"], inp["W_g"], inp["W_u"]
+    conv_w, Proj = inp["conv_w"], inp["Proj"]
+    d, F, Kc = len(X[0]), len(W_g[0]), len(conv_w[0])
+    chunks = g[update]["chunks"]
+    assert [c["tokens"] for c in chunks] == [[0, 2], [2, 4], [4, 5]]
+    for c in chunks:
+        s, e = c["tokens"]
+        for t in range(s, e):
+            for f in range(F):
+                a = sum(X[t][i] * W_g[i][f] for i in range(d))
+                u = sum(X[t][i] * W_u[i][f] for i in range(d))
+                assert c["Z"][t - s][f] == pytest.approx(a * u / (1.0 + math.exp(-a)), rel=1e-14,
+                                                         abs=1e-15)
+            conv = [sum(conv_w[ch][j] * E[t + j][ch] for j in range(Kc) if t + j < e)
+                    for ch in range(d)]
+            for o in range(d):
+                v = sum(conv[i] * Proj[i][o] for i in range(d))
+                assert c["V"][t - s][o] == pytest.approx(v, rel=1e-14, abs=1e-15)
+        Ob, Wb = brute(X[:e], E[:e], W_g, W_u, conv_w, Proj, inp["W_0"], eta, B, update)
+        np.testing.assert_allclose(np.array(c["O"]), np.array(Ob[s:e]), rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(np.array(c["W_after"]), np.array(Wb), rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("update", ["linear", "mse"])
+def test_worked_example_oracle(update):
+    """The oracle still reproduces the stored worked example."""
+    g = _worked_example()
+    a = {k: np.array(v, dtype=np.float64) for k, v in g["inputs"].items()}
+    O, Wf = oracle.prefill(a["X"][None], a["E"][None], a["W_g"], a["W_u"], a["conv_w"],
+                           a["Proj"], a["W_0"][None], g["eta"], g["chunk"], update=update)
+    chunks = g[update]["chunks"]
+    np.testing.assert_allclose(O[0], np.concatenate([np.array(c["O"]) for c in chunks]),
+                               rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(Wf[0], np.array(chunks[-1]["W_after"]), rtol=1e-13, atol=1e-15)
