@@ -13,7 +13,9 @@ benchmark runs. The chunk-size sweep streams the prefix-sum form instead
 evaluates.
 
 Also at full size: a run split into several passes over the sequence equals
-the one-pass run bit for bit.
+the one-pass run bit for bit. The longest case (256k tokens of the 4B-shaped
+layer) puts more than 2^31 elements in each sequence's Zt and its chunk copies
+of W, so every offset into them must be 64-bit.
 Bar: relative Frobenius error 2e-2 per chunk (bf16 inputs, fp32 accumulation).
 """
 from __future__ import annotations
@@ -76,7 +78,7 @@ def stream_scan(w, ow, x, e, o_cpu, label):
 
 
 @pytest.mark.parametrize("name", ["qwen3_4b_L128k_B1024", "qwen3_4b_L32k_B512",
-                                  "pretrain_1p5b_8x16k_B512_mse"])
+                                  "pretrain_1p5b_8x16k_B512_mse", "qwen3_4b_L256k_B1024"])
 def test_full_size(name):
     w = wl.WORKLOADS[name]
     say(f"[full] {name}: generating inputs")
