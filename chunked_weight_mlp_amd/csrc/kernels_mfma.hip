@@ -4,13 +4,15 @@
 // wave grid, the K step, the MFMA shape and the wave tile (Cfg): WM x WN
 // waves, each computing a 128 x WTN output tile from FM x FM MFMA tiles
 // (v_mfma_f32_32x32x16_bf16 or v_mfma_f32_16x16x32_bf16), so a block covers
-// (128 WM) x (WTN WN). K is staged through LDS BK at a time in two buffers,
-// the next step's copies in flight while a step runs on MFMA. gate/up, proj
-// and the update fill the buffers with direct global-to-LDS copies into
-// unpadded rows whose 16-byte pieces are XOR-swizzled (kslot); the update,
-// one wave per SIMD, also prefetches each MFMA sub-step's fragments into
-// registers behind the previous sub-step. The apply and the Gram stage
-// through registers into padded rows (PAD / PADT elements). A K-contiguous
+// (128 WM) x (WTN WN). K is staged through LDS BK at a time in two buffers
+// (three in the update), the next steps' copies in flight while a step runs
+// on MFMA. gate/up, proj and the update fill the buffers with direct
+// global-to-LDS copies into unpadded rows whose 16-byte pieces are
+// XOR-swizzled (kslot) and load each MFMA sub-step's fragments into registers
+// behind the previous sub-step's MFMAs. The apply, the Gram and the MSE
+// corrections stage through registers into padded rows (PAD / PADT
+// elements): their K-major operands are read with transposing LDS reads, which
+// the compiler makes wait for every direct copy in flight. A K-contiguous
 // operand gives each lane 8 consecutive K values with one 16-byte LDS read; a
 // K-major one is read with ds_read_b64_tr_b16. Shapes, paddings and staging
 // were picked by timing on MI355X.
