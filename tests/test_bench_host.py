@@ -1,6 +1,6 @@
 """Host-side pieces of bench.py (no GPU): the HBM traffic summary from two
 rocprofv3 counter runs, its staleness check against the kernel sources, and
-the kernel-trace table."""
+the kernel-trace table, the refusal of more than one GPU."""
 import csv
 import json
 import os
@@ -97,3 +97,14 @@ def test_trace_summary_names_and_order(tmp_path):
     assert lines[2] == "| `k_gateup` | 3 | 10.000 | 9.900 | 10.100 | 60.00 |"
     assert lines[3] == "| `k_update<Cfg<1, 2> >` | 3 | 8.000 | 7.900 | 8.100 | 39.90 |"
     assert lines[4].startswith("| `copyBuffer` | 3 | 0.040 |")
+
+
+def test_more_than_one_gpu_is_refused():
+    """The library runs on one GPU: --gpus above 1 prints a JSON error line and
+    exits with status 2 before touching a device."""
+    import subprocess
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300, cwd=ROOT)
+    assert r.returncode == 2
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    assert line["n_gpus"] == 2 and "one GPU" in line["error"]
