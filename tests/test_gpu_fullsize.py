@@ -78,7 +78,8 @@ def stream_scan(w, ow, x, e, o_cpu, label):
 
 
 @pytest.mark.parametrize("name", ["qwen3_4b_L128k_B1024", "qwen3_4b_L32k_B512",
-                                  "pretrain_1p5b_8x16k_B512_mse", "qwen3_4b_L256k_B1024"])
+                                  "pretrain_1p5b_8x16k_B512_mse", "qwen3_4b_L256k_B1024",
+                                  "qwen3_4b_L32k_B512_mse"])
 def test_full_size(name):
     w = wl.WORKLOADS[name]
     say(f"[full] {name}: generating inputs")

@@ -74,6 +74,8 @@ WORKLOADS = {
         _w("pretrain_1p5b_8x16k_B512_mse", 8, 2048, 8192, 16384, 512, "bf16", 1e-4, "mse"),
         # the longest parity case: d_ff x L (Zt elements per sequence) exceeds 2^31
         _w("qwen3_4b_L256k_B1024", 1, 2560, 9728, 262144, 1024, "bf16", 1e-3, "linear"),
+        # parity case: the MSE rule on the 4B-shaped layer, one sequence
+        _w("qwen3_4b_L32k_B512_mse", 1, 2560, 9728, 32768, 512, "bf16", 1e-4, "mse"),
     ]
     + [
         _w(f"qwen3_4b_L64k_B{B}", 1, 2560, 9728, 65536, B, "bf16", 1e-3, "linear")
