@@ -160,59 +160,76 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
       const auto y = __builtin_amdgcn_permlane16_swap(ua.y, ub.y, false, false);
       return uint4{x[0], y[0], x[1], y[1]};
     };
+    // tiles wholly inside the slab, the sequence and d_ff, without the
+    // backward's pre-activations: no per-row masks and no store predicates (a
+    // predicated store would also wait for the next tile's copies in flight)
+    const bool full = !at && s.B == s.Bp && m0 + C::BM <= P && s.tok0 + m0 + C::BM <= s.L &&
+                      f0 + FT <= s.F;
+    const auto tile_out = [&](auto full_tag) __attribute__((always_inline)) {
+      constexpr bool FULL = decltype(full_tag)::value;
 #pragma unroll
-    for (int i = 0; i < C::MI; i += 2) {
-      // rows p .. p + 3 of each tile lie in one chunk (Bp is a multiple of 4);
-      // chunk-padding rows and tokens past the sequence end are exact zeros
-      bool real[2][4];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int p = m0 + wm * C::WTM + C::FM * (i + h) + M::rrow(lane, 0);
-        if (s.B == s.Bp) {  // no padding rows: slab row p is token tok0 + p
-          const int64_t t0 = s.tok0 + p;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) real[h][r] = p < P && t0 + r < s.L;
-        } else {
-          const int jc = p / s.Bp, ic = p - jc * s.Bp;
-          const int64_t t0 = s.tok0 + (int64_t)jc * s.B + ic;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) real[h][r] = jc < s.nc && ic + r < s.B && t0 + r < s.L;
-        }
-      }
-      const int pl = m0 + wm * C::WTM + C::FM * i + 8 * (gq >> 1) + C::FM * (gq & 1);
-#pragma unroll
-      for (int j = 0; j < HJ; ++j) {
-        const int f = f0 + wn * WF + C::FM * j + M::rcol(lane);
-        bf16x4 v[2];
+      for (int i = 0; i < C::MI; i += 2) {
+        // rows p .. p + 3 of each tile lie in one chunk (Bp is a multiple of 4);
+        // chunk-padding rows and tokens past the sequence end are exact zeros
+        bool real[2][4];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const f32x4 gv = get4(acc[i + h][j], 0), uv = get4(acc[i + h][j + HJ], 0);
+          if constexpr (FULL) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r)  // SiLU(a) = a sigmoid(a)
-            v[h][r] = (__bf16)(real[h][r] ? gv[r] * fast_sigmoid(gv[r]) * uv[r] : 0.f);
+            for (int r = 0; r < 4; ++r) real[h][r] = true;
+            continue;
+          }
+          const int p = m0 + wm * C::WTM + C::FM * (i + h) + M::rrow(lane, 0);
+          if (s.B == s.Bp) {  // no padding rows: slab row p is token tok0 + p
+            const int64_t t0 = s.tok0 + p;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) real[h][r] = p < P && t0 + r < s.L;
+          } else {
+            const int jc = p / s.Bp, ic = p - jc * s.Bp;
+            const int64_t t0 = s.tok0 + (int64_t)jc * s.B + ic;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) real[h][r] = jc < s.nc && ic + r < s.B && t0 + r < s.L;
+          }
         }
-        const uint4 z = swap8(v[0], v[1]);
-        if (pl < P && f < s.F) *(uint4 *)(zts + (int64_t)f * s.Lp + pl) = z;
-        if (at) {  // pre-activations, for the backward
-          bf16x4 va[2], vu[2];
+        const int pl = m0 + wm * C::WTM + C::FM * i + 8 * (gq >> 1) + C::FM * (gq & 1);
+#pragma unroll
+        for (int j = 0; j < HJ; ++j) {
+          const int f = f0 + wn * WF + C::FM * j + M::rcol(lane);
+          bf16x4 v[2];
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             const f32x4 gv = get4(acc[i + h][j], 0), uv = get4(acc[i + h][j + HJ], 0);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              va[h][r] = (__bf16)(real[h][r] ? gv[r] : 0.f);
-              vu[h][r] = (__bf16)(real[h][r] ? uv[r] : 0.f);
-            }
+            for (int r = 0; r < 4; ++r)  // SiLU(a) = a sigmoid(a)
+              v[h][r] = (__bf16)(real[h][r] ? gv[r] * fast_sigmoid(gv[r]) * uv[r] : 0.f);
           }
-          const uint4 za = swap8(va[0], va[1]), zu = swap8(vu[0], vu[1]);
-          const int64_t off = (int64_t)n_seq * s.F * s.Lp + (int64_t)f * s.Lp + pl;
-          if (pl < P && f < s.F) {
-            *(uint4 *)(at + off) = za;
-            *(uint4 *)(ut + off) = zu;
+          const uint4 z = swap8(v[0], v[1]);
+          if (FULL || (pl < P && f < s.F)) *(uint4 *)(zts + (int64_t)f * s.Lp + pl) = z;
+          if (!FULL && at) {  // pre-activations, for the backward
+            bf16x4 va[2], vu[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const f32x4 gv = get4(acc[i + h][j], 0), uv = get4(acc[i + h][j + HJ], 0);
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                va[h][r] = (__bf16)(real[h][r] ? gv[r] : 0.f);
+                vu[h][r] = (__bf16)(real[h][r] ? uv[r] : 0.f);
+              }
+            }
+            const uint4 za = swap8(va[0], va[1]), zu = swap8(vu[0], vu[1]);
+            const int64_t off = (int64_t)n_seq * s.F * s.Lp + (int64_t)f * s.Lp + pl;
+            if (pl < P && f < s.F) {
+              *(uint4 *)(at + off) = za;
+              *(uint4 *)(ut + off) = zu;
+            }
           }
         }
       }
-    }
+    };
+    if (full)
+      tile_out(std::true_type());
+    else
+      tile_out(std::false_type());
   };
 
   run_tiles<C, PERS>(smem, la, lb, per_seq * s.n_seq, s.d / C::BK, wave, lane, wm * C::WTM, brow,
