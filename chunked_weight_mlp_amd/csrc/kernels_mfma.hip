@@ -667,7 +667,10 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
 // the chunks last to first, snapshot S[j] before chunk j (the backward's
 // G_{j+1}). BLK: snapshots in the blocked layout snap_offset describes (the
 // forward's, read by the apply), else row-major [d][F] (the backward's).
-template <class C, bool BLK>
+// FULL: every tile lies inside the matrix (d_ff and d whole multiples of the
+// tile), so no store tests its bounds: a predicated store inside the K loop
+// also waits for every copy in flight.
+template <class C, bool BLK, bool FULL>
 __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC))) void k_update(
     Slab s, int j_first, int n_chunks, int G, const __bf16 *__restrict__ zt,
     const __bf16 *__restrict__ bsrc, int64_t b_ld, int64_t b_seq_stride, int64_t b_chunk_stride,
@@ -715,7 +718,7 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
         for (int g = 0; g < M::NG; ++g) {
           const int f = f0 + wm * C::WTM + C::FM * i + M::rrow(lane, g);
           const int c = c0 + wn * C::WTN + C::FM * jj + M::rcol(lane);
-          if (f < s.F && c < s.d) {
+          if (FULL || (f < s.F && c < s.d)) {
             const f32x4 a4 = get4(acc[i][jj], g);
             bf16x4 v;
 #pragma unroll
@@ -777,7 +780,7 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
     const int gq = lane >> 4;
     const int f = f0 + wm * C::WTM + C::FM * i + 8 * (gq >> 1) + C::FM * (gq & 1);
     const int c = cl + C::FM * jj;
-    if (f < s.F && c < s.d) *(uint4 *)(sdst + snap_offset<BLK>(s, c, f)) = v;
+    if (FULL || (f < s.F && c < s.d)) *(uint4 *)(sdst + snap_offset<BLK>(s, c, f)) = v;
   };
   static_assert(PPS % 2 == 0 && C::FM == 16, "slots store pairs of 16-row tiles");
   auto store_slot = [&](int slot) __attribute__((always_inline)) {
@@ -839,7 +842,7 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
       for (int g = 0; g < M::NG; ++g) {
         const int f = f0 + wm * C::WTM + C::FM * i + M::rrow(lane, g);
         const int c = c0 + wn * C::WTN + C::FM * jj + M::rcol(lane);
-        if (f < s.F && c < s.d) *(f32x4 *)(ws + (int64_t)c * s.F + f) = get4(acc[i][jj], g);
+        if (FULL || (f < s.F && c < s.d)) *(f32x4 *)(ws + (int64_t)c * s.F + f) = get4(acc[i][jj], g);
       }
 }
 
@@ -978,15 +981,27 @@ hipError_t launch_gram(const Slab &s, const WsPtrs &ws, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Launches k_update over nb tiles, in its FULL form when the tiles cover d_ff
+// and d exactly.
+template <class C, bool BLK, class... Args>
+hipError_t launch_k_update(const Slab &s, int64_t nb, hipStream_t st, Args... args) {
+  if (s.F % C::BM == 0 && s.d % C::BN == 0)
+    hipLaunchKernelGGL((k_update<C, BLK, true>), dim3((unsigned)nb), dim3(C::NTHR), 0, st, s,
+                       args...);
+  else
+    hipLaunchKernelGGL((k_update<C, BLK, false>), dim3((unsigned)nb), dim3(C::NTHR), 0, st, s,
+                       args...);
+  return hipGetLastError();
+}
+
 template <class C, bool BLK>
 hipError_t launch_update_scan(const Slab &s, const WsPtrs &ws, float *w_state, hipStream_t st) {
   const int64_t dF = (int64_t)s.d * s.F;
   const int64_t nb = ((s.F + C::BM - 1) / C::BM) * ((s.d + C::BN - 1) / C::BN) * s.n_seq;
   // B operand: Vt rows c; chunk jc starts jc * Bp tokens along the row
-  hipLaunchKernelGGL((k_update<C, BLK>), dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, 0, s.nc, s.G,
-                     (const __bf16 *)ws.zt, (const __bf16 *)ws.vt, s.Lp, (int64_t)s.d * s.Lp,
-                     (int64_t)s.Bp, w_state, (__bf16 *)ws.s, (int64_t)s.ng_cap * dF, dF, 1, 0, 0);
-  return hipGetLastError();
+  return launch_k_update<C, BLK>(s, nb, st, 0, s.nc, s.G, (const __bf16 *)ws.zt,
+                                 (const __bf16 *)ws.vt, s.Lp, (int64_t)s.d * s.Lp, (int64_t)s.Bp,
+                                 w_state, (__bf16 *)ws.s, (int64_t)s.ng_cap * dF, dF, 1, 0, 0);
 }
 
 // MSE rule over chunk groups: W += sum over the chunks of group q of
@@ -997,10 +1012,9 @@ hipError_t launch_update_group(const Slab &s, int q, const WsPtrs &ws, float *w_
   const int64_t dF = (int64_t)s.d * s.F, RG = (int64_t)s.G * s.Bp;
   const int j_first = q * s.G, n_chunks = std::min(s.G, s.nc - j_first);
   const int64_t nb = ((s.F + C::BM - 1) / C::BM) * ((s.d + C::BN - 1) / C::BN) * s.n_seq;
-  hipLaunchKernelGGL((k_update<C, true>), dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, j_first,
-                     n_chunks, 1, (const __bf16 *)ws.zt, (const __bf16 *)ws.rt, RG, s.d * RG,
-                     (int64_t)s.Bp, w_state, (__bf16 *)ws.s, dF, (int64_t)0, 0, 1, 0);
-  return hipGetLastError();
+  return launch_k_update<C, true>(s, nb, st, j_first, n_chunks, 1, (const __bf16 *)ws.zt,
+                                  (const __bf16 *)ws.rt, RG, s.d * RG, (int64_t)s.Bp, w_state,
+                                  (__bf16 *)ws.s, dF, (int64_t)0, 0, 1, 0);
 }
 
 // Backward scan: G (fp32, [n][d][F] like W) += Zt_j . Bt_j over the chunks in
@@ -1011,10 +1025,8 @@ hipError_t launch_update_reverse(const Slab &s, const __bf16 *zt, const __bf16 *
                                  __bf16 *snap, hipStream_t st) {
   const int64_t dF = (int64_t)s.d * s.F;
   const int64_t nb = ((s.F + C::BM - 1) / C::BM) * ((s.d + C::BN - 1) / C::BN) * s.n_seq;
-  hipLaunchKernelGGL((k_update<C, false>), dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, 0, s.nc, 1, zt, bt,
-                     s.Lp, (int64_t)s.d * s.Lp, (int64_t)s.Bp, g, snap, (int64_t)s.nc_cap * dF, dF,
-                     1, 0, 1);
-  return hipGetLastError();
+  return launch_k_update<C, false>(s, nb, st, 0, s.nc, 1, zt, bt, s.Lp, (int64_t)s.d * s.Lp,
+                                   (int64_t)s.Bp, g, snap, (int64_t)s.nc_cap * dF, dF, 1, 0, 1);
 }
 
 template <class C>
@@ -1023,11 +1035,9 @@ hipError_t launch_update_one(const Slab &s, int j, const WsPtrs &ws, float *w_st
   const int64_t dF = (int64_t)s.d * s.F;
   const int64_t nb = ((s.F + C::BM - 1) / C::BM) * ((s.d + C::BN - 1) / C::BN) * s.n_seq;
   // B operand: Rt [n][d][Bp] of chunk j
-  hipLaunchKernelGGL((k_update<C, true>), dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, j, 1, 1,
-                     (const __bf16 *)ws.zt, (const __bf16 *)ws.rt, (int64_t)s.Bp,
-                     (int64_t)s.d * s.Bp, (int64_t)0, w_state, (__bf16 *)ws.s, dF, (int64_t)0, 0,
-                     1, 0);
-  return hipGetLastError();
+  return launch_k_update<C, true>(s, nb, st, j, 1, 1, (const __bf16 *)ws.zt,
+                                  (const __bf16 *)ws.rt, (int64_t)s.Bp, (int64_t)s.d * s.Bp,
+                                  (int64_t)0, w_state, (__bf16 *)ws.s, dF, (int64_t)0, 0, 1, 0);
 }
 
 template <int KC>
@@ -1141,10 +1151,9 @@ hipError_t mf_update_chunk(const Slab &s, int j, const __bf16 *zt, const __bf16 
                            int64_t snap_seq, hipStream_t st) {
   using C = mfma::UpdateCfg;
   const int64_t nb = ((s.F + C::BM - 1) / C::BM) * ((s.d + C::BN - 1) / C::BN) * s.n_seq;
-  hipLaunchKernelGGL((mfma::k_update<C, false>), dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, j, 1, 1, zt,
-                     bsrc, b_ld, b_seq, (int64_t)0, w, snap_after, snap_seq, (int64_t)0, 0,
-                     snap_after ? 1 : 0, 0);
-  return hipGetLastError();
+  return mfma::launch_k_update<C, false>(s, nb, st, j, 1, 1, zt, bsrc, b_ld, b_seq, (int64_t)0, w,
+                                         snap_after, snap_seq, (int64_t)0, 0, snap_after ? 1 : 0,
+                                         0);
 }
 hipError_t mf_snapshot(const Slab &s, const float *w_state, __bf16 *snap, int64_t snap_seq_stride,
                        hipStream_t st) {
