@@ -274,22 +274,38 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
     int n_seq, m0, n0;
     tile(id, n_seq, m0, n0);
     __bf16 *vts = vt + (int64_t)n_seq * s.d * s.Lp;
+    // Row tiles i and i + 1 together, their halves swapped between lane groups
+    // (as gate/up's Zt): each lane stores 8 consecutive tokens of its column n.
+    static_assert(M::NG == 1 && C::MI % 2 == 0, "pairs of 16-row tiles");
+    const int gq = lane >> 4;
+    const bool full = m0 + C::BM <= P && n0 + C::BN <= s.d;
+    const auto tile_out = [&](auto full_tag) __attribute__((always_inline)) {
+      constexpr bool FULL = decltype(full_tag)::value;
 #pragma unroll
-    for (int i = 0; i < C::MI; ++i)
+      for (int i = 0; i < C::MI; i += 2) {
+        const int pl = m0 + wm * C::WTM + C::FM * i + 8 * (gq >> 1) + C::FM * (gq & 1);
 #pragma unroll
-      for (int j = 0; j < C::NJ; ++j)
-#pragma unroll
-        for (int g = 0; g < M::NG; ++g) {
-          const int p = m0 + wm * C::WTM + C::FM * i + M::rrow(lane, g);
+        for (int j = 0; j < C::NJ; ++j) {
           const int n = n0 + wn * C::WTN + C::FM * j + M::rcol(lane);
-          if (p < P && n < s.d) {
-            const f32x4 a4 = get4(acc[i][j], g);
-            bf16x4 v;
+          bf16x4 v[2];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) v[r] = (__bf16)(scale * a4[r]);
-            *(bf16x4 *)(vts + (int64_t)n * s.Lp + p) = v;
+          for (int h = 0; h < 2; ++h) {
+            const f32x4 a4 = get4(acc[i + h][j], 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[h][r] = (__bf16)(scale * a4[r]);
           }
+          const uint2 ua = __builtin_bit_cast(uint2, v[0]), ub = __builtin_bit_cast(uint2, v[1]);
+          const auto x = __builtin_amdgcn_permlane16_swap(ua.x, ub.x, false, false);
+          const auto y = __builtin_amdgcn_permlane16_swap(ua.y, ub.y, false, false);
+          const uint4 z{x[0], y[0], x[1], y[1]};
+          if (FULL || (pl < P && n < s.d)) *(uint4 *)(vts + (int64_t)n * s.Lp + pl) = z;
         }
+      }
+    };
+    if (full)
+      tile_out(std::true_type());
+    else
+      tile_out(std::false_type());
   };
   run_tiles<C, PERS>(smem, la, lb, per_seq * s.n_seq, s.d / C::BK, wave, lane, wm * C::WTM, brow,
                      acc, init, epilogue);
