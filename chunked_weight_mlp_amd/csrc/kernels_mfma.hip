@@ -278,6 +278,8 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
     // (as gate/up's Zt): each lane stores 8 consecutive tokens of its column n.
     static_assert(M::NG == 1 && C::MI % 2 == 0, "pairs of 16-row tiles");
     const int gq = lane >> 4;
+    // tiles wholly inside the slab and d store without predicates (a
+    // predicated store would also wait for the next tile's copies in flight)
     const bool full = m0 + C::BM <= P && n0 + C::BN <= s.d;
     const auto tile_out = [&](auto full_tag) __attribute__((always_inline)) {
       constexpr bool FULL = decltype(full_tag)::value;
