@@ -563,45 +563,91 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
   }
 
   float *os = o + n_seq * s.x_seq_stride;
+  if constexpr (C::WM * C::WN < 8) {  // one wave per SIMD: registers for the whole tile
+    // every load of the tile (O and V, clamped in bounds, unconditional) before
+    // any store, so one wait covers them all; rows and columns out of range are
+    // never stored
+    static_assert(M::NG == 1, "one 4-row group per accumulator tile");
+    f32x4 ob[C::MI][C::NJ];
+    bf16x4 vb[C::MI][C::NJ];
 #pragma unroll
-  for (int i = 0; i < C::MI; ++i)
+    for (int i = 0; i < C::MI; ++i) {
+      const int m = min(m0 + wm * C::WTM + C::FM * i + M::rrow(lane, 0), mend - 4);
+      const int64_t t0 = s.tok0 + (int64_t)(j_first + jl) * s.B + (m - cs);
 #pragma unroll
-    for (int g = 0; g < M::NG; ++g) {
+      for (int jj = 0; jj < C::NJ; ++jj) {
+        const int n = min(n0 + wn * C::WTN + C::FM * jj + M::rcol(lane), s.d - 1);
+        vb[i][jj] = *(const bf16x4 *)(vts + (int64_t)n * s.Lp + row0 + m);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ob[i][jj][r] = os[min(t0 + r, s.L - 1) * s.d + n];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < C::MI; ++i) {
       // rows m .. m + 3 share one chunk (Bp is a multiple of 4)
-      const int m = m0 + wm * C::WTM + C::FM * i + M::rrow(lane, g);
+      const int m = m0 + wm * C::WTM + C::FM * i + M::rrow(lane, 0);
       if (m >= mend) continue;
       const int ic = m - cs;
       const int64_t t0 = s.tok0 + (int64_t)(j_first + jl) * s.B + ic;
       bool valid[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) valid[r] = ic + r < s.B && t0 + r < s.L;
-      // every load of the row tile before its stores, so one wait covers them
-      f32x4 ob[C::NJ];
-      bf16x4 vb[C::NJ];
-#pragma unroll
-      for (int jj = 0; jj < C::NJ; ++jj) {
-        // clamped in bounds and loaded unconditionally; rows and columns out of
-        // range are never stored
-        const int n = min(n0 + wn * C::WTN + C::FM * jj + M::rcol(lane), s.d - 1);
-        vb[jj] = *(const bf16x4 *)(vts + (int64_t)n * s.Lp + row0 + m);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ob[jj][r] = os[min(t0 + r, s.L - 1) * s.d + n];
-      }
 #pragma unroll
       for (int jj = 0; jj < C::NJ; ++jj) {
         const int n = n0 + wn * C::WTN + C::FM * jj + M::rcol(lane);
         if (n >= s.d) continue;
-        const f32x4 a4 = get4(acc[i][jj], g);
+        const f32x4 a4 = get4(acc[i][jj], 0);
         bf16x4 rv;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float ov = ob[jj][r] + a4[r];
+          const float ov = ob[i][jj][r] + a4[r];
           if (valid[r]) os[(t0 + r) * s.d + n] = ov;
-          rv[r] = (__bf16)(valid[r] ? s.eta * ((float)vb[jj][r] - ov) : 0.f);
+          rv[r] = (__bf16)(valid[r] ? s.eta * ((float)vb[i][jj][r] - ov) : 0.f);
         }
         *(bf16x4 *)(rts + (int64_t)n * RG + m) = rv;
       }
     }
+  } else {  // two waves per SIMD: a row tile at a time
+#pragma unroll
+    for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+      for (int g = 0; g < M::NG; ++g) {
+        // rows m .. m + 3 share one chunk (Bp is a multiple of 4)
+        const int m = m0 + wm * C::WTM + C::FM * i + M::rrow(lane, g);
+        if (m >= mend) continue;
+        const int ic = m - cs;
+        const int64_t t0 = s.tok0 + (int64_t)(j_first + jl) * s.B + ic;
+        bool valid[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) valid[r] = ic + r < s.B && t0 + r < s.L;
+        // every load of the row tile before its stores, so one wait covers them
+        f32x4 ob[C::NJ];
+        bf16x4 vb[C::NJ];
+#pragma unroll
+        for (int jj = 0; jj < C::NJ; ++jj) {
+          // clamped in bounds and loaded unconditionally; rows and columns out of
+          // range are never stored
+          const int n = min(n0 + wn * C::WTN + C::FM * jj + M::rcol(lane), s.d - 1);
+          vb[jj] = *(const bf16x4 *)(vts + (int64_t)n * s.Lp + row0 + m);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ob[jj][r] = os[min(t0 + r, s.L - 1) * s.d + n];
+        }
+#pragma unroll
+        for (int jj = 0; jj < C::NJ; ++jj) {
+          const int n = n0 + wn * C::WTN + C::FM * jj + M::rcol(lane);
+          if (n >= s.d) continue;
+          const f32x4 a4 = get4(acc[i][jj], g);
+          bf16x4 rv;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float ov = ob[jj][r] + a4[r];
+            if (valid[r]) os[(t0 + r) * s.d + n] = ov;
+            rv[r] = (__bf16)(valid[r] ? s.eta * ((float)vb[jj][r] - ov) : 0.f);
+          }
+          *(bf16x4 *)(rts + (int64_t)n * RG + m) = rv;
+        }
+      }
+  }
 }
 
 // ---------------------------------------------------------------------------
