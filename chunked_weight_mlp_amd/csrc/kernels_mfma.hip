@@ -469,6 +469,22 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
   }
 
   float *os = o ? o + n_seq * s.x_seq_stride : nullptr;  // nullptr: residual only
+  // the residual's V for the whole tile before any store (clamped in bounds,
+  // loaded unconditionally), so one wait covers every load
+  bf16x4 vb[C::MI][M::NG][C::NJ];
+  if (rt) {
+#pragma unroll
+    for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+      for (int g = 0; g < M::NG; ++g) {
+        const int m = min(m0 + wm * C::WTM + C::FM * i + M::rrow(lane, g), R - 4);
+#pragma unroll
+        for (int jj = 0; jj < C::NJ; ++jj) {
+          const int n = min(n0 + wn * C::WTN + C::FM * jj + M::rcol(lane), s.d - 1);
+          vb[i][g][jj] = *(const bf16x4 *)(vts + (int64_t)n * s.Lp + row0 + m);
+        }
+      }
+  }
 #pragma unroll
   for (int i = 0; i < C::MI; ++i)
 #pragma unroll
@@ -490,7 +506,7 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
         for (int r = 0; r < 4; ++r)
           if (os && valid[r]) os[(t0 + r) * s.d + n] = a4[r];
         if (rt) {
-          const bf16x4 v = *(const bf16x4 *)(vts + (int64_t)n * s.Lp + row0 + m);
+          const bf16x4 v = vb[i][g][jj];
           bf16x4 rv;
 #pragma unroll
           for (int r = 0; r < 4; ++r) rv[r] = (__bf16)(valid[r] ? s.eta * ((float)v[r] - a4[r]) : 0.f);
