@@ -16,6 +16,7 @@
 // segments (one per sequence) for the weight gradients. The epilogue is a
 // functor that receives four consecutive output rows of one column.
 #include <algorithm>
+#include <type_traits>
 
 #include "mfma_common.h"
 
@@ -42,6 +43,15 @@ struct GProb {
   int nph;        // 1 or 2 phases
   GPhase ph[2];
 };
+
+// Epilogues that read memory (In, load, store) get their loads issued for
+// part of a tile at a time before any of that part's stores: a store with a lane
+// predicate makes every later load wait for it, so loads interleaved with
+// stores would cost one memory round trip per output group.
+template <class E, class = void>
+struct EpiLoads : std::false_type {};
+template <class E>
+struct EpiLoads<E, std::void_t<typename E::In>> : std::true_type {};
 
 template <class C, bool TA, bool TB, class Epi>
 __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC))) void k_gemm(
@@ -116,16 +126,48 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
         kloop_g<C, TA, TB>(smem, la, lb, g.ph[ph].K / C::BK, tid, wm * C::WTM, brow, acc);
     }
   }
+  if constexpr (EpiLoads<Epi>::value) {
+    // row tiles loaded together: half the wave tile at one wave per SIMD, a
+    // quarter at two (whose 256 registers hold less beside the accumulators)
+    constexpr int H = C::WM * C::WN >= 8 ? C::MI / 4 : C::MI / 2;
+    static_assert(C::MI % 4 == 0, "quarters of the wave tile");
 #pragma unroll
-  for (int i = 0; i < C::MI; ++i)
+    for (int h0 = 0; h0 < C::MI; h0 += H) {
+      typename Epi::In in[H][C::NJ][M::NG];
 #pragma unroll
-    for (int jj = 0; jj < C::NJ; ++jj)
+      for (int i = 0; i < H; ++i)
 #pragma unroll
-      for (int q = 0; q < M::NG; ++q) {
-        const int m = m0 + wm * C::WTM + C::FM * i + M::rrow(lane, q);
-        const int n = n0 + wn * C::WTN + C::FM * jj + M::rcol(lane);
-        if (m < g.M && n < g.N) epi(b1, b2, m, n, get4(acc[i][jj], q));
-      }
+        for (int jj = 0; jj < C::NJ; ++jj)
+#pragma unroll
+          for (int q = 0; q < M::NG; ++q) {
+            // clamped in bounds and loaded unconditionally (M is a multiple of 4)
+            const int m = min(m0 + wm * C::WTM + C::FM * (h0 + i) + M::rrow(lane, q), g.M - 4);
+            const int n = min(n0 + wn * C::WTN + C::FM * jj + M::rcol(lane), g.N - 1);
+            in[i][jj][q] = epi.load(b1, b2, m, n);
+          }
+#pragma unroll
+      for (int i = 0; i < H; ++i)
+#pragma unroll
+        for (int jj = 0; jj < C::NJ; ++jj)
+#pragma unroll
+          for (int q = 0; q < M::NG; ++q) {
+            const int m = m0 + wm * C::WTM + C::FM * (h0 + i) + M::rrow(lane, q);
+            const int n = n0 + wn * C::WTN + C::FM * jj + M::rcol(lane);
+            if (m < g.M && n < g.N) epi.store(b1, b2, m, n, get4(acc[h0 + i][jj], q), in[i][jj][q]);
+          }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+      for (int jj = 0; jj < C::NJ; ++jj)
+#pragma unroll
+        for (int q = 0; q < M::NG; ++q) {
+          const int m = m0 + wm * C::WTM + C::FM * i + M::rrow(lane, q);
+          const int n = n0 + wn * C::WTN + C::FM * jj + M::rcol(lane);
+          if (m < g.M && n < g.N) epi(b1, b2, m, n, get4(acc[i][jj], q));
+        }
+  }
 }
 
 // ---- epilogues (m .. m + 3 are consecutive output rows, n one column) -------
@@ -137,13 +179,22 @@ struct EpiDZ {
   __bf16 *dat, *dut;
   int64_t seq_stride, Lp;
   int Bp;
-  __device__ void operator()(int b1, int b2, int m, int n, f32x4 v) const {
-    const int64_t off = b1 * seq_stride + n * Lp + (int64_t)b2 * Bp + m;
-    const bf16x4 a = *(const bf16x4 *)(at + off), u = *(const bf16x4 *)(ut + off);
+  struct In {
+    bf16x4 a, u;
+  };
+  __device__ int64_t offset(int b1, int b2, int m, int n) const {
+    return b1 * seq_stride + n * Lp + (int64_t)b2 * Bp + m;
+  }
+  __device__ In load(int b1, int b2, int m, int n) const {
+    const int64_t off = offset(b1, b2, m, n);
+    return {*(const bf16x4 *)(at + off), *(const bf16x4 *)(ut + off)};
+  }
+  __device__ void store(int b1, int b2, int m, int n, f32x4 v, In in) const {
+    const int64_t off = offset(b1, b2, m, n);
     bf16x4 da, du;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float A = (float)a[r], U = (float)u[r];
+      const float A = (float)in.a[r], U = (float)in.u[r];
       const float sg = fast_sigmoid(A);
       da[r] = (__bf16)(v[r] * U * sg * (1.f + A * (1.f - sg)));
       du[r] = (__bf16)(v[r] * A * sg);
@@ -185,13 +236,18 @@ struct EpiMseP {
   __bf16 *dyt, *dvt;
   int64_t seq_stride, Lp, col0;
   float eta;
-  __device__ void operator()(int b1, int, int m, int n, f32x4 v) const {
+  struct In {
+    bf16x4 o;
+  };
+  __device__ In load(int b1, int, int m, int n) const {
+    return {*(const bf16x4 *)(dot + b1 * seq_stride + n * Lp + col0 + m)};
+  }
+  __device__ void store(int b1, int, int m, int n, f32x4 v, In in) const {
     const int64_t off = b1 * seq_stride + n * Lp + col0 + m;
-    const bf16x4 o = *(const bf16x4 *)(dot + off);
     bf16x4 dy, dv;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      dy[r] = (__bf16)((float)o[r] - eta * v[r]);
+      dy[r] = (__bf16)((float)in.o[r] - eta * v[r]);
       dv[r] = (__bf16)(eta * v[r]);
     }
     *(bf16x4 *)(dyt + off) = dy;
