@@ -90,7 +90,8 @@ __device__ __forceinline__ void run_tiles(__bf16 *smem, DmaLoader<C, C::BM> &la,
 // ---------------------------------------------------------------------------
 // PERS: persistent blocks (one per CU), each running a range of its XCD's
 // tiles back to back through kloop_dma_pl_tiles; otherwise one tile per block.
-template <class C, bool PERS>
+// PRE: also write the pre-activations (at, ut) for the backward.
+template <class C, bool PERS, bool PRE>
 __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC))) void k_gateup(
     Slab s, const __bf16 *__restrict__ x, const __bf16 *__restrict__ wg,
     const __bf16 *__restrict__ wu, __bf16 *__restrict__ zt, __bf16 *__restrict__ at,
@@ -160,10 +161,10 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
       const auto y = __builtin_amdgcn_permlane16_swap(ua.y, ub.y, false, false);
       return uint4{x[0], y[0], x[1], y[1]};
     };
-    // tiles wholly inside the slab, the sequence and d_ff, without the
-    // backward's pre-activations: no per-row masks and no store predicates (a
-    // predicated store would also wait for the next tile's copies in flight)
-    const bool full = !at && s.B == s.Bp && m0 + C::BM <= P && s.tok0 + m0 + C::BM <= s.L &&
+    // tiles wholly inside the slab, the sequence and d_ff: no per-row masks and
+    // no store predicates (a predicated store would also wait for the next
+    // tile's copies in flight)
+    const bool full = s.B == s.Bp && m0 + C::BM <= P && s.tok0 + m0 + C::BM <= s.L &&
                       f0 + FT <= s.F;
     const auto tile_out = [&](auto full_tag) __attribute__((always_inline)) {
       constexpr bool FULL = decltype(full_tag)::value;
@@ -205,7 +206,7 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
           }
           const uint4 z = swap8(v[0], v[1]);
           if (FULL || (pl < P && f < s.F)) *(uint4 *)(zts + (int64_t)f * s.Lp + pl) = z;
-          if (!FULL && at) {  // pre-activations, for the backward
+          if constexpr (PRE) {  // pre-activations, for the backward
             bf16x4 va[2], vu[2];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
@@ -218,7 +219,7 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
             }
             const uint4 za = swap8(va[0], va[1]), zu = swap8(vu[0], vu[1]);
             const int64_t off = (int64_t)n_seq * s.F * s.Lp + (int64_t)f * s.Lp + pl;
-            if (pl < P && f < s.F) {
+            if (FULL || (pl < P && f < s.F)) {
               *(uint4 *)(at + off) = za;
               *(uint4 *)(ut + off) = zu;
             }
@@ -1004,8 +1005,12 @@ hipError_t launch_gateup(const Slab &s, const __bf16 *x, const Weights &w, const
   const int64_t ntiles =
       ((P + C::BM - 1) / C::BM) * ((s.F + C::BN / 2 - 1) / (C::BN / 2)) * s.n_seq;
   const int64_t nb = PERS ? std::min<int64_t>(ntiles, device_cus()) : ntiles;
-  hipLaunchKernelGGL((k_gateup<C, PERS>), dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, x,
-                     (const __bf16 *)w.w_gate, (const __bf16 *)w.w_up, (__bf16 *)ws.zt, at, ut);
+  if (at)
+    hipLaunchKernelGGL((k_gateup<C, PERS, true>), dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, x,
+                       (const __bf16 *)w.w_gate, (const __bf16 *)w.w_up, (__bf16 *)ws.zt, at, ut);
+  else
+    hipLaunchKernelGGL((k_gateup<C, PERS, false>), dim3((unsigned)nb), dim3(C::NTHR), 0, st, s, x,
+                       (const __bf16 *)w.w_gate, (const __bf16 *)w.w_up, (__bf16 *)ws.zt, at, ut);
   return hipGetLastError();
 }
 
