@@ -1139,7 +1139,7 @@ static_assert(kChunkAlign % CONV_RUN == 0, "conv runs must not cross a chunk");
 // timing on MI355X at the 4B layer shape (d 2560, d_ff 9728, 16 chunks of
 // 1024), alternating candidates within one run.
 using GateUpCfg = Cfg<2, 4, 64, 16, 0, 8, 1, 4>;   // direct LDS copies, swizzled rows
-using ProjCfg = Cfg<2, 4, 64, 16, 0, 8, 1, 4>;     // direct LDS copies, swizzled rows
+using ProjCfg = Cfg<2, 4, 64, 16, 0, 8, 1, 8>;     // direct LDS copies, swizzled rows
 // K-major (transposed) rows are padded by 16 elements: the four K rows one
 // 16-lane transposing read touches then start 8 banks apart and never share a
 // bank (a pad of 8 leaves every such read 2-way conflicted).
