@@ -1142,7 +1142,8 @@ using GateUpCfg = Cfg<2, 4, 64, 16, 0, 8, 1, 4>;   // direct LDS copies, swizzle
 using ProjCfg = Cfg<2, 4, 64, 16, 0, 8, 1, 8>;     // direct LDS copies, swizzled rows
 // K-major (transposed) rows are padded by 16 elements: the four K rows one
 // 16-lane transposing read touches then start 8 banks apart and never share a
-// bank (a pad of 8 leaves every such read 2-way conflicted).
+// bank (a pad of 8 leaves every such read 2-way conflicted); trow_off moves the
+// rows the other 16 lanes of the same 32 read onto the other half of the banks.
 using ApplyCfg = Cfg<2, 4, 64, 16, 16, 16>;
 using ApplySmallCfg = Cfg<1, 2, 64, 16, 16, 16>;  // when ApplyCfg would leave most CUs idle
 using UpdateCfg = Cfg<1, 4, 64, 16, 0, 8, 1, 16>;  // direct copies, pipelined, interleaved fragments

@@ -97,14 +97,15 @@ struct Cfg {
   static constexpr int A_STAGE = BM * PITCH, B_STAGE = BN * PITCH;
   static constexpr int SMEM_ELEMS = 2 * (A_STAGE + B_STAGE);
   // A held K-major in LDS ([BK rows of K][BM columns of M]) for an A operand
-  // stored M-contiguous in memory.
+  // stored M-contiguous in memory; a stage also holds the 64-element shift of
+  // each run of 8 K rows (trow_off).
   static constexpr int PITCH_T = BM + PADT_;
   static constexpr int AT_PIECES = BK * (BM / 8) / NTHR;
-  static constexpr int AT_STAGE = BK * PITCH_T;
+  static constexpr int AT_STAGE = BK * PITCH_T + 64 * (BK / 8);
   static constexpr int SMEM_T_ELEMS = 2 * (AT_STAGE + B_STAGE);
   // both operands K-major ([BK rows of K][BM or BN columns])
   static constexpr int PITCH_TB = BN + PADT_;
-  static constexpr int BT_STAGE = BK * PITCH_TB;
+  static constexpr int BT_STAGE = BK * PITCH_TB + 64 * (BK / 8);
   static constexpr int SMEM_TT_ELEMS = 2 * (AT_STAGE + BT_STAGE);
   static_assert(BK % 32 == 0 && BM % RPP == 0 && BN % RPP == 0, "bad tile config");
   static_assert(PAD_ % 8 == 0 && PADT_ % 4 == 0, "LDS rows must keep 16 / 8-byte alignment");
@@ -240,6 +241,19 @@ __device__ __forceinline__ void mma_stage(const __bf16 *As, const __bf16 *Bs, in
 }
 
 // ---- A operand stored M-contiguous (K-major rows) ---------------------------
+// Start of K row r in a K-major LDS tile of COLS columns. The hardware serves
+// a transposing read 32 lanes (256 bytes, all 64 banks) at a time, and the
+// second 16-lane group of each 32 reads the K rows 8 below the first group's
+// (the next 8 K values of its MFMA operand). At the padded pitch alone those
+// rows start on the same banks (8 rows of 8 banks each: 64); shifting every
+// run of 8 K rows by a further 64 elements (128 bytes, half the banks) puts
+// the two groups on disjoint halves. Tiles narrower than 128 columns keep
+// plain rows.
+template <int COLS>
+__device__ __forceinline__ int trow_off(int r, int pitch) {
+  if constexpr (COLS >= 128) return r * pitch + 64 * (r >> 3); else return r * pitch;
+}
+
 // The tile is copied into LDS as BK rows of BM elements; each MFMA A fragment
 // (8 consecutive K values of one M row per lane) is assembled from two
 // ds_read_b64_tr_b16. That instruction works on groups of 16 lanes: lane i of
@@ -266,7 +280,8 @@ struct LoaderT {
   }
   __device__ __forceinline__ void stash(__bf16 *stage, int tid) const {
 #pragma unroll
-    for (int i = 0; i < NP; ++i) *(uint4 *)(stage + krow(tid, i) * PITCH + col(tid, i)) = v[i];
+    for (int i = 0; i < NP; ++i)
+      *(uint4 *)(stage + trow_off<COLS>(krow(tid, i), PITCH) + col(tid, i)) = v[i];
   }
 };
 
@@ -276,10 +291,12 @@ __device__ __forceinline__ v4i16 ds_read_tr16(const __bf16 *p) {
 
 // One MFMA operand fragment (8 K values of one row) from a K-major LDS tile
 // of row pitch `pitch`, via two transposing reads.
-template <class M>
+template <class M, int COLS>
 __device__ __forceinline__ bf16x8 frag_t(const __bf16 *tile, int pitch, int u, int col0, int trr,
                                          int trc) {
-  const __bf16 *base = tile + (M::K * u + trr) * pitch + col0 + trc;
+  // K u is a multiple of 8, so the row offset splits into a constant and the lane's part
+  const __bf16 *base =
+      tile + trow_off<COLS>(M::K * u, pitch) + trow_off<COLS>(trr, pitch) + col0 + trc;
   const v4i16 lo = ds_read_tr16(base), hi = ds_read_tr16(base + 4 * pitch);
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
@@ -297,12 +314,12 @@ __device__ __forceinline__ void mma_stage_t(const __bf16 *At, const __bf16 *Bs, 
     bf16x8 a[C::MI], b[C::NJ];
 #pragma unroll
     for (int j = 0; j < C::NJ; ++j)
-      b[j] = TB ? frag_t<M>(Bs, C::PITCH_TB, u, brow[j], trr, trc)
+      b[j] = TB ? frag_t<M, C::BN>(Bs, C::PITCH_TB, u, brow[j], trr, trc)
                 : *(const bf16x8 *)(Bs + (brow[j] + r) * C::PITCH +
                                     kslot<C>(brow[j] + r, M::K * u + kq));
 #pragma unroll
     for (int i = 0; i < C::MI; ++i)
-      a[i] = frag_t<M>(At, C::PITCH_T, u, arow0 + C::FM * i, trr, trc);
+      a[i] = frag_t<M, C::BM>(At, C::PITCH_T, u, arow0 + C::FM * i, trr, trc);
 #pragma unroll
     for (int i = 0; i < C::MI; ++i)
 #pragma unroll
@@ -434,12 +451,12 @@ __device__ __forceinline__ void mma_stage_g(const __bf16 *As, const __bf16 *Bs, 
     bf16x8 a[C::MI], b[C::NJ];
 #pragma unroll
     for (int j = 0; j < C::NJ; ++j)
-      b[j] = TB ? frag_t<M>(Bs, C::PITCH_TB, u, brow[j], trr, trc)
+      b[j] = TB ? frag_t<M, C::BN>(Bs, C::PITCH_TB, u, brow[j], trr, trc)
                 : *(const bf16x8 *)(Bs + (brow[j] + r) * C::PITCH +
                                     kslot<C>(brow[j] + r, M::K * u + kq));
 #pragma unroll
     for (int i = 0; i < C::MI; ++i)
-      a[i] = TA ? frag_t<M>(As, C::PITCH_T, u, arow0 + C::FM * i, trr, trc)
+      a[i] = TA ? frag_t<M, C::BM>(As, C::PITCH_T, u, arow0 + C::FM * i, trr, trc)
                 : *(const bf16x8 *)(As + (arow0 + C::FM * i + r) * C::PITCH +
                                     kslot<C>(arow0 + C::FM * i + r, M::K * u + kq));
 #pragma unroll
