@@ -305,6 +305,7 @@ def cpu_baseline(w: wl.Workload, x, e, weights, n_chunks: int):
     return {
         "value": tokens / dt,
         "unit": "tokens/s",
+        "gflops": round(w.flops_per_token() * tokens / dt / 1e9, 2),  # float64, algorithmic
         "cores": threads,
         "kind": "oracle",
         "sample": f"the oracle's chunk scan (float64 numpy) over the first {tokens} tokens "
@@ -440,19 +441,21 @@ def main():
         print(f"[bench] warmup {i + 1}/{args.warmup} done", file=sys.stderr, flush=True)
 
     torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+    # one event between consecutive steps (recording adds no synchronisation):
+    # the total and each step's own time
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     ipttt.ipttt_profile_begin(layer.handle)
     wall0 = time.perf_counter()
-    ev0.record()
-    for _ in range(args.steps):
+    evs[0].record()
+    for i in range(args.steps):
         step()
-    ev1.record()
+        evs[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     prof = ipttt.ipttt_profile_end(layer.handle)
-    ms_total = ev0.elapsed_time(ev1)
+    ms_total = evs[0].elapsed_time(evs[-1])
     ms_step = ms_total / args.steps
+    step_ms = step_stats([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
     tokens = w.n_seq * w.seq_len
     value = tokens / (ms_step / 1e3)
     print(f"[bench] {args.steps} steps in {ms_total:.1f} ms (wall {wall * 1e3:.1f} ms)", file=sys.stderr,
@@ -487,6 +490,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "step_ms": step_ms,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -510,6 +514,14 @@ def main():
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
+
+
+def step_stats(ms: list[float]) -> dict:
+    """Median, minimum and maximum of the timed steps' own durations (ms)."""
+    v = sorted(ms)
+    n = len(v)
+    med = v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+    return {"median": round(med, 4), "min": round(v[0], 4), "max": round(v[-1], 4)}
 
 
 def cpu_baseline_backward(w: wl.Workload, x, e, weights, d_o, n_chunks: int):

@@ -108,3 +108,9 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     line = json.loads(r.stdout.strip().splitlines()[-1])
     assert line["n_gpus"] == 2 and "one GPU" in line["error"]
+
+
+def test_step_stats_median_min_max():
+    assert bench.step_stats([3.0, 1.0, 2.0]) == {"median": 2.0, "min": 1.0, "max": 3.0}
+    assert bench.step_stats([4.0, 1.0, 2.0, 3.0]) == {"median": 2.5, "min": 1.0, "max": 4.0}
+    assert bench.step_stats([5.0]) == {"median": 5.0, "min": 5.0, "max": 5.0}
