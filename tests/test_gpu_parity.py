@@ -191,6 +191,39 @@ def test_bf16_mse_chunk_groups(Bc, G, L, N):
     check_against_oracle(w, n_seq=N, seq_len=L, group_chunks=G)
 
 
+@pytest.mark.parametrize("N", [2, 3, 4])
+def test_mse_batch_entry_points_bitwise(N):
+    """MSE chunk groups over several sequences: every sequence's output and
+    final fast weight from ipttt_prefill_layer equal, bit for bit, those of the
+    allocation-free entry point (same kernels and grouping, workspace in the
+    library's scratch area); N = 2 is also checked against the oracle chunk by
+    chunk."""
+    w = BF16_SMALL.replace(chunk=64, update="mse", eta=2e-3, n_seq=N, seq_len=1500)
+    weights = wl.make_weights(w)
+    x, e = wl.make_inputs(w)
+    layer = make_layer(w, weights, group_chunks=4)   # 24 chunks: 6 groups
+    try:
+        xd, ed = x.to(DEV), e.to(DEV)
+        runs = []
+        for fn in (B.ipttt_prefill_layer, B.ipttt_prefill_layer_noalloc):
+            layer.reset()
+            o = torch.full((N, w.seq_len, w.d), float("nan"), dtype=torch.float32, device=DEV)
+            fn(layer.handle, xd, ed, o, N, w.seq_len)
+            torch.cuda.synchronize()
+            runs.append((o.cpu(), layer.w_state[:N].cpu()))
+        (o_reg, w_reg), (o_na, w_na) = runs
+        assert torch.isfinite(o_reg).all()
+        assert torch.equal(o_reg, o_na)
+        assert torch.equal(w_reg, w_na)
+        if N == 2:
+            O_ref, W_ref = oracle_run(w, x, e, weights)
+            check_chunks(o_reg.double().numpy(), O_ref, w.chunk, TOL[w.dtype], "entry points")
+            check_weights(w_reg.double().numpy().transpose(0, 2, 1), W_ref, TOL[w.dtype],
+                          "entry points")
+    finally:
+        layer.close()
+
+
 def test_bf16_chunk_groups_multi_slab():
     """A workspace for 7 chunks with groups of 3: slabs of 6 chunks (whole groups)."""
     check_against_oracle(BF16_SMALL.replace(chunk=64), seq_len=20 * 64 - 9, slab_chunks=7,
