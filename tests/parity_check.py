@@ -15,8 +15,18 @@ import numpy as np
 import oracle
 
 
+# every check's summary line, printed again in pytest's terminal summary
+# (tests/conftest.py), where captured output does not hide it
+REPORT: list = []
+
+
 def say(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def report(line: str) -> None:
+    REPORT.append(line)
+    say(line)
 
 
 def rel_fro(a, b) -> float:
@@ -48,8 +58,8 @@ class ChunkErrors:
         n, k, s, err, _ = self.worst()
         mx = max(r[4] for r in self.rows)
         mean = float(np.mean([r[3] for r in self.rows]))
-        say(f"[{self.label}] {len(self.rows)} chunks: worst rel_fro O = {err:.3e} (sequence {n}, "
-            f"chunk {k}, tokens from {s}), mean {mean:.3e}, max |dO| = {mx:.3e} (tol {tol:.0e})")
+        report(f"[{self.label}] {len(self.rows)} chunks: worst rel_fro O = {err:.3e} (sequence {n}, "
+               f"chunk {k}, tokens from {s}), mean {mean:.3e}, max |dO| = {mx:.3e} (tol {tol:.0e})")
         bad = [r for r in self.rows if not (r[3] <= tol)]
         assert not bad, f"{len(bad)} chunks above {tol}: first {bad[0]}"
         return err
@@ -67,7 +77,7 @@ def check_weights(W_gpu, W_ref, tol: float, label: str) -> float:
     """Final fast weights [N, F, d] (pages' orientation): every sequence within tol."""
     errs = [rel_fro(W_gpu[n], W_ref[n]) for n in range(W_ref.shape[0])]
     worst = int(np.argmax(errs))
-    say(f"[{label}] final W: worst rel_fro {errs[worst]:.3e} (sequence {worst}) over {len(errs)} "
-        f"sequence(s), max |dW| = {float(np.max(np.abs(np.asarray(W_gpu) - W_ref))):.3e}")
+    report(f"[{label}] final W: worst rel_fro {errs[worst]:.3e} (sequence {worst}) over {len(errs)} "
+           f"sequence(s), max |dW| = {float(np.max(np.abs(np.asarray(W_gpu) - W_ref))):.3e}")
     assert all(e <= tol for e in errs), errs
     return errs[worst]

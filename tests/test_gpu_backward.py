@@ -22,6 +22,7 @@ import torch
 import oracle
 import workloads as wl
 from chunked_weight_mlp_amd import ipttt as B
+from parity_check import report
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -68,7 +69,7 @@ def compare(got, ref, label, keys=None):
     worst = 0.0
     for k in keys or ref:
         err = rel(got[k], ref[k])
-        say(f"[backward] {label} {k}: rel_fro {err:.3e}")
+        report(f"[backward] {label} {k}: rel_fro {err:.3e}")
         assert np.isfinite(got[k]).all(), k
         assert err <= TOL, (k, err)
         worst = max(worst, err)
@@ -223,7 +224,7 @@ def test_backward_full_size_32k():
                                                d_wf[0].double().numpy().T, rows, cols)
     got_e = g1["dw0"].double().cpu().numpy()[cols, rows]
     err = rel(got_e, ref_e)
-    say(f"[backward] 32k: sampled dW_0 rel err {err:.3e}")
+    report(f"[backward] 32k: sampled dW_0 rel err {err:.3e}")
     assert err <= TOL
     for k in ("dx", "de", "dw_gate", "dw_up", "dproj", "dconv_w"):
         assert torch.isfinite(g1[k]).all(), k

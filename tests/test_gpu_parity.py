@@ -16,7 +16,7 @@ import torch
 import oracle
 import workloads as wl
 from chunked_weight_mlp_amd import ipttt as B
-from parity_check import ChunkErrors, check_chunks, check_weights
+from parity_check import ChunkErrors, check_chunks, check_weights, report
 
 pytestmark = pytest.mark.gpu
 
@@ -427,5 +427,5 @@ def test_decode_token_by_token(dtype, update):
                      f"decode prefill {dtype} {update} seq {n}")
         W_ref.append(W_after)
     ew = rel_fro(w_pages(layer, 2), np.stack(W_ref))
-    say(f"[decode] {dtype} {update}: rel_fro W={ew:.3e}")
+    report(f"[decode] {dtype} {update}: rel_fro W={ew:.3e}")
     assert ew <= tol
