@@ -161,6 +161,20 @@ hipError_t mf_apply_mse_chunk(const Slab &s, int j, const __bf16 *zt, const __bf
 hipError_t mf_update_chunk(const Slab &s, int j, const __bf16 *zt, const __bf16 *bsrc,
                            int64_t b_ld, int64_t b_seq, float *w, __bf16 *snap_after,
                            int64_t snap_seq, hipStream_t st);
+// Group q of the MSE rule with explicit buffers and row-major copies of W (the
+// backward's recompute over chunk groups, s.G chunks each): the apply of the
+// group's rows from snap (+ n * snap_seq, W at the group's first chunk),
+// writing O (o + n * s.x_seq_stride, token rows) and Rt = eta (V - O)^T to rt
+// ([n][d][G Bp], the group's rows), after which mf_mse_fix corrects chunks
+// 1 .. of the group; then the group's update W += Zt . Rt with a row-major
+// copy of W before each of its chunks at snap + j dF (j = 0 .. chunks - 1, the
+// first one unchanged) and, when more chunks follow, the copy after its last
+// chunk at the next slot.
+hipError_t mf_apply_mse_group_rm(const Slab &s, int q, const __bf16 *zt, const __bf16 *snap,
+                                 int64_t snap_seq, const __bf16 *vt, float *o, __bf16 *rt,
+                                 hipStream_t st);
+hipError_t mf_update_group_rm(const Slab &s, int q, const __bf16 *zt, const __bf16 *rt, float *w,
+                              __bf16 *snap, int64_t snap_seq, hipStream_t st);
 
 // ---- backward (bf16 MFMA path, one slab holding the whole sequence) -----------
 struct BwBufs {

@@ -482,7 +482,8 @@ bool bw_supported(const ipttt_layer_desc *d) { return use_mfma(d); }
 
 struct BwLayout {
   size_t zt, at, ut, c, vt, wscr, gscr, snap_w, snap_g, dot, xt, dat, dut, dvt, dc, part, part2,
-      dproj_part, dyt, rt, total;
+      dproj_part, dyt, rt, p, oscr, rtg, total;
+  int G;  // chunks per group of the MSE recompute (1: chunk by chunk)
 };
 
 // Workspace of the backward: the whole sequence in one slab of K chunks.
@@ -517,6 +518,13 @@ BwLayout bw_layout(const ipttt_layer_desc &d, int n, int64_t L) {
   const bool mse = d.update == IPTTT_UPDATE_MSE;
   w.dyt = take(mse ? N * D * Lp * 2 : 0);
   w.rt = take(mse ? N * D * Lp * 2 : 0);
+  // the MSE recompute over chunk groups: block-causal Gram, O of every token,
+  // the current group's residuals
+  w.G = mse ? (int)std::min<size_t>((size_t)group_chunks(&d), K) : 1;
+  const size_t G = (size_t)w.G, ng = (K + G - 1) / G, RG = G * Bp;
+  w.p = take(w.G > 1 ? N * ng * RG * RG * 2 : 0);
+  w.oscr = take(w.G > 1 ? N * (size_t)L * D * 4 : 0);
+  w.rtg = take(w.G > 1 ? N * D * RG * 2 : 0);
   w.total = off;
   return w;
 }
@@ -704,6 +712,34 @@ ipttt_status ipttt_backward_layer(ipttt_layer *h, const void *x, const void *e, 
   const int64_t tstride = (int64_t)d.d * sl.Lp;  // [n][d][Lp] pitch between sequences
   if (!mse) {
     LAUNCH(IPTTT_K_UPDATE, mf_update_scan(sl, ws, wscr, false, st), "update scan launch");
+  } else if (lay.G > 1) {
+    // chunk groups, as the forward: per group one apply (from W at its first
+    // chunk), the Gram corrections of its later chunks, one update that keeps
+    // a row-major W per chunk; the group's residuals then go to their place
+    // in the token-contiguous Rt the reverse pass reads
+    Slab sg = sl;
+    sg.G = lay.G;
+    sg.ng_cap = (int)((K + lay.G - 1) / lay.G);
+    const int64_t RG = (int64_t)lay.G * Bp;
+    __bf16 *rtg = (__bf16 *)(base + lay.rtg);
+    float *oscr = (float *)(base + lay.oscr);
+    WsPtrs wsg{nullptr, base + lay.zt, nullptr, base + lay.vt, nullptr, rtg, base + lay.p};
+    LAUNCH(IPTTT_K_SNAPSHOT, gen_snapshot<__bf16>(sl, wscr, snap_w, sseq, st), "snapshot launch");
+    LAUNCH(IPTTT_K_GRAM, mf_gram(sg, wsg, st), "Gram launch");
+    for (int q = 0; (int64_t)q * lay.G < K; ++q) {
+      const int64_t j0 = (int64_t)q * lay.G, nq = std::min<int64_t>(lay.G, K - j0);
+      LAUNCH(IPTTT_K_APPLY,
+             mf_apply_mse_group_rm(sg, q, bb.zt, snap_w + j0 * dF, sseq, bb.vt, oscr, rtg, st),
+             "apply launch");
+      for (int jl = 1; jl < nq; ++jl)
+        LAUNCH(IPTTT_K_MSE_FIX, mf_mse_fix(sg, q, jl, wsg, oscr, st), "MSE correction launch");
+      LAUNCH(IPTTT_K_UPDATE, mf_update_group_rm(sg, q, bb.zt, rtg, wscr, snap_w + j0 * dF, sseq, st),
+             "update launch");
+      TRY_HIP(hipMemcpy2DAsync(rt + j0 * Bp, (size_t)sl.Lp * 2, rtg, (size_t)RG * 2,
+                               (size_t)(nq * Bp) * 2, (size_t)batch * d.d, hipMemcpyDeviceToDevice,
+                               st),
+              "residual copy");
+    }
   } else {
     // chunk by chunk: W_j kept per chunk, residual eta (V - O_j) kept per chunk
     LAUNCH(IPTTT_K_SNAPSHOT, gen_snapshot<__bf16>(sl, wscr, snap_w, sseq, st), "snapshot launch");

@@ -916,7 +916,10 @@ __global__ __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::OCC)
 #pragma unroll
   for (int k = 0; k < NSLOT; ++k)
     if (k >= nslot) store_slot(k);
-  if (snap_after) write_snap(snap + n_seq * snap_seq_stride);
+  // after the last chunk: the next slot when the groups have their own copies
+  if (snap_after)
+    write_snap(snap + n_seq * snap_seq_stride +
+               (snap_each_group ? (int64_t)((n_chunks + G - 1) / G) * snap_group_stride : 0));
 #pragma unroll
   for (int i = 0; i < C::MI; ++i)
 #pragma unroll
@@ -1233,6 +1236,30 @@ hipError_t mf_apply_mse_chunk(const Slab &s, int j, const __bf16 *zt, const __bf
                                                             nullptr, vt, rt, rt_seq, rt_ld, st);
   return mfma::launch_apply_x<C, false>(s, j, 1, zt, snap, snap_seq, 0, nullptr, nullptr, vt, rt,
                                         rt_seq, rt_ld, st);
+}
+hipError_t mf_apply_mse_group_rm(const Slab &s, int q, const __bf16 *zt, const __bf16 *snap,
+                                 int64_t snap_seq, const __bf16 *vt, float *o, __bf16 *rt,
+                                 hipStream_t st) {
+  using C = mfma::ApplyCfg;
+  const int64_t RG = (int64_t)s.G * s.Bp;
+  const int64_t big_blocks = ((RG + C::BM - 1) / C::BM) * ((s.d + C::BN - 1) / C::BN) * s.n_seq;
+  if (big_blocks < 512)
+    return mfma::launch_apply_x<mfma::ApplySmallCfg, false>(s, q, 1, zt, snap, snap_seq, 0, nullptr,
+                                                            o, vt, rt, s.d * RG, RG, st);
+  return mfma::launch_apply_x<C, false>(s, q, 1, zt, snap, snap_seq, 0, nullptr, o, vt, rt,
+                                        s.d * RG, RG, st);
+}
+hipError_t mf_update_group_rm(const Slab &s, int q, const __bf16 *zt, const __bf16 *rt, float *w,
+                              __bf16 *snap, int64_t snap_seq, hipStream_t st) {
+  using C = mfma::UpdateCfg;
+  const int64_t dF = (int64_t)s.d * s.F, RG = (int64_t)s.G * s.Bp;
+  const int j_first = q * s.G, n_chunks = std::min(s.G, s.nc - j_first);
+  const int64_t nb = ((s.F + C::BM - 1) / C::BM) * ((s.d + C::BN - 1) / C::BN) * s.n_seq;
+  // one copy group per chunk (G = 1 inside the launch), the B operand the
+  // group's Rt rows (chunk jc at jc Bp)
+  return mfma::launch_k_update<C, false>(s, nb, st, j_first, n_chunks, 1, zt, rt, RG, s.d * RG,
+                                         (int64_t)s.Bp, w, snap, snap_seq, dF, 1,
+                                         j_first + n_chunks < s.nc ? 1 : 0, 0);
 }
 hipError_t mf_update_chunk(const Slab &s, int j, const __bf16 *zt, const __bf16 *bsrc,
                            int64_t b_ld, int64_t b_seq, float *w, __bf16 *snap_after,

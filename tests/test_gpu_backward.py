@@ -124,9 +124,11 @@ def test_backward_conv_taps(Kc, Bc, L, update):
     (128, 700, 2, True),     # ragged last chunk, two sequences
     (96, 500, 1, False),     # padding rows in every chunk
     (512, 1100, 1, True),    # full-height tiles
+    (64, 3000, 2, True),     # the recompute in two chunk groups (32 and 15 chunks)
 ])
 def test_backward_mse_small_shapes(Bc, L, N, with_dwf):
-    """MSE rule: the reverse pass runs chunk by chunk (dY_j = dO_j - eta Z_j G_{j+1})."""
+    """MSE rule: the forward is recomputed over chunk groups (a copy of W kept per
+    chunk), the reverse pass runs chunk by chunk (dY_j = dO_j - eta Z_j G_{j+1})."""
     w = SMALL.replace(chunk=Bc, seq_len=L, n_seq=N, update="mse", eta=2e-3)
     weights = wl.make_weights(w)
     x, e = wl.make_inputs(w)
